@@ -1,0 +1,206 @@
+"""Split-plan heuristic, step by step (oracle; test infrastructure).
+
+The pages fix what a plan is but print no formula: a caller builds, on the
+host and next to the decode CSR, a split count and a split_indptr per row
+(ATOM pull request 2462, "Summary", part 1); a uniform plan depends only on
+the row count and config, so graph capture and replay agree (same section);
+the persistent kernel instead plans from the real per-row KV lengths on every
+call (same page, "Summary", part 2), and its gate is fp8 KV, 128 local heads
+and 15 <= rows <= 32768. The constants and tie-breaks below are this
+library's own choice (spec version 1); the library's C++ planner must produce
+the same int32 words.
+
+Constants: M_UNIT 64 query rows per work item, N_MAX 64 splits per row,
+MIN_SPLIT_KEYS 256, ITEM_OVERHEAD 64, OCC 2 resident work items per compute
+unit, XCDS 8 (the chiplets whose L2 a launch spreads over).
+All arithmetic is integer; cdiv(a, b) = (a + b - 1) // b.
+
+Steps:
+1. u = cdiv(H * q_len_max, M_UNIT): M tiles per split. A query row is
+   (token i, head h) at index i * H + h of its request row.
+2. Mode. AUTO means LENGTH_AWARE iff kv is fp8, H == 128 and
+   15 <= R <= 32768 (the persistent gate), else UNIFORM.
+3. UNIFORM: n = clamp(min(cdiv(OCC*C, R*u), cdiv(max L, MIN_SPLIT_KEYS)), 1,
+   N_MAX); every row gets n splits.
+4. LENGTH_AWARE: T = max(MIN_SPLIT_KEYS, cdiv(u * sum L, OCC*C));
+   n_b = clamp(cdiv(L_b, T), 1, N_MAX).
+5. split_indptr is the running sum of n_b. Split k of row b (global id
+   split_indptr[b] + k) covers keys [k*L_b // n_b, (k+1)*L_b // n_b); empty
+   ranges are legal. Splits of rows with n_b > 1 get partial-buffer slots
+   0, 1, 2, ... in split order; the others get -1.
+6. Split cost = (end - begin) + ITEM_OVERHEAD. Splits are ranked by
+   (-cost, split id). Rank k goes to chiplet k mod X, with X = XCDS for
+   UNIFORM and min(XCDS, G) for LENGTH_AWARE. Each chiplet's item list is its
+   splits in rank order, each followed by its M tiles m = 0..u-1.
+7. UNIFORM: one item per workgroup, G = W = S*u. Workgroup ids are dealt to
+   chiplets round-robin (id mod XCDS), so for j < n_min (the shortest
+   chiplet list) workgroup XCDS*j + x runs item j of chiplet x; the remaining
+   items, taken by (j, x), fill the ids from XCDS*n_min upward in order.
+8. LENGTH_AWARE: G = min(OCC*C, W) persistent workgroups; workgroup g belongs
+   to chiplet g mod X. Each chiplet's items, in list order, go one by one to
+   that chiplet's workgroup with the least (load, id), load being the sum of
+   its item costs; a workgroup runs its items in the order they came.
+9. Words (int32): a 20-word header [magic 0x4D4C4150, version 1, R, H,
+   q_len_max, kv_dtype, C, mode_used, M_UNIT, u, N_MAX, MIN_SPLIT_KEYS,
+   ITEM_OVERHEAD, OCC, S, W, G, P, 20, total words], then split_indptr[R+1],
+   split_row[S], split_begin[S], split_end[S], split_part[S],
+   work_indptr[G+1], item_split[W], item_m[W].
+"""
+import numpy as np
+
+MAGIC = 0x4D4C4150
+VERSION = 1
+HEADER_WORDS = 20
+M_UNIT = 64
+N_MAX = 64
+MIN_SPLIT_KEYS = 256
+ITEM_OVERHEAD = 64
+OCC = 2
+XCDS = 8
+
+MODE_AUTO, MODE_UNIFORM, MODE_LENGTH_AWARE = 0, 1, 2
+KV_BF16, KV_FP8 = 0, 1
+
+
+def cdiv(a, b):
+    return (a + b - 1) // b
+
+
+def clamp(x, lo, hi):
+    return max(lo, min(hi, x))
+
+
+def choose_mode(mode, kv_dtype, H, R):
+    if mode != MODE_AUTO:
+        return mode
+    if kv_dtype == KV_FP8 and H == 128 and 15 <= R <= 32768:
+        return MODE_LENGTH_AWARE
+    return MODE_UNIFORM
+
+
+def plan_ref(kv_lens, H, q_len_max, kv_dtype, mode, C):
+    """Returns the plan as a numpy int32 array of words."""
+    lens = [int(x) for x in kv_lens]
+    R = len(lens)
+    if R < 1 or not (1 <= H <= 128) or not (1 <= q_len_max <= 16) or C < 1:
+        raise ValueError("unsupported plan arguments")
+    if any(L < 0 for L in lens):
+        raise ValueError("negative KV length")
+
+    # 1-2
+    u = cdiv(H * q_len_max, M_UNIT)
+    mode_used = choose_mode(mode, kv_dtype, H, R)
+
+    # 3-4: split count per row
+    if mode_used == MODE_UNIFORM:
+        n = clamp(min(cdiv(OCC * C, R * u), cdiv(max(lens), MIN_SPLIT_KEYS)), 1, N_MAX)
+        nsplit = [n] * R
+    else:
+        T = max(MIN_SPLIT_KEYS, cdiv(u * sum(lens), OCC * C))
+        nsplit = [clamp(cdiv(L, T), 1, N_MAX) for L in lens]
+
+    # 5: CSR of splits, key ranges, partial slots
+    split_indptr = [0]
+    for nb in nsplit:
+        split_indptr.append(split_indptr[-1] + nb)
+    S = split_indptr[-1]
+    split_row, split_begin, split_end, split_part = [], [], [], []
+    next_slot = 0
+    for b, (L, nb) in enumerate(zip(lens, nsplit)):
+        for k in range(nb):
+            split_row.append(b)
+            split_begin.append(k * L // nb)
+            split_end.append((k + 1) * L // nb)
+            if nb > 1:
+                split_part.append(next_slot)
+                next_slot += 1
+            else:
+                split_part.append(-1)
+    P = next_slot
+
+    # 6: ranking and chiplet lists
+    W = S * u
+    cost = [split_end[s] - split_begin[s] + ITEM_OVERHEAD for s in range(S)]
+    ranked = sorted(range(S), key=lambda s: (-cost[s], s))
+    if mode_used == MODE_UNIFORM:
+        G = W
+        X = XCDS
+    else:
+        G = min(OCC * C, W)
+        X = min(XCDS, G)
+    lists = [[] for _ in range(X)]
+    for k, s in enumerate(ranked):
+        for m in range(u):
+            lists[k % X].append((s, m))
+
+    # 7-8: workgroups
+    if mode_used == MODE_UNIFORM:
+        order = [None] * W
+        n_min = min(len(lst) for lst in lists)
+        for x in range(X):
+            for j in range(n_min):
+                order[XCDS * j + x] = lists[x][j]
+        nxt = XCDS * n_min
+        tail_len = max(len(lst) for lst in lists)
+        for j in range(n_min, tail_len):
+            for x in range(X):
+                if j < len(lists[x]):
+                    order[nxt] = lists[x][j]
+                    nxt += 1
+        assert nxt == W
+        groups = [[it] for it in order]
+    else:
+        groups = [[] for _ in range(G)]
+        load = [0] * G
+        for x in range(X):
+            members = [g for g in range(G) if g % X == x]
+            for (s, m) in lists[x]:
+                g = min(members, key=lambda g: (load[g], g))
+                groups[g].append((s, m))
+                load[g] += cost[s]
+
+    work_indptr = [0]
+    item_split, item_m = [], []
+    for grp in groups:
+        for (s, m) in grp:
+            item_split.append(s)
+            item_m.append(m)
+        work_indptr.append(len(item_split))
+
+    total = HEADER_WORDS + (R + 1) + 4 * S + (G + 1) + 2 * W
+    header = [MAGIC, VERSION, R, H, q_len_max, kv_dtype, C, mode_used, M_UNIT, u,
+              N_MAX, MIN_SPLIT_KEYS, ITEM_OVERHEAD, OCC, S, W, G, P, HEADER_WORDS, total]
+    words = (header + split_indptr + split_row + split_begin + split_end + split_part
+             + work_indptr + item_split + item_m)
+    assert len(words) == total
+    return np.asarray(words, dtype=np.int64).astype(np.int32)
+
+
+FIELDS = ["magic", "version", "R", "H", "q_len_max", "kv_dtype", "C", "mode", "M_UNIT", "u",
+          "N_MAX", "MIN_SPLIT_KEYS", "ITEM_OVERHEAD", "OCC", "S", "W", "G", "P",
+          "header_words", "total_words"]
+
+
+def unpack_plan(words):
+    """Split the words into a dict of named fields and arrays."""
+    w = [int(x) for x in words]
+    d = dict(zip(FIELDS, w[:HEADER_WORDS]))
+    pos = HEADER_WORDS
+    R, S, W, G = d["R"], d["S"], d["W"], d["G"]
+
+    def take(n):
+        nonlocal pos
+        out = w[pos:pos + n]
+        pos += n
+        return out
+
+    d["split_indptr"] = take(R + 1)
+    d["split_row"] = take(S)
+    d["split_begin"] = take(S)
+    d["split_end"] = take(S)
+    d["split_part"] = take(S)
+    d["work_indptr"] = take(G + 1)
+    d["item_split"] = take(W)
+    d["item_m"] = take(W)
+    assert pos == d["total_words"] == len(w)
+    return d
