@@ -1,0 +1,218 @@
+"""Benchmark of the paged MLA decode hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: host split plan (C++),
+plan upload (pinned host -> device, async), decode kernel, merge kernel (when a
+row is split). Inputs are resident in HBM before the timed region. Successive
+steps rotate over three disjoint index lists of the same pool, so a step does
+not find the previous step's KV rows in the 256 MB Infinity Cache.
+
+Prints one JSON line. `value` is the effective KV bandwidth of the whole step
+(KV bytes gathered / step time); MFMA TFLOP/s (visible pairs only) and the
+decode kernel's roofline entry are reported beside it; `cpu_baseline` times
+the float64 CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode effective KV GB/s + MFMA TFLOP/s (128 heads, q_len 8, fp8 KV)"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+KERNEL_SRC = os.path.join(ROOT, "paged_mla_decode_02_amd", "csrc", "kernels.hip")
+
+
+def kernel_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def visible_pairs(kv_lens, q_lens, causal):
+    total = 0
+    for L, q in zip(kv_lens, q_lens):
+        L, q = int(L), int(q)
+        if causal:
+            total += sum(min(max(L - q + i + 1, 0), L) for i in range(q))
+        else:
+            total += L * q
+    return total
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_sha") != kernel_sha():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s):
+    """Time the float64 oracle on whole rows of the workload until about
+    budget_s seconds of CPU work (at least one row)."""
+    from oracle.attention import attend_case
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    order = list(range(case.rows))
+    attend_case(case, rows=order[:1])          # warm-up
+    done, kv_bytes, t_used = [], 0, 0.0
+    elem = 2 if case.kv_dtype == "bf16" else 1
+    for b in order:
+        t0 = time.perf_counter()
+        attend_case(case, rows=[b])
+        t_used += time.perf_counter() - t0
+        done.append(b)
+        kv_bytes += int(case.kv_lens[b]) * 576 * elem
+        if t_used >= budget_s:
+            break
+    return {"value": kv_bytes / t_used / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(done)} of {case.rows} rows of {case.name} ({sum(int(case.kv_lens[b]) for b in done)} keys), "
+                      f"float64 numpy, {t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="verify_causal")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work; 0 skips")
+    ap.add_argument("--rotate", type=int, default=3, help="disjoint index lists cycled over steps")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the decode has no "
+                                   "multi-GPU path in this build (see the design notes on sharding)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import paged_mla_decode_02_amd as mla
+    from workloads import make_config
+
+    torch.cuda.set_device(0)
+    mla.load_library()
+    case = make_config(args.workload, extra_index_sets=max(args.rotate - 1, 0))
+    index_sets = [case.kv_indices] + list(case.alt_kv_indices)
+    dev = mla.device_inputs(case.q_codes, case.q_scale, case.pool_codes, case.kv_scale,
+                            case.qo_indptr, case.kv_indptr, case.kv_indices)
+    idx_dev = [dev["kv_indices"]] + [torch.from_numpy(i).cuda() for i in index_sets[1:]]
+    inputs = [dict(dev, kv_indices=t) for t in idx_dev]
+    dec = mla.MlaDecoder(case.heads, case.q_len, case.q_dtype, case.kv_dtype, case.causal,
+                         float(case.sm_scale))
+    T = case.num_tokens
+    o = torch.empty((T, case.heads, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, case.heads), dtype=torch.float32, device="cuda")
+    kv_lens = case.kv_lens
+    stream = torch.cuda.current_stream()
+
+    def step(k, ev=None):
+        words = dec.make_plan(kv_lens)                 # A1: host plan
+        plan_dev = dec.upload_plan(words)              # A2: upload
+        ws = dec.workspace(words)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.decode_fwd(inputs[k % len(inputs)]["q"], dec.q_dtype, dev["q_scale"], dev["kv_pool"],
+                       dec.kv_dtype, dev["kv_scale"], dev["qo_indptr"], dev["kv_indptr"],
+                       inputs[k % len(inputs)]["kv_indices"], words, plan_dev, case.rows,
+                       case.heads, case.q_len, case.causal, float(case.sm_scale), o, lse, ws,
+                       stream)
+        if ev is not None:
+            ev[1].record(stream)
+        return words
+
+    for k in range(args.warmup):
+        words = step(k)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        words = step(k, evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = t_start.elapsed_time(t_end)
+    ms_per_step = max(wall * 1e3, gpu_ms) / args.steps
+    fwd_ms = [a.elapsed_time(b) for a, b in evs]
+    fwd_avg = float(np.mean(fwd_ms))
+
+    plan_info = mla_plan_info(words)
+    elem = 2 if case.kv_dtype == "bf16" else 1
+    keys = int(kv_lens.sum())
+    kv_bytes = keys * 576 * elem
+    pairs = visible_pairs(kv_lens, case.q_lens, case.causal)
+    flops = 2.0 * (576 + 512) * case.heads * pairs
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    tflops_step = flops / (ms_per_step * 1e-3) / 1e12
+
+    # Dominant kernel: the decode kernel (plus the merge, when the plan splits
+    # rows, since one mla_decode_fwd call launches both).
+    q_elem = 2 if case.q_dtype == "bf16" else 1
+    alg_bytes = (kv_bytes + keys * 4 + T * case.heads * 576 * q_elem + T * case.heads * (512 * 2 + 4))
+    compute_dtype = "bf16"
+    achieved_tflops = flops / (fwd_avg * 1e-3) / 1e12
+    achieved_gbs = alg_bytes / (fwd_avg * 1e-3) / 1e9
+    ridge = MFMA_PEAK_TFLOPS[compute_dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "mfma" if flops / alg_bytes > ridge else "hbm"
+    traffic = measured_traffic(args.workload)
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(achieved_tflops, 2),
+                "peak": MFMA_PEAK_TFLOPS[compute_dtype], "unit": "TFLOP/s",
+                "frac": round(achieved_tflops / MFMA_PEAK_TFLOPS[compute_dtype], 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = traffic
+    roof["kernel"] = "decode_kernel" + ("+merge_kernel" if plan_info["P"] > 0 else "")
+    roof["launch_ms"] = round(fwd_avg, 4)
+    roof["algorithmic_bytes"] = alg_bytes
+    roof["algorithmic_flops"] = flops
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": compute_dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "rows": case.rows, "q_len": case.q_len,
+                   "heads": case.heads, "q_dtype": case.q_dtype, "kv_dtype": case.kv_dtype,
+                   "causal": case.causal, "kv_keys": keys, "plan_mode": plan_info["mode"],
+                   "splits": plan_info["S"], "workgroups": plan_info["G"],
+                   "index_rotation": len(inputs)},
+        "mfma_tflops": round(tflops_step, 2),
+        "roofline": roof,
+    }
+    if args.cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+def mla_plan_info(words):
+    names = ["magic", "version", "R", "H", "q_len_max", "kv_dtype", "C", "mode", "M_UNIT", "u",
+             "N_MAX", "MIN_SPLIT_KEYS", "ITEM_OVERHEAD", "OCC", "S", "W", "G", "P"]
+    d = dict(zip(names, [int(x) for x in words[:18]]))
+    d["mode"] = {1: "uniform", 2: "length_aware"}.get(d["mode"], d["mode"])
+    return d
+
+
+if __name__ == "__main__":
+    main()

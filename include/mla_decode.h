@@ -1,0 +1,166 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) paged MLA decode library.
+ *
+ * The operation: multi-head latent attention decode over a paged latent KV
+ * cache. Every KV slot holds one latent row of 576 values (512 compressed
+ * "nope" dims followed by 64 RoPE dims); all heads attend to the same row and
+ * V is its first 512 dims. Pages hold one token each, so a request row names
+ * its keys with a flat CSR index list (kv_indptr, kv_indices) -- "one row per
+ * request, same index list" ([ROCm][Spec Decode] Add Aiter MLA decode support
+ * non-causal draft block, vLLM pull request 53001, Purpose). A request row may
+ * carry a block of up to 16 query tokens (qo_indptr): causal for a speculative
+ * verify pass, with the mask on global positions (ATOM pull request 2760,
+ * Problem), or non-causal for a draft block, the mask being a runtime flag
+ * rather than a separate kernel (vLLM pull request 53001, Purpose). Long rows
+ * are split across workgroups by a host-built split plan ([DSV4] Tuned ASM
+ * FP8 decode with split plans, ATOM pull request 2462, Summary part 1) or one
+ * planned per call from the real lengths (same page, Summary part 2), and the
+ * split partials are merged by log-sum-exp (same page, Dependencies: split and
+ * merge).
+ *
+ * Semantics, for request row b with L = kv_indptr[b+1] - kv_indptr[b] keys
+ * and q_b = qo_indptr[b+1] - qo_indptr[b] query tokens:
+ *   k_j   = pool[kv_indices[kv_indptr[b] + j]] * kv_scale,   j in [0, L)
+ *   q     = Q[qo_indptr[b] + i, h] * q_scale
+ *   token i sits at position L - q_b + i, key j at position j; causal: token i
+ *   sees keys j <= L - q_b + i; non-causal: all j < L
+ *   s_j   = softmax_scale * (q . k_j)
+ *   LSE   = ln sum_visible exp(s_j)        (natural log, fp32)
+ *   O     = sum_visible exp(s_j - LSE) * k_j[0:512]   (rounded to bf16)
+ *   no visible key: O = 0, LSE = -inf.
+ *
+ * Conventions for every call:
+ *   - All integers are int32 unless noted. Device buffers are contiguous.
+ *   - The caller owns every buffer. The library never allocates device
+ *     memory, never synchronizes the device and keeps no pointer between
+ *     calls. All work is enqueued on the caller's stream.
+ *   - Every entry point returns an mla_status. A negative value is an error;
+ *     mla_last_error() gives the message (thread-local). Arguments are checked
+ *     on the host before anything is launched; an error launches nothing.
+ *   - Data that lives on the device (index values, indptr monotonicity,
+ *     q_b <= q_len_max) cannot be checked without a synchronization and is a
+ *     caller contract: kv_indices values in [0, num_slots), kv_indptr and
+ *     qo_indptr non-decreasing, qo_indptr[0] = 0, per-row q_b <= q_len_max, and
+ *     kv_indptr[b+1] - kv_indptr[b] equal to the kv_lens the plan was built
+ *     from. kv_indptr[0] may be non-zero (an offset list; indices are used as
+ *     absolute positions in kv_indices).
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point is exported from libmla_decode.so (built with hidden
+ * visibility for everything else). */
+#define MLA_API __attribute__((visibility("default")))
+
+#define MLA_ABI_VERSION 1
+#define MLA_D_LATENT 576   /* latent row: 512 compressed dims + 64 RoPE dims */
+#define MLA_D_V 512        /* V = the first 512 latent dims */
+#define MLA_MAX_HEADS 128
+#define MLA_MAX_Q_LEN 16
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,   /* null pointer, bad enum, misalignment, bad size */
+  MLA_ERR_UNSUPPORTED = -2,   /* a shape or dtype outside the supported range */
+  MLA_ERR_WORKSPACE = -3,     /* workspace too small for the plan */
+  MLA_ERR_PLAN_MISMATCH = -4, /* plan words do not match this call */
+  MLA_ERR_HIP = -5            /* a HIP launch reported an error */
+} mla_status;
+
+/* Element formats. fp8 is OCP e4m3fn (max 448, no infinities); a stored value
+ * times its per-tensor scale is the real value. */
+typedef enum { MLA_BF16 = 0, MLA_FP8_E4M3 = 1 } mla_dtype;
+
+/* AUTO picks LENGTH_AWARE for fp8 KV with 128 heads and 15..32768 rows (the
+ * persistent-kernel gate of ATOM pull request 2462, Summary part 2), else
+ * UNIFORM. */
+typedef enum { MLA_PLAN_AUTO = 0, MLA_PLAN_UNIFORM = 1, MLA_PLAN_LENGTH_AWARE = 2 } mla_plan_mode;
+
+/* Upper bound on the int32 words mla_decode_plan can write for these sizes.
+ * Host only; never fails for rows >= 1, heads in [1,128], q_len_max in [1,16],
+ * num_cus >= 1. */
+MLA_API int32_t mla_decode_plan_capacity(int32_t rows, int32_t num_cus, int32_t num_heads,
+                                 int32_t q_len_max, int64_t* words_out);
+
+/* Build the split plan on the host (pure: the same inputs give the same
+ * words). kv_lens: host [rows], each >= 0. num_cus: the device's compute-unit
+ * count (256 on MI355X). plan: host buffer of plan_words int32, caller-owned;
+ * on success word 19 holds the number of words written.
+ *
+ * Plan words: a 20-word header [magic 0x4D4C4150, version 1, rows, heads,
+ * q_len_max, kv_dtype, num_cus, mode_used, M_UNIT, u, N_MAX, MIN_SPLIT_KEYS,
+ * ITEM_OVERHEAD, OCC, S, W, G, P, 20, total_words], then split_indptr[rows+1],
+ * split_row[S], split_begin[S], split_end[S], split_part[S], work_indptr[G+1],
+ * item_split[W], item_m[W]. S splits, W work items (split, M tile of 64 query
+ * rows), G workgroups, P partial-buffer slots. Errors: INVALID_ARG (null,
+ * negative length, too few words), UNSUPPORTED (heads, q_len_max or rows out
+ * of range). */
+MLA_API int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t num_heads,
+                        int32_t q_len_max, mla_dtype kv_dtype, mla_plan_mode mode,
+                        int32_t num_cus, int32_t* plan, int64_t plan_words);
+
+/* Workspace bytes mla_decode_fwd needs for this plan (0 when no row is
+ * split): P * q_len_max * heads * (512 + 1) * 4 bytes of fp32 partials.
+ * plan: host words from mla_decode_plan. Errors: INVALID_ARG, PLAN_MISMATCH
+ * (bad magic or version). */
+MLA_API int32_t mla_decode_workspace_size(const int32_t* plan, int64_t* bytes_out);
+
+/*
+ * Enqueue the decode: one decode kernel over the plan's G workgroups, then,
+ * if any row is split, one merge kernel. No host synchronization.
+ *   q          device, [qo_indptr[rows], num_heads, 576] of q_dtype, 16-byte aligned
+ *   q_scale    device float scalar, or NULL for 1.0 (fp8 Q needs its scale)
+ *   kv_pool    device, [num_slots, 576] of kv_dtype, 16-byte aligned
+ *   kv_scale   device float scalar, or NULL for 1.0
+ *   qo_indptr  device [rows+1];  kv_indptr device [rows+1];  kv_indices device
+ *   plan_host  host words from mla_decode_plan; plan_dev a device copy of the
+ *              same words (the caller uploads it, e.g. from pinned memory)
+ *   causal     0 = non-causal, 1 = causal on positions (see top of file)
+ *   softmax_scale  finite and > 0
+ *   o          device bf16 [qo_indptr[rows], num_heads, 512], 16-byte aligned
+ *   lse        device fp32 [qo_indptr[rows], num_heads]
+ *   workspace  device, >= mla_decode_workspace_size bytes, 16-byte aligned
+ *              (may be NULL when that size is 0); contents are scratch
+ *   stream     hipStream_t (NULL = the default stream)
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, PLAN_MISMATCH (plan header
+ * differs from rows / num_heads / q_len_max / kv_dtype, or a plan from a
+ * different spec version), HIP (launch failure).
+ */
+MLA_API int32_t mla_decode_fwd(const void* q, mla_dtype q_dtype, const float* q_scale,
+                       const void* kv_pool, mla_dtype kv_dtype, const float* kv_scale,
+                       int64_t num_slots, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                       const int32_t* kv_indices, const int32_t* plan_host,
+                       const int32_t* plan_dev, int32_t rows, int32_t num_heads,
+                       int32_t q_len_max, int32_t causal, float softmax_scale, void* o,
+                       float* lse, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Test hook: run the decode kernel's own index gather and tile loader over
+ * every split of the plan and write the rows it staged in LDS, in the form
+ * the matrix cores consume (bf16; fp8 slots converted exactly), to
+ * dense_out: device bf16 [kv_indptr[rows] - kv_indptr[0], 576], row
+ * kv_indptr[b] - kv_indptr[0] + j for key j of row b. Same argument rules and
+ * errors as mla_decode_fwd.
+ */
+MLA_API int32_t mla_debug_gather(const void* kv_pool, mla_dtype kv_dtype, int64_t num_slots,
+                         const int32_t* kv_indptr, const int32_t* kv_indices,
+                         const int32_t* plan_host, const int32_t* plan_dev, int32_t rows,
+                         void* dense_out, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+MLA_API const char* mla_last_error(void);
+
+/* MLA_ABI_VERSION of the built library. */
+MLA_API int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

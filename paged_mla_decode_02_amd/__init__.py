@@ -1,0 +1,242 @@
+"""Python binding of libmla_decode.so (paged MLA decode for MI355X / gfx950).
+
+Argument marshalling only: every step of the decode runs in the library's HIP
+kernels; torch supplies device memory and streams. The entry points mirror the
+C ABI in include/mla_decode.h:
+
+    plan(kv_lens, heads, q_len_max, kv_dtype, mode, num_cus) -> int32 numpy words
+    workspace_size(plan_words) -> bytes
+    decode_fwd(...)        enqueue decode (+ merge) on the current stream
+    debug_gather(...)      the decode kernel's gather, written to a dense tensor
+
+``MlaDecoder`` wraps the per-batch steps a caller repeats (build the plan on the
+host, upload it, size the workspace, launch). If the library is missing or a
+call fails, an error is raised; there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla_decode.so")
+
+MLA_BF16, MLA_FP8_E4M3 = 0, 1
+PLAN_AUTO, PLAN_UNIFORM, PLAN_LENGTH_AWARE = 0, 1, 2
+D_LATENT, D_V = 576, 512
+STATUS = {0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "WORKSPACE", -4: "PLAN_MISMATCH",
+          -5: "HIP"}
+
+_lib = None
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the shared library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} not found: build it first (python -m paged_mla_decode_02_amd.build)")
+    lib = ctypes.CDLL(path)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    lib.mla_decode_plan_capacity.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i64)]
+    lib.mla_decode_plan_capacity.restype = i32
+    lib.mla_decode_plan.argtypes = [p32, i32, i32, i32, i32, i32, i32, p32, i64]
+    lib.mla_decode_plan.restype = i32
+    lib.mla_decode_workspace_size.argtypes = [p32, ctypes.POINTER(i64)]
+    lib.mla_decode_workspace_size.restype = i32
+    lib.mla_decode_fwd.argtypes = [vp, i32, vp, vp, i32, vp, i64, vp, vp, vp, p32, vp, i32, i32,
+                                   i32, i32, ctypes.c_float, vp, vp, vp, i64, vp]
+    lib.mla_decode_fwd.restype = i32
+    lib.mla_debug_gather.argtypes = [vp, i32, i64, vp, vp, p32, vp, i32, vp, vp]
+    lib.mla_debug_gather.restype = i32
+    lib.mla_last_error.argtypes = []
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_abi_version.argtypes = []
+    lib.mla_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().mla_last_error().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise MlaError(status, last_error())
+
+
+def _dtype_code(name_or_code) -> int:
+    if name_or_code in (MLA_BF16, MLA_FP8_E4M3):
+        return int(name_or_code)
+    return {"bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}[name_or_code]
+
+
+def _host_i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def plan_capacity(rows: int, num_cus: int, heads: int, q_len_max: int) -> int:
+    n = ctypes.c_int64(0)
+    _check(load_library().mla_decode_plan_capacity(rows, num_cus, heads, q_len_max, ctypes.byref(n)))
+    return n.value
+
+
+def plan(kv_lens, heads: int, q_len_max: int, kv_dtype, mode: int = PLAN_AUTO,
+         num_cus: int = 256) -> np.ndarray:
+    """Host split plan (int32 words) for these per-row KV lengths."""
+    lens = _host_i32(kv_lens)
+    rows = int(lens.shape[0])
+    cap = plan_capacity(max(rows, 1), num_cus, heads, q_len_max) if rows >= 1 and 1 <= heads <= 128 \
+        and 1 <= q_len_max <= 16 and num_cus >= 1 else 64
+    out = np.zeros(cap, dtype=np.int32)
+    _check(load_library().mla_decode_plan(
+        lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), rows, heads, q_len_max,
+        _dtype_code(kv_dtype), int(mode), num_cus,
+        out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), cap))
+    return out[:int(out[19])].copy()
+
+
+def workspace_size(plan_words: np.ndarray) -> int:
+    w = _host_i32(plan_words)
+    n = ctypes.c_int64(0)
+    _check(load_library().mla_decode_workspace_size(w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                                   ctypes.byref(n)))
+    return n.value
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def decode_fwd(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, kv_indptr, kv_indices,
+               plan_host: np.ndarray, plan_dev, rows: int, heads: int, q_len_max: int, causal: bool,
+               softmax_scale: float, o, lse, workspace=None, stream=None):
+    """Enqueue mla_decode_fwd. Tensors are device tensors; q/kv_pool hold the
+    stored codes (bf16 as int16/bfloat16, fp8 as uint8/float8_e4m3fn);
+    q_scale/kv_scale are 1-element float32 device tensors or None."""
+    ph = _host_i32(plan_host)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().mla_decode_fwd(
+        _ptr(q), _dtype_code(q_dtype), _ptr(q_scale), _ptr(kv_pool), _dtype_code(kv_dtype),
+        _ptr(kv_scale), int(kv_pool.shape[0]), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices),
+        ph.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(plan_dev), rows, heads, q_len_max,
+        1 if causal else 0, float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream_handle(stream))
+    _check(st)
+
+
+def debug_gather(kv_pool, kv_dtype, kv_indptr, kv_indices, plan_host: np.ndarray, plan_dev,
+                 rows: int, dense_out, stream=None):
+    ph = _host_i32(plan_host)
+    st = load_library().mla_debug_gather(
+        _ptr(kv_pool), _dtype_code(kv_dtype), int(kv_pool.shape[0]), _ptr(kv_indptr),
+        _ptr(kv_indices), ph.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(plan_dev), rows,
+        _ptr(dense_out), _stream_handle(stream))
+    _check(st)
+
+
+class MlaDecoder:
+    """Holds the device tensors of one decode batch and runs the hot path:
+    host plan -> plan upload (pinned, async) -> decode kernel -> merge kernel.
+
+    ``inputs`` is a dict of device tensors: q, kv_pool, qo_indptr, kv_indptr,
+    kv_indices, and optional q_scale / kv_scale (float32, 1 element)."""
+
+    def __init__(self, heads: int, q_len_max: int, q_dtype, kv_dtype, causal: bool,
+                 softmax_scale: float, mode: int = PLAN_AUTO, num_cus: Optional[int] = None,
+                 device=None):
+        import torch
+        self.torch = torch
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+        self.heads, self.q_len_max = heads, q_len_max
+        self.q_dtype, self.kv_dtype = _dtype_code(q_dtype), _dtype_code(kv_dtype)
+        self.causal, self.softmax_scale, self.mode = causal, softmax_scale, mode
+        if num_cus is None:
+            num_cus = torch.cuda.get_device_properties(self.device).multi_processor_count
+        self.num_cus = num_cus
+        self._plan_pinned = None
+        self._plan_dev = None
+        self._plan_copied = None   # event: the last host->device plan copy finished reading
+        self._ws = None
+
+    def make_plan(self, kv_lens) -> np.ndarray:
+        return plan(kv_lens, self.heads, self.q_len_max, self.kv_dtype, self.mode, self.num_cus)
+
+    def upload_plan(self, words: np.ndarray):
+        torch = self.torch
+        n = int(words.shape[0])
+        if self._plan_pinned is None or self._plan_pinned.numel() < n:
+            self._plan_pinned = torch.empty(max(n, 1024), dtype=torch.int32, pin_memory=True)
+            self._plan_dev = torch.empty(max(n, 1024), dtype=torch.int32, device=self.device)
+        if self._plan_copied is not None:
+            self._plan_copied.synchronize()   # the pinned buffer may still be in flight
+        self._plan_pinned[:n].copy_(torch.from_numpy(words))
+        self._plan_dev[:n].copy_(self._plan_pinned[:n], non_blocking=True)
+        self._plan_copied = torch.cuda.Event()
+        self._plan_copied.record()
+        return self._plan_dev
+
+    def workspace(self, words: np.ndarray):
+        nbytes = workspace_size(words)
+        if nbytes == 0:
+            return None
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = self.torch.empty(nbytes, dtype=self.torch.uint8, device=self.device)
+        return self._ws
+
+    def run(self, inputs: dict, kv_lens, o, lse, words: Optional[np.ndarray] = None):
+        """One pass of the hot path; returns the plan words used."""
+        if words is None:
+            words = self.make_plan(kv_lens)
+        plan_dev = self.upload_plan(words)
+        ws = self.workspace(words)
+        rows = int(len(kv_lens))
+        decode_fwd(inputs["q"], self.q_dtype, inputs.get("q_scale"), inputs["kv_pool"],
+                   self.kv_dtype, inputs.get("kv_scale"), inputs["qo_indptr"], inputs["kv_indptr"],
+                   inputs["kv_indices"], words, plan_dev, rows, self.heads, self.q_len_max,
+                   self.causal, self.softmax_scale, o, lse, ws)
+        return words
+
+
+def device_inputs(q_codes: np.ndarray, q_scale, pool_codes: np.ndarray, kv_scale,
+                  qo_indptr, kv_indptr, kv_indices, device="cuda") -> dict:
+    """Copy stored host arrays (bf16 bit patterns as uint16, fp8 codes as uint8,
+    int32 CSR lists, float scales or None) to device tensors."""
+    import torch
+
+    def codes(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(device)
+        if a.dtype == np.uint8:
+            return torch.from_numpy(a).to(device)
+        raise TypeError(f"stored codes must be uint16 (bf16) or uint8 (fp8), got {a.dtype}")
+
+    def scale(x):
+        return None if x is None else torch.tensor([float(x)], dtype=torch.float32, device=device)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).to(device)
+
+    return {"q": codes(q_codes), "q_scale": scale(q_scale), "kv_pool": codes(pool_codes),
+            "kv_scale": scale(kv_scale), "qo_indptr": i32(qo_indptr), "kv_indptr": i32(kv_indptr),
+            "kv_indices": i32(kv_indices)}

@@ -1,0 +1,156 @@
+// C ABI entry points: host-side validation, then the launches.
+//
+// Everything the library can check without touching device memory is checked
+// here, before any launch, and reported as a status code; a missing kernel or
+// an unsupported shape is never a process abort (the failure mode the
+// non-causal draft page reports for a kernel lookup miss, vLLM pull request
+// 53001, Purpose). A dtype mismatch is refused, never reinterpreted (the
+// review thread of vLLM pull request 57942 traces corrupted cache rows to an
+// fp32 tensor read as bf16).
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "kernel_args.h"
+#include "mla_internal.h"
+
+using namespace mla;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_dtype(int d) { return d == MLA_BF16 || d == MLA_FP8_E4M3; }
+
+int32_t check_plan_for_call(const int32_t* plan_host, const int32_t* plan_dev, int32_t rows,
+                            int32_t heads, int32_t q_len_max, int32_t kv_dtype, PlanView* v) {
+  if (!plan_dev) return set_error(MLA_ERR_INVALID_ARG, "plan_dev is null");
+  int32_t st = view_plan(plan_host, v);
+  if (st != MLA_OK) return st;
+  if (v->rows != rows) return set_error(MLA_ERR_PLAN_MISMATCH, "plan was built for a different row count");
+  if (v->heads != heads) return set_error(MLA_ERR_PLAN_MISMATCH, "plan was built for a different head count");
+  if (v->q_len_max != q_len_max)
+    return set_error(MLA_ERR_PLAN_MISMATCH, "plan was built for a different q_len_max");
+  if (v->kv_dtype != kv_dtype) return set_error(MLA_ERR_PLAN_MISMATCH, "plan was built for a different KV dtype");
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t mla_decode_fwd(const void* q, mla_dtype q_dtype, const float* q_scale,
+                                  const void* kv_pool, mla_dtype kv_dtype, const float* kv_scale,
+                                  int64_t num_slots, const int32_t* qo_indptr,
+                                  const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  const int32_t* plan_host, const int32_t* plan_dev, int32_t rows,
+                                  int32_t num_heads, int32_t q_len_max, int32_t causal,
+                                  float softmax_scale, void* o, float* lse, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+  clear_error();
+  if (!q || !kv_pool || !qo_indptr || !kv_indptr || !kv_indices || !plan_host || !o || !lse)
+    return set_error(MLA_ERR_INVALID_ARG, "a required pointer is null");
+  if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype))
+    return set_error(MLA_ERR_INVALID_ARG, "unknown dtype (expected MLA_BF16 or MLA_FP8_E4M3)");
+  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(o))
+    return set_error(MLA_ERR_INVALID_ARG, "q, kv_pool and o must be 16-byte aligned");
+  if (rows < 1) return set_error(MLA_ERR_INVALID_ARG, "rows must be >= 1");
+  if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
+    return set_error(MLA_ERR_UNSUPPORTED, "num_heads must be in 1..128");
+  if (q_len_max < 1 || q_len_max > MLA_MAX_Q_LEN)
+    return set_error(MLA_ERR_UNSUPPORTED, "q_len_max must be in 1..16");
+  if (causal != 0 && causal != 1) return set_error(MLA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return set_error(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (num_slots < 1 || num_slots > ((int64_t)1 << 31))
+    return set_error(MLA_ERR_INVALID_ARG, "num_slots must be in 1..2^31");
+  PlanView v;
+  int32_t st = check_plan_for_call(plan_host, plan_dev, rows, num_heads, q_len_max, kv_dtype, &v);
+  if (st != MLA_OK) return st;
+  const int64_t need = (int64_t)v.P * q_len_max * num_heads * (MLA_D_V + 1) * 4;
+  if (need > 0) {
+    if (!workspace) return set_error(MLA_ERR_WORKSPACE, "this plan needs a workspace");
+    if (workspace_bytes < need)
+      return set_error(MLA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+    if (!aligned16(workspace)) return set_error(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  const int64_t max_tokens = (int64_t)rows * q_len_max;
+  if (max_tokens * num_heads * MLA_D_LATENT > ((int64_t)1 << 40))
+    return set_error(MLA_ERR_UNSUPPORTED, "query tensor too large");
+
+  DecodeArgs a;
+  a.q = q;
+  a.q_scale = q_scale;
+  a.kv = kv_pool;
+  a.kv_scale = kv_scale;
+  a.qo_indptr = qo_indptr;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.plan = plan_dev;
+  a.off_split_row = (int32_t)v.off_split_row;
+  a.off_split_begin = (int32_t)v.off_split_begin;
+  a.off_split_end = (int32_t)v.off_split_end;
+  a.off_split_part = (int32_t)v.off_split_part;
+  a.off_work_indptr = (int32_t)v.off_work_indptr;
+  a.off_item_split = (int32_t)v.off_item_split;
+  a.off_item_m = (int32_t)v.off_item_m;
+  a.heads = num_heads;
+  a.q_len_max = q_len_max;
+  a.causal = causal;
+  a.score_scale_log2 = softmax_scale * 1.44269504088896340736f;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  const int64_t ws_o_elems = (int64_t)v.P * q_len_max * num_heads * MLA_D_V;
+  a.ws_o = need > 0 ? (float*)workspace : nullptr;
+  a.ws_lse = need > 0 ? (float*)workspace + ws_o_elems : nullptr;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_decode(a, q_dtype == MLA_FP8_E4M3, kv_dtype == MLA_FP8_E4M3, v.G, s);
+  if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
+  if (v.P > 0) {
+    MergeArgs mg;
+    mg.qo_indptr = qo_indptr;
+    mg.plan = plan_dev;
+    mg.off_split_indptr = (int32_t)v.off_split_indptr;
+    mg.off_split_part = (int32_t)v.off_split_part;
+    mg.heads = num_heads;
+    mg.q_len_max = q_len_max;
+    mg.ws_o = a.ws_o;
+    mg.ws_lse = a.ws_lse;
+    mg.o = a.o;
+    mg.lse = lse;
+    e = launch_merge(mg, rows, num_heads, q_len_max, s);
+    if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+  }
+  return MLA_OK;
+}
+
+extern "C" int32_t mla_debug_gather(const void* kv_pool, mla_dtype kv_dtype, int64_t num_slots,
+                                    const int32_t* kv_indptr, const int32_t* kv_indices,
+                                    const int32_t* plan_host, const int32_t* plan_dev,
+                                    int32_t rows, void* dense_out, void* stream) {
+  clear_error();
+  if (!kv_pool || !kv_indptr || !kv_indices || !plan_host || !dense_out)
+    return set_error(MLA_ERR_INVALID_ARG, "a required pointer is null");
+  if (!valid_dtype(kv_dtype)) return set_error(MLA_ERR_INVALID_ARG, "unknown kv_dtype");
+  if (!aligned16(kv_pool) || !aligned16(dense_out))
+    return set_error(MLA_ERR_INVALID_ARG, "kv_pool and dense_out must be 16-byte aligned");
+  if (num_slots < 1 || num_slots > ((int64_t)1 << 31))
+    return set_error(MLA_ERR_INVALID_ARG, "num_slots must be in 1..2^31");
+  if (!plan_dev) return set_error(MLA_ERR_INVALID_ARG, "plan_dev is null");
+  PlanView v;
+  int32_t st = view_plan(plan_host, &v);
+  if (st != MLA_OK) return st;
+  if (v.rows != rows) return set_error(MLA_ERR_PLAN_MISMATCH, "plan was built for a different row count");
+  if (v.kv_dtype != kv_dtype) return set_error(MLA_ERR_PLAN_MISMATCH, "plan was built for a different KV dtype");
+  GatherArgs g;
+  g.kv = kv_pool;
+  g.kv_indptr = kv_indptr;
+  g.kv_indices = kv_indices;
+  g.plan = plan_dev;
+  g.off_split_row = (int32_t)v.off_split_row;
+  g.off_split_begin = (int32_t)v.off_split_begin;
+  g.off_split_end = (int32_t)v.off_split_end;
+  g.dense = (uint16_t*)dense_out;
+  hipError_t e = launch_gather(g, kv_dtype == MLA_FP8_E4M3, v.S, (hipStream_t)stream);
+  if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("gather launch: ") + hipGetErrorString(e));
+  return MLA_OK;
+}

@@ -1,0 +1,58 @@
+// Kernel argument blocks and launchers (internal; shared by api.cpp and
+// kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mla {
+
+// Everything the decode kernel reads, by value. Plan arrays are addressed as
+// plan + off_*, offsets taken from the host copy of the plan header.
+struct DecodeArgs {
+  const void* q;
+  const float* q_scale;     // device scalar or null
+  const void* kv;
+  const float* kv_scale;    // device scalar or null
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* plan;
+  int32_t off_split_row, off_split_begin, off_split_end, off_split_part;
+  int32_t off_work_indptr, off_item_split, off_item_m;
+  int32_t heads, q_len_max, causal;
+  float score_scale_log2;   // softmax_scale * log2(e)
+  uint16_t* o;              // bf16 bits
+  float* lse;
+  float* ws_o;              // [P, q_len_max, heads, 512] fp32 partial O
+  float* ws_lse;            // [P, q_len_max, heads] fp32 partial LSE
+};
+
+struct MergeArgs {
+  const int32_t* qo_indptr;
+  const int32_t* plan;
+  int32_t off_split_indptr, off_split_part;
+  int32_t heads, q_len_max;
+  const float* ws_o;
+  const float* ws_lse;
+  uint16_t* o;
+  float* lse;
+};
+
+struct GatherArgs {
+  const void* kv;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* plan;
+  int32_t off_split_row, off_split_begin, off_split_end;
+  uint16_t* dense;          // bf16 [nnz, 576]
+};
+
+constexpr int kBlockThreads = 256;   // 4 waves of 64
+constexpr int kMergeHeadsPerBlock = 4;
+
+hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, int grid, hipStream_t st);
+hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, hipStream_t st);
+hipError_t launch_gather(const GatherArgs& a, bool kv_fp8, int splits, hipStream_t st);
+
+}  // namespace mla

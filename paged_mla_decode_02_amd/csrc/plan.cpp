@@ -1,0 +1,227 @@
+// Host split planner (plan spec version 1).
+//
+// A plan is a split count and split_indptr per request row, built on the host
+// next to the decode CSR ([DSV4] Tuned ASM FP8 decode with split plans, ATOM
+// pull request 2462, Summary part 1). UNIFORM plans depend only on the row
+// count, the longest row and the config (the same page: such plans keep graph
+// capture and replay in agreement); LENGTH_AWARE plans follow the real per-row
+// lengths on every call, as the persistent decode kernel of the same page does
+// (Summary part 2), whose gate (fp8 KV, 128 heads, 15..32768 rows) AUTO uses.
+//
+// On top of the splits the plan fixes the launch: work items are (split, tile
+// of 64 query rows); splits are ranked longest first and dealt to the eight
+// chiplets (XCDs), so that all M tiles of one split -- which read the same
+// keys -- run on one chiplet and share its L2. UNIFORM launches one workgroup
+// per item, ordering workgroup ids so that the hardware's round-robin
+// dispatch over chiplets lands each chiplet's items on it; LENGTH_AWARE
+// launches min(2 x CUs, items) persistent workgroups and gives each chiplet's
+// items to its least-loaded workgroup.
+#include <algorithm>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Item {
+  int32_t split, m;
+};
+
+}  // namespace
+
+int32_t view_plan(const int32_t* plan, PlanView* v) {
+  if (!plan) return set_error(MLA_ERR_INVALID_ARG, "plan is null");
+  if (plan[H_MAGIC] != kPlanMagic) return set_error(MLA_ERR_PLAN_MISMATCH, "plan magic mismatch");
+  if (plan[H_VERSION] != kPlanVersion || plan[H_HWORDS] != kHeaderWords)
+    return set_error(MLA_ERR_PLAN_MISMATCH, "plan from a different spec version");
+  v->rows = plan[H_ROWS];
+  v->heads = plan[H_HEADS];
+  v->q_len_max = plan[H_QLEN];
+  v->kv_dtype = plan[H_KVDTYPE];
+  v->mode = plan[H_MODE];
+  v->m_unit = plan[H_MUNIT];
+  v->u = plan[H_U];
+  v->S = plan[H_S];
+  v->W = plan[H_W];
+  v->G = plan[H_G];
+  v->P = plan[H_P];
+  v->total = plan[H_TOTAL];
+  if (v->rows < 1 || v->S < v->rows || v->W != (int64_t)v->S * v->u || v->G < 1 || v->P < 0 ||
+      v->P > v->S || v->m_unit != kMUnit)
+    return set_error(MLA_ERR_PLAN_MISMATCH, "plan header is inconsistent");
+  int64_t off = kHeaderWords;
+  v->off_split_indptr = off; off += v->rows + 1;
+  v->off_split_row = off; off += v->S;
+  v->off_split_begin = off; off += v->S;
+  v->off_split_end = off; off += v->S;
+  v->off_split_part = off; off += v->S;
+  v->off_work_indptr = off; off += v->G + 1;
+  v->off_item_split = off; off += v->W;
+  v->off_item_m = off; off += v->W;
+  if (off != v->total) return set_error(MLA_ERR_PLAN_MISMATCH, "plan length mismatch");
+  return MLA_OK;
+}
+
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" int32_t mla_decode_plan_capacity(int32_t rows, int32_t num_cus, int32_t num_heads,
+                                            int32_t q_len_max, int64_t* words_out) {
+  clear_error();
+  if (!words_out) return set_error(MLA_ERR_INVALID_ARG, "words_out is null");
+  if (rows < 1 || num_cus < 1) return set_error(MLA_ERR_INVALID_ARG, "rows and num_cus must be >= 1");
+  if (num_heads < 1 || num_heads > MLA_MAX_HEADS || q_len_max < 1 || q_len_max > MLA_MAX_Q_LEN)
+    return set_error(MLA_ERR_UNSUPPORTED, "heads must be 1..128 and q_len_max 1..16");
+  const int64_t u = cdiv((int64_t)num_heads * q_len_max, kMUnit);
+  // UNIFORM: S <= rows * N_MAX; LENGTH_AWARE: S <= rows + OCC * CUs.
+  const int64_t s_max = std::max<int64_t>((int64_t)rows * kNMax, (int64_t)rows + (int64_t)kOcc * num_cus);
+  const int64_t w_max = s_max * u;
+  *words_out = kHeaderWords + (rows + 1) + 4 * s_max + (w_max + 1) + 2 * w_max;
+  return MLA_OK;
+}
+
+extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t num_heads,
+                                   int32_t q_len_max, mla_dtype kv_dtype, mla_plan_mode mode,
+                                   int32_t num_cus, int32_t* plan, int64_t plan_words) {
+  clear_error();
+  if (!kv_lens || !plan) return set_error(MLA_ERR_INVALID_ARG, "kv_lens and plan must be non-null");
+  if (rows < 1 || rows > (1 << 24)) return set_error(MLA_ERR_UNSUPPORTED, "rows must be in 1..2^24");
+  if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
+    return set_error(MLA_ERR_UNSUPPORTED, "num_heads must be in 1..128");
+  if (q_len_max < 1 || q_len_max > MLA_MAX_Q_LEN)
+    return set_error(MLA_ERR_UNSUPPORTED, "q_len_max must be in 1..16");
+  if (kv_dtype != MLA_BF16 && kv_dtype != MLA_FP8_E4M3)
+    return set_error(MLA_ERR_INVALID_ARG, "unknown kv_dtype");
+  if (mode != MLA_PLAN_AUTO && mode != MLA_PLAN_UNIFORM && mode != MLA_PLAN_LENGTH_AWARE)
+    return set_error(MLA_ERR_INVALID_ARG, "unknown plan mode");
+  if (num_cus < 1) return set_error(MLA_ERR_INVALID_ARG, "num_cus must be >= 1");
+
+  int64_t sum_len = 0, max_len = 0;
+  for (int32_t b = 0; b < rows; ++b) {
+    if (kv_lens[b] < 0) return set_error(MLA_ERR_INVALID_ARG, "negative KV length");
+    sum_len += kv_lens[b];
+    max_len = std::max<int64_t>(max_len, kv_lens[b]);
+  }
+  if (sum_len > INT32_MAX) return set_error(MLA_ERR_UNSUPPORTED, "total KV length exceeds int32");
+
+  const int64_t u = cdiv((int64_t)num_heads * q_len_max, kMUnit);
+  int32_t used = mode;
+  if (used == MLA_PLAN_AUTO)
+    used = (kv_dtype == MLA_FP8_E4M3 && num_heads == 128 && rows >= 15 && rows <= 32768)
+               ? MLA_PLAN_LENGTH_AWARE
+               : MLA_PLAN_UNIFORM;
+
+  // Split counts.
+  std::vector<int32_t> nsplit(rows);
+  if (used == MLA_PLAN_UNIFORM) {
+    int64_t n = std::min(cdiv((int64_t)kOcc * num_cus, (int64_t)rows * u), cdiv(max_len, kMinSplitKeys));
+    n = std::clamp<int64_t>(n, 1, kNMax);
+    std::fill(nsplit.begin(), nsplit.end(), (int32_t)n);
+  } else {
+    const int64_t T = std::max<int64_t>(kMinSplitKeys, cdiv(u * sum_len, (int64_t)kOcc * num_cus));
+    for (int32_t b = 0; b < rows; ++b)
+      nsplit[b] = (int32_t)std::clamp<int64_t>(cdiv(kv_lens[b], T), 1, kNMax);
+  }
+
+  // Split CSR, key ranges, partial slots.
+  std::vector<int32_t> split_indptr(rows + 1, 0);
+  for (int32_t b = 0; b < rows; ++b) split_indptr[b + 1] = split_indptr[b] + nsplit[b];
+  const int32_t S = split_indptr[rows];
+  std::vector<int32_t> srow(S), sbeg(S), send(S), spart(S);
+  int32_t P = 0;
+  for (int32_t b = 0; b < rows; ++b) {
+    const int64_t L = kv_lens[b], n = nsplit[b];
+    for (int64_t k = 0; k < n; ++k) {
+      const int32_t s = split_indptr[b] + (int32_t)k;
+      srow[s] = b;
+      sbeg[s] = (int32_t)(k * L / n);
+      send[s] = (int32_t)((k + 1) * L / n);
+      spart[s] = n > 1 ? P++ : -1;
+    }
+  }
+
+  // Rank splits longest first and deal them to chiplets.
+  const int64_t W64 = (int64_t)S * u;
+  if (W64 > INT32_MAX) return set_error(MLA_ERR_UNSUPPORTED, "too many work items");
+  const int32_t W = (int32_t)W64;
+  const int32_t G = used == MLA_PLAN_UNIFORM ? W : (int32_t)std::min<int64_t>((int64_t)kOcc * num_cus, W);
+  const int32_t X = used == MLA_PLAN_UNIFORM ? kXcds : std::min(kXcds, G);
+  std::vector<int64_t> cost(S);
+  for (int32_t s = 0; s < S; ++s) cost[s] = (int64_t)send[s] - sbeg[s] + kItemOverhead;
+  std::vector<int32_t> rank(S);
+  std::iota(rank.begin(), rank.end(), 0);
+  std::stable_sort(rank.begin(), rank.end(), [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+  std::vector<std::vector<Item>> chiplet(X);
+  for (int32_t k = 0; k < S; ++k)
+    for (int32_t m = 0; m < (int32_t)u; ++m) chiplet[k % X].push_back({rank[k], m});
+
+  // Workgroups.
+  std::vector<int32_t> work_indptr(G + 1, 0);
+  std::vector<Item> items;
+  items.reserve(W);
+  if (used == MLA_PLAN_UNIFORM) {
+    std::vector<Item> by_id(W);
+    size_t n_min = SIZE_MAX, n_max = 0;
+    for (auto& c : chiplet) { n_min = std::min(n_min, c.size()); n_max = std::max(n_max, c.size()); }
+    for (int32_t x = 0; x < X; ++x)
+      for (size_t j = 0; j < n_min; ++j) by_id[(size_t)kXcds * j + x] = chiplet[x][j];
+    size_t next = (size_t)kXcds * n_min;
+    for (size_t j = n_min; j < n_max; ++j)
+      for (int32_t x = 0; x < X; ++x)
+        if (j < chiplet[x].size()) by_id[next++] = chiplet[x][j];
+    items = by_id;
+    for (int32_t g = 0; g <= G; ++g) work_indptr[g] = g;
+  } else {
+    std::vector<std::vector<Item>> groups(G);
+    std::vector<int64_t> load(G, 0);
+    for (int32_t x = 0; x < X; ++x) {
+      for (const Item& it : chiplet[x]) {
+        int32_t best = -1;
+        for (int32_t g = x; g < G; g += X)   // workgroups of chiplet x
+          if (best < 0 || load[g] < load[best]) best = g;
+        groups[best].push_back(it);
+        load[best] += cost[it.split];
+      }
+    }
+    for (int32_t g = 0; g < G; ++g) {
+      items.insert(items.end(), groups[g].begin(), groups[g].end());
+      work_indptr[g + 1] = (int32_t)items.size();
+    }
+  }
+
+  const int64_t total = kHeaderWords + (rows + 1) + 4 * (int64_t)S + (G + 1) + 2 * (int64_t)W;
+  if (total > plan_words) return set_error(MLA_ERR_INVALID_ARG, "plan buffer too small");
+  int32_t* w = plan;
+  const int32_t header[kHeaderWords] = {kPlanMagic, kPlanVersion, rows, num_heads, q_len_max,
+                                        (int32_t)kv_dtype, num_cus, used, kMUnit, (int32_t)u,
+                                        kNMax, kMinSplitKeys, kItemOverhead, kOcc, S, W, G, P,
+                                        kHeaderWords, (int32_t)total};
+  std::memcpy(w, header, sizeof(header));
+  w += kHeaderWords;
+  auto put = [&](const std::vector<int32_t>& a) { std::memcpy(w, a.data(), a.size() * 4); w += a.size(); };
+  put(split_indptr);
+  put(srow);
+  put(sbeg);
+  put(send);
+  put(spart);
+  put(work_indptr);
+  for (const Item& it : items) *w++ = it.split;
+  for (const Item& it : items) *w++ = it.m;
+  return MLA_OK;
+}
+
+extern "C" int32_t mla_decode_workspace_size(const int32_t* plan, int64_t* bytes_out) {
+  clear_error();
+  if (!bytes_out) return set_error(MLA_ERR_INVALID_ARG, "bytes_out is null");
+  PlanView v;
+  int32_t st = view_plan(plan, &v);
+  if (st != MLA_OK) return st;
+  *bytes_out = (int64_t)v.P * v.q_len_max * v.heads * (MLA_D_V + 1) * 4;
+  return MLA_OK;
+}

@@ -1,0 +1,194 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on the
+same seeded inputs. Run on an MI355X; skipped elsewhere."""
+import numpy as np
+import pytest
+
+from oracle.attention import attend_case, gather_rows
+from oracle.codecs import decode
+from oracle.plan import unpack_plan
+from tests.gpu_harness import run_gpu, assert_parity, compare, tolerance
+from workloads import make_case, make_config, BF16, FP8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    import torch
+    import paged_mla_decode_02_amd as mla
+    assert torch.cuda.is_available()
+    mla.load_library()     # raises if the HIP library was not built
+    return mla
+
+
+def bf16_bits_of(values: np.ndarray) -> np.ndarray:
+    """Exact bf16 bit patterns of values that are bf16-representable."""
+    f = values.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), values)
+    bits = f.view(np.uint32)
+    assert not (bits & 0xFFFF).any()
+    return (bits >> 16).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# Index gather, bit-exact
+
+@pytest.mark.parametrize("kv_dtype", [BF16, FP8])
+@pytest.mark.parametrize("offset", [0, 45])
+def test_gather_bit_exact(lib, kv_dtype, offset):
+    import torch
+    lens = [0, 1, 31, 32, 33, 100, 257, 1000]
+    case = make_case(21, lens, heads=16, q_len=1, q_dtype=BF16, kv_dtype=kv_dtype, causal=True,
+                     pool_slots=8192, kv_indptr_offset=offset)
+    if kv_dtype == FP8:
+        # every finite e4m3fn code appears in the pool
+        codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+        case.pool_codes[:4] = np.resize(codes, (4, 576))
+        case.kv_indices[offset:offset + 4] = [0, 1, 2, 3]
+    words = lib.plan(case.kv_lens, 16, 1, kv_dtype, lib.PLAN_UNIFORM, 64)
+    assert unpack_plan(words)["S"] > len(lens)          # rows really are split
+    dev = lib.device_inputs(case.q_codes, None, case.pool_codes, case.kv_scale, case.qo_indptr,
+                            case.kv_indptr, case.kv_indices)
+    plan_dev = torch.from_numpy(words).cuda()
+    nnz = int(case.kv_indptr[-1] - case.kv_indptr[0])
+    dense = torch.zeros((nnz, 576), dtype=torch.int16, device="cuda")
+    lib.debug_gather(dev["kv_pool"], kv_dtype, dev["kv_indptr"], dev["kv_indices"], words, plan_dev,
+                     case.rows, dense)
+    torch.cuda.synchronize()
+    got = dense.cpu().numpy().view(np.uint16)
+    for b in range(case.rows):
+        ref = gather_rows(case.pool_codes, kv_dtype, None, case.kv_indptr, case.kv_indices, b)
+        lo = int(case.kv_indptr[b] - case.kv_indptr[0])
+        assert np.array_equal(got[lo:lo + len(ref)], bf16_bits_of(ref)), f"row {b}"
+
+
+# --------------------------------------------------------------------------
+# The five workloads (full size; the oracle checks a sample of rows)
+
+CONFIG_SAMPLES = {
+    "tiny_causal": None,
+    "verify_causal": "extremes",
+    "draft_noncausal": [0, 7],
+    "longctx_split": [0, 3],
+    "ragged_persistent_causal": "extremes",
+    "ragged_persistent_noncausal": "extremes",
+}
+
+
+def sample_rows(case, how):
+    if how is None:
+        return None
+    if how == "extremes":
+        lens = case.kv_lens
+        order = np.argsort(lens, kind="stable")
+        pick = {int(order[0]), int(order[-1]), int(order[len(order) // 2]), 1, case.rows - 1}
+        return sorted(pick)
+    return how
+
+
+@pytest.mark.parametrize("name", list(CONFIG_SAMPLES))
+def test_workload_parity(lib, name):
+    case = make_config(name)
+    O, LSE, words = run_gpu(case)
+    rows = sample_rows(case, CONFIG_SAMPLES[name])
+    ratio, lse_err = assert_parity(case, O, LSE, rows)
+    print(f"{name}: err/max={ratio:.2e} lse_err={lse_err:.2e} plan S={unpack_plan(words)['S']}")
+    assert not np.isnan(O).any() and not np.isnan(LSE).any()
+
+
+# --------------------------------------------------------------------------
+# Shapes, dtypes, masks and plans on small inputs (full oracle check)
+
+SMALL = [
+    # (heads, q_len, q_dtype, kv_dtype, causal, lens, mode, num_cus)
+    (16, 1, BF16, BF16, True, [37, 128], 0, 256),
+    (1, 1, BF16, BF16, True, [1, 2, 300], 0, 256),
+    (8, 4, BF16, BF16, True, [0, 5, 64, 65, 700], 0, 256),
+    (12, 3, BF16, FP8, False, [33, 31, 1000], 0, 256),
+    (24, 16, BF16, BF16, True, [16, 17, 400], 0, 256),
+    (32, 2, FP8, FP8, True, [90, 3, 2048], 0, 256),
+    (64, 8, FP8, FP8, False, [512, 1023], 0, 256),
+    (96, 5, FP8, BF16, True, [200, 7, 1500], 0, 256),
+    (128, 1, BF16, FP8, True, [4000, 50, 0, 9000], 1, 256),         # uniform, many splits
+    (128, 2, BF16, FP8, False, [4000, 50, 0, 9000] * 4, 2, 256),    # length-aware
+    (128, 8, BF16, BF16, True, [2048, 100], 1, 256),
+    (128, 16, BF16, BF16, True, [3, 20, 5000], 1, 16),               # q_len > L for row 0
+    (7, 9, BF16, FP8, True, [1, 0, 9], 1, 2),                        # heads not a multiple of 16
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"h{c[0]}q{c[1]}{c[2]}{c[3]}{'c' if c[4] else 'n'}m{c[6]}")
+def test_small_parity(lib, cfg):
+    H, q, qd, kd, causal, lens, mode, C = cfg
+    case = make_case(1000 + H * 17 + q, lens, heads=H, q_len=q, q_dtype=qd, kv_dtype=kd,
+                     causal=causal, pool_slots=max(4096, 2 * sum(lens)))
+    O, LSE, words = run_gpu(case, mode=mode, num_cus=C)
+    assert_parity(case, O, LSE)
+
+
+@pytest.mark.parametrize("heads", [1, 8, 12, 16, 24, 32, 64, 96, 128])
+def test_head_sweep(lib, heads):
+    case = make_case(50 + heads, [300, 77], heads=heads, q_len=2, q_dtype=BF16, kv_dtype=BF16,
+                     causal=True, pool_slots=4096)
+    O, LSE, _ = run_gpu(case)
+    assert_parity(case, O, LSE)
+
+
+@pytest.mark.parametrize("q_len", list(range(1, 17)))
+@pytest.mark.parametrize("kv_dtype", [BF16, FP8])
+def test_block_length_sweep(lib, q_len, kv_dtype):
+    # includes the fp8 2-token block
+    case = make_case(80 + q_len, [q_len + 5, 130], heads=16, q_len=q_len, q_dtype=BF16,
+                     kv_dtype=kv_dtype, causal=(q_len % 2 == 0), pool_slots=4096)
+    O, LSE, _ = run_gpu(case)
+    assert_parity(case, O, LSE)
+
+
+def test_ragged_blocks_and_offset_indptr(lib):
+    case = make_case(91, [40, 0, 300, 17, 5], heads=16, q_len=6, q_dtype=BF16, kv_dtype=FP8,
+                     causal=True, pool_slots=4096, q_lens=[6, 2, 0, 6, 1], kv_indptr_offset=13)
+    O, LSE, _ = run_gpu(case, mode=1, num_cus=8)
+    assert_parity(case, O, LSE)
+
+
+def test_forced_split_matches_unsplit(lib):
+    case = make_case(92, [6000, 3000], heads=64, q_len=2, q_dtype=BF16, kv_dtype=BF16,
+                     causal=True, pool_slots=16384)
+    O1, L1, w1 = run_gpu(case, mode=1, num_cus=1)       # one split per row
+    O2, L2, w2 = run_gpu(case, mode=1, num_cus=256)     # many splits + merge
+    assert unpack_plan(w1)["S"] == 2 and unpack_plan(w2)["S"] > 2
+    ref = attend_case(case)
+    assert_parity(case, O1, L1, ref=ref)
+    assert_parity(case, O2, L2, ref=ref)
+    assert np.abs(O1 - O2).max() <= 1e-2 * np.abs(O1).max()
+
+
+def test_mask_discrimination(lib):
+    """The kernel runs the mask that was asked for: close to the right-mask
+    reference, far from the wrong one (the check the non-causal draft page
+    reports)."""
+    for causal in (True, False):
+        case = make_case(93, [64, 200], heads=16, q_len=8, q_dtype=BF16, kv_dtype=FP8,
+                         causal=causal, pool_slots=4096)
+        O, LSE, _ = run_gpu(case)
+        right, _ = compare(case, O, LSE, ref=attend_case(case, causal=causal))
+        wrong_ref = attend_case(case, causal=not causal)
+        refmax = max(float(np.abs(v[0]).max()) for v in wrong_ref.values())
+        wrong = max(float(np.abs(O[case.qo_indptr[b]:case.qo_indptr[b + 1]] - v[0]).max())
+                    for b, v in wrong_ref.items()) / refmax
+        assert right <= tolerance(case)
+        assert wrong > 10 * right, (right, wrong)
+
+
+def test_deterministic_and_identical_rows(lib):
+    case = make_case(94, [500, 500, 500, 500], heads=16, q_len=4, q_dtype=BF16, kv_dtype=FP8,
+                     causal=False, pool_slots=4096, shared_slots=True)
+    for r in range(1, 4):
+        case.q_codes[4 * r:4 * r + 4] = case.q_codes[0:4]
+    O1, L1, _ = run_gpu(case)
+    O2, L2, _ = run_gpu(case)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    for r in range(1, 4):
+        assert np.array_equal(O1[4 * r:4 * r + 4], O1[0:4])
+        assert np.array_equal(L1[4 * r:4 * r + 4], L1[0:4])
+    assert_parity(case, O1, L1)

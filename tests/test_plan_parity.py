@@ -1,0 +1,71 @@
+"""The library's C++ planner must produce the oracle's plan words exactly
+(CPU only: the planner is host code)."""
+import numpy as np
+import pytest
+
+from oracle.plan import plan_ref, MODE_AUTO, MODE_UNIFORM, MODE_LENGTH_AWARE
+from workloads import CONFIGS, config_lengths, FP8
+
+lib = pytest.importorskip("paged_mla_decode_02_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    from tests.lib_build import ensure_built
+    ensure_built()
+
+
+def _same(lens, H, q, kv, mode, C):
+    ref = plan_ref(lens, H, q, kv, mode, C)
+    got = lib.plan(lens, H, q, kv, mode, C)
+    assert got.dtype == np.int32
+    assert got.shape == ref.shape and np.array_equal(got, ref), (lens[:8], H, q, kv, mode, C)
+
+
+def test_fixtures_match():
+    _same([1000, 0, 700], 16, 1, 0, MODE_UNIFORM, 4)
+    _same([1000, 300, 5000, 0], 128, 1, 1, MODE_LENGTH_AWARE, 4)
+
+
+def test_random_plans_match_oracle():
+    rng = np.random.default_rng(1234)
+    for t in range(3000):
+        R = int(rng.integers(1, 48))
+        kind = t % 4
+        if kind == 0:
+            lens = rng.integers(0, 3000, R)
+        elif kind == 1:
+            lens = np.clip(np.rint(np.exp(rng.normal(6.0, 1.5, R))), 0, 200000).astype(int)
+        elif kind == 2:
+            lens = np.zeros(R, int)
+            lens[rng.integers(0, R)] = int(rng.integers(0, 100000))
+        else:
+            lens = rng.integers(0, 40, R)
+        H = int(rng.choice([1, 7, 16, 32, 64, 96, 128, int(rng.integers(1, 129))]))
+        q = int(rng.integers(1, 17))
+        C = int(rng.choice([1, 3, 8, 20, 64, 256, 304]))
+        mode = int(rng.integers(0, 3))
+        kv = int(rng.integers(0, 2))
+        _same([int(x) for x in lens], H, q, kv, mode, C)
+
+
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_workload_plans_match_oracle(name):
+    spec = CONFIGS[name]
+    lens = [int(x) for x in config_lengths(name)]
+    kv = 1 if spec["kv_dtype"] == FP8 else 0
+    _same(lens, spec["heads"], spec["q_len"], kv, MODE_AUTO, 256)
+
+
+def test_capacity_bounds_every_plan():
+    rng = np.random.default_rng(99)
+    for _ in range(300):
+        R = int(rng.integers(1, 64))
+        H = int(rng.integers(1, 129))
+        q = int(rng.integers(1, 17))
+        C = int(rng.integers(1, 400))
+        cap = lib.plan_capacity(R, C, H, q)
+        for mode in (MODE_UNIFORM, MODE_LENGTH_AWARE):
+            lens = [int(x) for x in rng.integers(0, 300000, R)]
+            w = lib.plan(lens, H, q, 1, mode, C)
+            assert len(w) <= cap
