@@ -1,38 +1,42 @@
 // Paged MLA decode kernels for CDNA4 (gfx950).
 //
-// One workgroup of 4 waves runs a work item: 64 query rows (token i, head h,
-// ordered i * heads + h) of one request row against one split of its keys.
-// Each wave owns 16 query rows and keeps their queries (576 dims, bf16) in
-// registers for the whole item. Keys stream through LDS in tiles of 32 latent
-// rows: the tile's slots come from the row's page-size-1 index list (vLLM
-// pull request 53001, Purpose: one row per request, one flat index list),
-// each row is fetched once with 16-byte loads straight into LDS and shared by
-// all 64 query rows, i.e. by all heads, since MLA has a single latent KV head.
+// One workgroup of 8 waves per compute unit runs a work item at a time: 64
+// query rows (token i, head h, ordered i * heads + h) of one request row
+// against one split of its keys. Keys stream through LDS in tiles of 32 latent
+// rows: the tile's slots come from the row's page-size-1 index list (vLLM pull
+// request 53001, Purpose: one row per request, one flat index list); each row
+// is fetched once with 16-byte loads straight into LDS and shared by all 64
+// query rows, i.e. by all heads, since MLA has a single latent KV head.
 //
-// Per tile and wave:
-//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16, keys are the MFMA M side, the
-//                  576-dim latent the contraction): two 16-key blocks x 18
-//                  k-steps; the output leaves each lane with 8 scores of one
-//                  query row.
-//   mask          causal on positions -- token i of a q_b-token block sits at
-//                 L - q_b + i and sees keys j <= L - q_b + i (ATOM pull
-//                 request 2760, Problem) -- or only the split's key range for
-//                 a non-causal draft block (vLLM pull request 53001, Purpose).
-//   softmax       online, base 2 (log2 e folded into the score scale); the
-//                 row max is a cross-lane max over the four 16-lane groups;
-//                 the running reference max only moves when a row's tile max
-//                 exceeds it by more than 8 (so exp2 stays <= 256), which
-//                 skips most rescales of the 128 accumulator registers.
-//   O^T += V^T P^T  P^T stays in the registers it was computed in: the lane's
-//                   8 scores are exactly its B operand once keys are taken in
-//                   the order {4g..4g+3, 16+4g..16+4g+3} for lane group g; V^T
-//                   comes from the same LDS tile (V = the first 512 latent
-//                   dims, no second load) through ds_read_b64_tr_b16, read in
-//                   that same key order.
+// The waves are specialized, two per SIMD, and work one tile apart:
+//   QK team   waves 0..3; wave q owns query rows 16q..16q+15 and keeps their
+//             queries (576 dims, bf16) in registers. For tile t it computes
+//             S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (keys are the MFMA M
+//             side, the 576-dim latent the contraction), applies the mask --
+//             causal on positions, token i of a q_b-token block sits at
+//             L - q_b + i and sees keys j <= L - q_b + i (ATOM pull request
+//             2760, Problem), or only the split's range for a non-causal draft
+//             block (vLLM pull request 53001, Purpose) -- and runs the online
+//             softmax in base 2. It publishes P^T (bf16) and per-row rescale
+//             factors in LDS. The running reference max only moves when a
+//             row's tile max exceeds it by more than 8, so most tiles need no
+//             rescale of the accumulators.
+//   PV team   waves 4..7; wave p owns output columns 128p..128p+127 of all 64
+//             rows and accumulates O^T += V^T P^T for tile t-1, V being the
+//             first 512 dims of the same LDS tile (no second load), read
+//             transposed with ds_read_b64_tr_b16; each V^T fragment feeds the
+//             four row blocks.
+// While one team waits on its softmax or its LDS reads, the other keeps the
+// SIMD's matrix core busy; one barrier per tile hands P^T over. The lane
+// layout of an S^T accumulator is exactly the B operand of the PV MFMA once
+// the 32 keys are taken in the order {4g..4g+3, 16+4g..16+4g+3} for lane
+// group g, so P never needs a register shuffle; the V^T reads use the same
+// key order.
+//
 // fp8 KV is fetched as fp8 (half the HBM bytes) into a staging tile and
-// converted once per tile to the bf16 tile (exact: every e4m3fn value is a
-// bf16 value), so the compute core is the same for all dtypes; fp8 Q is
-// converted to bf16 at load. Scales are applied to the fp32 scores and to O.
+// converted once per tile to a bf16 tile (exact: every e4m3fn value is a bf16
+// value), so the compute core is the same for all dtypes; fp8 Q is converted
+// to bf16 at load. Scales are applied to the fp32 scores and to O.
 //
 // The epilogue writes bf16 O and the natural-log LSE when the row has one
 // split, or the split's fp32 partial (O_k, LSE_k) to the workspace; the merge
@@ -41,13 +45,18 @@
 //
 // LDS tile layout (bf16): a "main" array of 32 rows x 1024 bytes (latent dims
 // 0..511, which are also V) and a "rope" array of 32 rows x 128 bytes (dims
-// 512..575). One wave-wide 16-byte direct-to-LDS load then covers exactly one
-// main row, so its pool slot is wave-uniform. Within each aligned group of 8
-// 16-byte chunks of a row, chunk c is stored at c ^ swz(row); the swizzle is
-// applied on the global side of the load (the LDS side of a direct load is
-// fixed to 64 consecutive chunks) and keeps the K reads (8 lanes, 8 keys,
-// same chunk) and the transposed V reads (16 lanes, 4 keys x 32 bytes) on
-// distinct banks.
+// 512..575). One wave-wide 16-byte direct-to-LDS load covers exactly one main
+// row, so its pool slot is wave-uniform. The LDS has 64 four-byte banks: main
+// chunk c of row r is stored at c ^ (r & 15) (inside its aligned group of 16
+// chunks) and rope chunk c at c ^ ((r >> 1) & 7), which keeps the K reads (16
+// lanes, 16 keys, same chunk) and the transposed V reads (16 lanes, 4 keys x 32
+// bytes) on distinct banks. The swizzle is applied on the global side of each
+// load (the LDS side of a direct load is fixed to consecutive 16-byte chunks).
+//
+// Loads run two tiles ahead. Every wave issues the same number of loads per
+// tile and waits for its own with an exact vmcnt before the barrier that
+// publishes the tile; the loads are inline assembly, so the compiler neither
+// waits for them early nor tracks them.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <type_traits>
@@ -78,36 +87,50 @@ constexpr int kF8MainRow = 512, kF8RopeRow = 64;
 constexpr int kF8MainBytes = kNT * kF8MainRow;        // 16384
 constexpr int kF8TileBytes = kF8MainBytes + kNT * kF8RopeRow;  // 18432
 constexpr int kKSteps = kDLat / 32;           // 18 QK k-steps (16 main + 2 rope)
-constexpr int kColTiles = kDV / 16;           // 32 PV column tiles
-constexpr int kLdsBytes = 2 * kTileBytes;     // 73728 for either KV dtype
+constexpr int kWaves = kDecodeThreads / 64;   // 8
+constexpr int kTeam = kWaves / 2;             // 4 waves per team
+constexpr int kRowBlocks = 4;                 // 16-row blocks per work item
+constexpr int kWaveCols = kDV / kTeam;        // 128 output columns per PV wave
+constexpr int kWaveColTiles = kWaveCols / 16; // 8
+constexpr int kBufs = 4;                      // tile buffers (bf16 KV) / staging tiles (fp8 KV)
+constexpr int kAhead = 2;                     // tiles in flight
+constexpr int kSlotRing = 4;                  // per-wave ring of tile slot lists
+constexpr int kTilesBytes = kBufs * kTileBytes;       // 147456 for either KV dtype
+constexpr int kOffP = kTilesBytes;                    // P^T [2][4 row blocks][64 lanes] bf16x8
+constexpr int kOffAlpha = kOffP + 2 * kRowBlocks * 64 * 16;   // [2][64] f32 rescale factors
+constexpr int kOffFlags = kOffAlpha + 2 * 64 * 4;     // [2][4] u32 "any rescale" per QK wave
+constexpr int kOffL = kOffFlags + 2 * 16;             // [64] f32 row sums (epilogue)
+constexpr int kOffSlots = kOffL + 64 * 4;             // [8 waves][4][32] int32
+constexpr int kSmemBytes = kOffSlots + kWaves * kSlotRing * kNT * 4;   // 160544
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;
+static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
 
-// LDS offsets. bf16 KV: two tiles, ropes first so that every immediate
-// offset of a ds_read stays below 64 KB. fp8 KV: one bf16 tile and two fp8
-// staging tiles (main 16 KB + rope 2 KB each).
+// LDS offsets of the compute tiles. bf16 KV: four tiles, ropes first, loaded
+// directly. fp8 KV: two bf16 compute tiles (QK on tile t, PV on tile t-1) and
+// four fp8 staging tiles (main 16 KB + rope 2 KB each) that the loads target.
 template <bool KV_FP8> struct Layout;
 template <> struct Layout<false> {
-  static constexpr int rope(int buf) { return buf * kRopeBytes; }
-  static constexpr int main(int buf) { return 2 * kRopeBytes + buf * kMainBytes; }
+  static constexpr int rope(int t) { return (t % kBufs) * kRopeBytes; }
+  static constexpr int main(int t) { return kBufs * kRopeBytes + (t % kBufs) * kMainBytes; }
 };
 template <> struct Layout<true> {
-  static constexpr int rope(int) { return 0; }
-  static constexpr int main(int) { return kRopeBytes; }
-  static constexpr int stage(int buf) { return kTileBytes + buf * kF8TileBytes; }
+  static constexpr int rope(int t) { return (t % 2) * kRopeBytes; }
+  static constexpr int main(int t) { return 2 * kRopeBytes + (t % 2) * kMainBytes; }
+  static constexpr int stage(int t) { return 2 * kTileBytes + (t % kBufs) * kF8TileBytes; }
 };
+static_assert(Layout<true>::stage(kBufs - 1) + kF8TileBytes <= kTilesBytes, "fp8 layout");
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int swz_main(int row) { return row & 15; }
+__device__ __forceinline__ int swz_rope(int row) { return (row >> 1) & 7; }
 
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// 16-byte direct-to-LDS loads (global_load_lds_dwordx4): lane l's 16 bytes
-// land at LDS byte address lds_addr + 16 l. Issued as inline assembly so the
-// compiler does not treat them as pending LDS writes: it would otherwise wait
-// for the next tile's loads before every LDS read of the current tile. Their
-// completion is awaited explicitly (wait_vm_all) before the barrier that
-// publishes a tile. The compiler never uses M0 in these kernels (checked on
-// the generated code), so setting it here is safe.
+// 16-byte (and 4-byte) direct-to-LDS loads: lane l's data lands at LDS byte
+// address lds_addr + 16 l (4 l). Inline assembly keeps them out of the
+// compiler's wait-count tracking (it would otherwise wait for the next tiles'
+// loads before every LDS read of the current one); completion is awaited
+// explicitly with wait_vm before the barrier that publishes a tile. The
+// compiler never uses M0 in these kernels (checked on the generated code), so
+// setting it here is safe.
 __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(lds_addr), "v"(voff), "s"(sbase) : "memory");
@@ -116,8 +139,26 @@ __device__ __forceinline__ void dma16_vaddr(const void* vaddr, uint32_t lds_addr
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds_addr), "v"(vaddr) : "memory");
 }
+__device__ __forceinline__ void dma4_vaddr(const void* vaddr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds_addr), "v"(vaddr) : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N> __device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_vm_all() { wait_vm<0>(); }
 
 __device__ __forceinline__ uint32_t lds_addr_of(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
+
+// A copy of v the compiler cannot see through: values derived from it inside
+// the tile loop are recomputed there (a few VALU ops) instead of being hoisted
+// out of the loop and kept live.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 template <typename T> __device__ __forceinline__ T lds_load(const lds_u8* base, int off) {
   return *(const __attribute__((address_space(3))) T*)(base + off);
@@ -139,9 +180,68 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 
 // ---------------------------------------------------------------------------
 // Tile loader (shared by the decode kernel and the gather test hook).
-//
-// Every lane loads the slot of key (lane & 31) of the tile; keys past the
-// split's end repeat the last valid key (finite data, masked later).
+
+// Issue one tile's direct-to-LDS loads (8 waves); slot_lane: lane j < 32
+// holds the pool slot of the tile's key j. bf16: wave w loads main rows 8i + w
+// (one 1 KB row per instruction, its slot read from lane j) and rope rows
+// 4w..4w+3 (half a wave). fp8: main rows 2k, 2k + 1 for k = 8i + w (two
+// 512-byte rows per instruction) and rope rows 4w..4w+3 (a quarter wave), into
+// the linear staging tile. Every wave issues the same number of loads.
+template <bool KV_FP8> struct TileLoads { static constexpr int n = KV_FP8 ? 3 : 5; };
+
+template <bool KV_FP8>
+__device__ __forceinline__ void issue_tile(const unsigned char* kv, int slot_lane, lds_u8* smem,
+                                           int main_off, int rope_off, int wave, int lane_in) {
+  const int lane = opaque(lane_in);
+  const uint32_t lds0 = lds_addr_of(smem);
+  if constexpr (!KV_FP8) {
+#pragma unroll
+    for (int i = 0; i < kNT / kWaves; ++i) {
+      const int j = kWaves * i + wave;
+      const int slot = __builtin_amdgcn_readlane(slot_lane, j);   // wave-uniform
+      const unsigned char* row = kv + (int64_t)slot * (2 * kDLat);
+      dma16_sbase(row, (uint32_t)((lane ^ (j & 15)) << 4), lds0 + main_off + j * kMainRow);
+    }
+    const int j = 4 * wave + (lane >> 3);
+    const int slot = __shfl(slot_lane, j & 31, 64);
+    const unsigned char* src =
+        kv + (int64_t)slot * (2 * kDLat) + kMainRow + (((lane & 7) ^ swz_rope(j)) << 4);
+    if (lane < 32) dma16_vaddr(src, lds0 + rope_off + wave * 512);
+  } else {
+    const uint32_t stage = lds0 + main_off;   // staging tile: main then rope
+    const uint32_t off = (uint32_t)((lane & 31) << 4);
+#pragma unroll
+    for (int i = 0; i < 16 / kWaves; ++i) {
+      const int k = kWaves * i + wave;            // rows 2k (lanes 0-31) and 2k + 1
+      const int slot = __shfl(slot_lane, 2 * k + (lane >> 5), 64);
+      dma16_vaddr(kv + (int64_t)slot * kDLat + off, stage + k * 1024);
+    }
+    const int j = 4 * wave + (lane >> 2);         // lanes 0-15: rope rows 4w..4w+3
+    const int slot = __shfl(slot_lane, j & 31, 64);
+    const unsigned char* src = kv + (int64_t)slot * kDLat + kF8MainRow + ((lane & 3) << 4);
+    if (lane < 16) dma16_vaddr(src, stage + kF8MainBytes + wave * 256);
+    (void)rope_off;
+  }
+}
+
+// DMA the slot list of tile `tile` (32 int32, keys clamped to the split) into
+// this wave's private ring entry (one load, lanes 0-31).
+__device__ __forceinline__ void issue_slots(const int32_t* kv_indices, int kv0, int begin, int end,
+                                            int tile, lds_u8* smem, int wave, int lane) {
+  int key = begin + tile * kNT + (lane & 31);
+  key = key < end ? key : end - 1;
+  const uint32_t dst =
+      lds_addr_of(smem) + kOffSlots + (wave * kSlotRing + (tile % kSlotRing)) * kNT * 4;
+  if (lane < 32) dma4_vaddr(kv_indices + kv0 + key, dst);
+}
+
+__device__ __forceinline__ int read_slots(const lds_u8* smem, int tile, int wave, int lane) {
+  return lds_load<int>(smem, kOffSlots + (wave * kSlotRing + (tile % kSlotRing)) * kNT * 4 +
+                                 (lane & 31) * 4);
+}
+
+// Slot of key (lane & 31) of a tile, straight from global memory (used by the
+// gather hook, which loads one tile at a time).
 __device__ __forceinline__ int load_tile_slot(const int32_t* kv_indices, int kv0, int key0, int end,
                                               int lane) {
   int key = key0 + (lane & 31);
@@ -149,128 +249,106 @@ __device__ __forceinline__ int load_tile_slot(const int32_t* kv_indices, int kv0
   return kv_indices[kv0 + key];
 }
 
-// Issue one tile's direct-to-LDS loads. bf16: wave w loads main rows 4i + w
-// (one 1 KB row per instruction, slot read from lane j) and rope rows 8w..8w+7.
-// fp8: 16 main instructions of two rows each and 2 rope instructions, into
-// the linear staging tile.
-template <bool KV_FP8>
-__device__ __forceinline__ void issue_tile(const unsigned char* kv, int slot_lane, lds_u8* smem,
-                                           int buf, int wave, int lane) {
-  const uint32_t lds0 = lds_addr_of(smem);
-  if constexpr (!KV_FP8) {
-    // Rows 4i + wave have swizzle (wave << 1) | (i & 1): two per-lane offsets.
-    const uint32_t off_even = (uint32_t)((lane ^ (wave << 1)) << 4);
-    const uint32_t off_odd = (uint32_t)((lane ^ ((wave << 1) | 1)) << 4);
+// fp8 staging tile -> swizzled bf16 tile (512 threads): a 16-byte fp8 chunk
+// becomes two bf16 chunks.
+__device__ __forceinline__ void convert_tile(lds_u8* smem, int stage, int main_off, int rope_off,
+                                             int tid) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = 4 * i + wave;
-      const int slot = __builtin_amdgcn_readlane(slot_lane, j);   // wave-uniform
-      const unsigned char* row = kv + (int64_t)slot * (2 * kDLat);
-      dma16_sbase(row, (i & 1) ? off_odd : off_even, lds0 + Layout<false>::main(buf) + j * kMainRow);
-    }
-    const int j = 8 * wave + (lane >> 3);
-    const int slot = __shfl(slot_lane, j, 64);
-    const unsigned char* src = kv + (int64_t)slot * (2 * kDLat) + kMainRow + (((lane & 7) ^ swz(j)) << 4);
-    dma16_vaddr(src, lds0 + Layout<false>::rope(buf) + wave * 1024);
-  } else {
-    const uint32_t stage = lds0 + Layout<true>::stage(buf);
-    const uint32_t off = (uint32_t)((lane & 31) << 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = 4 * i + wave;                 // rows 2k (lanes 0-31) and 2k + 1
-      const int slot = __shfl(slot_lane, 2 * k + (lane >> 5), 64);
-      dma16_vaddr(kv + (int64_t)slot * kDLat + off, stage + k * 1024);
-    }
-    if (wave < 2) {
-      const int j = 16 * wave + (lane >> 2);
-      const int slot = __shfl(slot_lane, j, 64);
-      const unsigned char* src = kv + (int64_t)slot * kDLat + kF8MainRow + ((lane & 3) << 4);
-      dma16_vaddr(src, stage + kF8MainBytes + wave * 1024);
-    }
-  }
-}
-
-// fp8 staging tile -> the swizzled bf16 tile: a 16-byte fp8 chunk becomes two
-// bf16 chunks.
-__device__ __forceinline__ void convert_tile(lds_u8* smem, int buf, int tid) {
-  const int stage = Layout<true>::stage(buf);
-#pragma unroll 1
-  for (int i = 0; i < 4; ++i) {
-    const int p = i * 256 + tid;
+  for (int i = 0; i < 1024 / kDecodeThreads; ++i) {
+    const int p = i * kDecodeThreads + tid;
     const int row = p >> 5, c = p & 31;
     const u32x4 w = lds_load<u32x4>(smem, stage + row * kF8MainRow + c * 16);
-    const int base = Layout<true>::main(0) + row * kMainRow;
-    lds_store(smem, base + (((2 * c) ^ swz(row)) << 4), cat(fp8x4_to_bf16(w[0]), fp8x4_to_bf16(w[1])));
-    lds_store(smem, base + (((2 * c + 1) ^ swz(row)) << 4), cat(fp8x4_to_bf16(w[2]), fp8x4_to_bf16(w[3])));
+    const int base = main_off + row * kMainRow;
+    lds_store(smem, base + (((2 * c) ^ swz_main(row)) << 4),
+              cat(fp8x4_to_bf16(w[0]), fp8x4_to_bf16(w[1])));
+    lds_store(smem, base + (((2 * c + 1) ^ swz_main(row)) << 4),
+              cat(fp8x4_to_bf16(w[2]), fp8x4_to_bf16(w[3])));
   }
   if (tid < 128) {
     const int row = tid >> 2, c = tid & 3;
     const u32x4 w = lds_load<u32x4>(smem, stage + kF8MainBytes + row * kF8RopeRow + c * 16);
-    const int base = Layout<true>::rope(0) + row * kRopeRow;
-    lds_store(smem, base + (((2 * c) ^ swz(row)) << 4), cat(fp8x4_to_bf16(w[0]), fp8x4_to_bf16(w[1])));
-    lds_store(smem, base + (((2 * c + 1) ^ swz(row)) << 4), cat(fp8x4_to_bf16(w[2]), fp8x4_to_bf16(w[3])));
+    const int base = rope_off + row * kRopeRow;
+    lds_store(smem, base + (((2 * c) ^ swz_rope(row)) << 4),
+              cat(fp8x4_to_bf16(w[0]), fp8x4_to_bf16(w[1])));
+    lds_store(smem, base + (((2 * c + 1) ^ swz_rope(row)) << 4),
+              cat(fp8x4_to_bf16(w[2]), fp8x4_to_bf16(w[3])));
   }
 }
 
-// Per-lane LDS byte offsets (relative to a tile's main / rope array) of the
-// K fragments (A operand of S^T = K Q^T) and the transposed V fragments (A
-// operand of O^T = V^T P^T). The remaining parts of each address are
-// compile-time immediates.
-struct LaneOffsets {
-  int k_main[2];   // k-step parity 0 / 1
-  int k_rope[2];
-  int v[4];        // column tile c & 3
-};
+// ---------------------------------------------------------------------------
+// QK team: one tile.
 
-__device__ __forceinline__ LaneOffsets lane_offsets(int li, int lg) {
-  LaneOffsets o;
-  const int sk = swz(li);   // K rows 16 kt + li share the swizzle of li
+// K rows 16 kt + li: main chunk 4 ks + lg sits at (4 ks + lg) ^ li, i.e. at
+// 16 (ks >> 2) + ((4 (ks & 3) + lg) ^ li); rope chunk 4 (ks - 16) + lg at
+// (4 (ks - 16) + lg) ^ ((li >> 1) & 7).
+struct KOffsets {
+  int main[4];
+  int rope[2];
+};
+__device__ __forceinline__ KOffsets k_offsets(int li, int lg) {
+  KOffsets o;
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    o.k_main[par] = li * kMainRow + (((4 * par + lg) ^ sk) << 4);
-    o.k_rope[par] = li * kRopeRow + (((4 * par + lg) ^ sk) << 4);
-  }
-  // transposed V read: source lane li of group lg points at key 4 lg + li/4,
-  // columns 16 c + 4 (li % 4) .. +3
-  const int vrow = 4 * lg + (li >> 2);
-  const int sv = swz(vrow);
-  const int half = (li & 3) >> 1, inner = (li & 1) << 3;
+  for (int s = 0; s < 4; ++s) o.main[s] = li * kMainRow + (((4 * s + lg) ^ li) << 4);
 #pragma unroll
-  for (int cr = 0; cr < 4; ++cr) o.v[cr] = vrow * kMainRow + (((2 * cr + half) ^ sv) << 4) + inner;
+  for (int s = 0; s < 2; ++s) o.rope[s] = li * kRopeRow + (((4 * s + lg) ^ swz_rope(li)) << 4);
   return o;
 }
 
-// One KV tile: QK, mask, online softmax, PV. MAIN / ROPE are the tile's LDS
-// offsets (compile-time, so they fold into the instructions' offsets).
 template <int MAIN, int ROPE>
-__device__ __forceinline__ void compute_tile(const lds_u8* smem, const LaneOffsets& lo,
-                                             const bf16x8 (&qf)[kKSteps], f32x4 (&oacc)[kColTiles],
-                                             float& m_ref, float& l_part, int key_base, int end,
-                                             int pos_limit, float score_c) {
-  f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+__device__ __forceinline__ void qk_tile(lds_u8* smem, int q, int lane_in, int par,
+                                        const bf16x8 (&qf)[kKSteps], float& m_ref, float& l_part,
+                                        int key_base, int end, int pos_limit, float score_c) {
+  const int lane = opaque(lane_in);
+  const KOffsets ko = k_offsets(lane & 15, lane >> 4);
+
+  // S^T: 2 key blocks x 4 independent accumulation chains (k-steps ks, ks+4,
+  // ...), summed at the end. The K fragments of k-step pair g+2 are read while
+  // pair g is multiplied (sched_barrier keeps this order; the wait-count pass
+  // then waits only for the fragments actually consumed).
+  f32x4 sacc[2][4];
 #pragma unroll
-  for (int ks = 0; ks < kKSteps; ++ks) {
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      bf16x8 kf;
-      if (ks < 16)
-        kf = lds_load<bf16x8>(smem, lo.k_main[ks & 1] + MAIN + kt * 16 * kMainRow + (ks >> 1) * 128);
-      else
-        kf = lds_load<bf16x8>(smem, lo.k_rope[ks & 1] + ROPE + kt * 16 * kRopeRow);
-      sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
+    for (int c = 0; c < 4; ++c) sacc[kt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto kfrag = [&](int ks, int kt) -> bf16x8 {
+    if (ks < 16)
+      return lds_load<bf16x8>(smem, ko.main[ks & 3] + MAIN + kt * 16 * kMainRow + (ks >> 2) * 256);
+    return lds_load<bf16x8>(smem, ko.rope[ks & 1] + ROPE + kt * 16 * kRopeRow);
+  };
+  constexpr int kGroups = kKSteps / 2;   // 9 pairs of k-steps, 4 fragments each
+  bf16x8 kbuf[3][4];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) kbuf[g][f] = kfrag(2 * g + (f >> 1), f & 1);
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    if (g + 2 < kGroups) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) kbuf[(g + 2) % 3][f] = kfrag(2 * (g + 2) + (f >> 1), f & 1);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int ks = 2 * g + (f >> 1), kt = f & 1;
+      sacc[kt][ks & 3] =
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[g % 3][f], qf[ks], sacc[kt][ks & 3], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // key_base = split-relative index of this lane's first score's key
+  // Mask and online softmax (key_base: split-relative key of this lane's first
+  // score).
   float sv[8];
   float tmax = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
+    const f32x4 s = (sacc[kt][0] + sacc[kt][1]) + (sacc[kt][2] + sacc[kt][3]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int key = key_base + kt * 16 + r;
       const bool vis = key < end && key <= pos_limit;
-      const float v = vis ? sacc[kt][r] * score_c : -INFINITY;
+      const float v = vis ? s[r] * score_c : -INFINITY;
       sv[kt * 4 + r] = v;
       tmax = fmaxf(tmax, v);
     }
@@ -278,13 +356,9 @@ __device__ __forceinline__ void compute_tile(const lds_u8* smem, const LaneOffse
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
   const bool need = tmax > m_ref + kRescaleSlack;
-  if (__ballot(need)) {   // wave-uniform
-    const float alpha = need ? exp2f(m_ref - tmax) : 1.0f;
-    m_ref = need ? tmax : m_ref;
-    l_part *= alpha;
-#pragma unroll
-    for (int c = 0; c < kColTiles; ++c) oacc[c] *= alpha;
-  }
+  const float alpha = need ? exp2f(m_ref - tmax) : 1.0f;
+  m_ref = need ? tmax : m_ref;
+  l_part *= alpha;
   const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
   bf16x8 pf;
 #pragma unroll
@@ -293,35 +367,109 @@ __device__ __forceinline__ void compute_tile(const lds_u8* smem, const LaneOffse
     l_part += p;
     pf[e] = (__bf16)p;
   }
+  // Publish P^T and the rescale factors of this wave's rows (buffer `par`).
+  lds_store(smem, kOffP + ((par * kRowBlocks + q) * 64 + lane) * 16, pf);
+  if (lane < 16) lds_store(smem, kOffAlpha + (par * 64 + q * 16 + lane) * 4, alpha);
+  const bool any_need = __ballot(need) != 0;
+  if (lane == 0) lds_store(smem, kOffFlags + (par * 4 + q) * 4, (uint32_t)any_need);
+}
 
+// ---------------------------------------------------------------------------
+// PV team: one tile (its P^T and rescale factors in buffer `par`).
+template <int MAIN>
+__device__ __forceinline__ void pv_tile(const lds_u8* smem, int p, int lane_in, int par,
+                                        f32x4 (&oacc)[kRowBlocks][kWaveColTiles]) {
+  const int lane = opaque(lane_in);
+  const int li = lane & 15, lg = lane >> 4;
+  const u32x4 flags = lds_load<u32x4>(smem, kOffFlags + par * 16);
+  if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) {   // uniform
 #pragma unroll
-  for (int c = 0; c < kColTiles; ++c) {
-    const int imm = MAIN + (c >> 2) * 128;
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+      const float a = lds_load<float>(smem, kOffAlpha + (par * 64 + rb * 16 + li) * 4);
+#pragma unroll
+      for (int c = 0; c < kWaveColTiles; ++c) oacc[rb][c] *= a;
+    }
+  }
+  bf16x8 pall[kRowBlocks];
+#pragma unroll
+  for (int rb = 0; rb < kRowBlocks; ++rb)
+    pall[rb] = lds_load<bf16x8>(smem, kOffP + ((par * kRowBlocks + rb) * 64 + lane) * 16);
+  // Transposed V read: source lane li of group lg points at key 4 lg + li / 4,
+  // columns 16 ct + 4 (li % 4) .. +3 -- chunk 2 ct + h with h = (li & 3) / 2,
+  // byte (li & 1) * 8 inside it; the chunk sits at (2 ct + h) ^ (row & 15) =
+  // 2 ct ^ (h ^ (row & 15)) since h is bit 0 of the chunk index. Global column
+  // tile ct = 8 p + c.
+  const int vrow = 4 * lg + (li >> 2);
+  const int v_row = vrow * kMainRow + ((li & 1) << 3) + p * 256;
+  const int v_xor = (((li & 3) >> 1) ^ swz_main(vrow)) << 4;
+  auto vfrag = [&](int c) -> bf16x8 {
+    const int voff = v_row + (((2 * c) << 4) ^ v_xor);
     const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(smem + lo.v[c & 3] + imm));
+        (__attribute__((address_space(3))) i16x4*)(smem + MAIN + voff));
     const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(smem + lo.v[c & 3] + imm + 16 * kMainRow));
-    const bf16x8 vf = cat(__builtin_bit_cast(bf16x4, v0), __builtin_bit_cast(bf16x4, v1));
-    oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[c], 0, 0, 0);
+        (__attribute__((address_space(3))) i16x4*)(smem + MAIN + voff + 16 * kMainRow));
+    return cat(__builtin_bit_cast(bf16x4, v0), __builtin_bit_cast(bf16x4, v1));
+  };
+  bf16x8 vbuf[3];
+  vbuf[0] = vfrag(0);
+  vbuf[1] = vfrag(1);
+#pragma unroll
+  for (int c = 0; c < kWaveColTiles; ++c) {
+    if (c + 2 < kWaveColTiles) vbuf[(c + 2) % 3] = vfrag(c + 2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb)
+      oacc[rb][c] =
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(vbuf[c % 3], pall[rb], oacc[rb][c], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // ---------------------------------------------------------------------------
+// Loop step shared by both teams: wait for tile t (if it exists), barrier,
+// (fp8: convert it, barrier), then start the loads of tile t + kAhead and the
+// slot list of tile t + 2 kAhead. After tile t's loads this wave issued one
+// slot load plus, if tile t+1 exists, that tile's loads.
+template <bool KV_FP8>
+__device__ __forceinline__ void loop_step(lds_u8* smem, const unsigned char* kv,
+                                          const int32_t* kv_indices, int kv0, int begin, int end,
+                                          int t, int ntiles, int wave, int lane, int tid) {
+  constexpr int n = TileLoads<KV_FP8>::n;
+  if (t + 1 < ntiles) wait_vm<1 + n>();
+  else if (t < ntiles) wait_vm<1>();
+  __syncthreads();   // tile t landed; tile t-2 and P^T of tile t-2 are free
+  if constexpr (KV_FP8) {
+    if (t < ntiles) {
+      convert_tile(smem, Layout<true>::stage(t), Layout<true>::main(t), Layout<true>::rope(t), tid);
+      __syncthreads();
+    }
+  }
+  issue_slots(kv_indices, kv0, begin, end, t + 2 * kAhead, smem, wave, lane);
+  if (t + kAhead < ntiles) {
+    const int ta = t + kAhead;
+    const int slot = read_slots(smem, ta, wave, lane);
+    if constexpr (KV_FP8)
+      issue_tile<true>(kv, slot, smem, Layout<true>::stage(ta), 0, wave, lane);
+    else
+      issue_tile<false>(kv, slot, smem, Layout<false>::main(ta), Layout<false>::rope(ta), wave, lane);
+  }
+}
+
 template <bool Q_FP8, bool KV_FP8>
-__global__ __launch_bounds__(kBlockThreads, 2) void decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kLdsBytes];
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmemBytes];
   lds_u8* smem = (lds_u8*)smem_raw;
   using LY = Layout<KV_FP8>;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool qk_team = wave < kTeam;
   const int li = lane & 15, lg = lane >> 4;
   const int H = a.heads;
   const unsigned char* kv = (const unsigned char*)a.kv;
   const float q_scale = a.q_scale ? *a.q_scale : 1.0f;
   const float kv_scale = a.kv_scale ? *a.kv_scale : 1.0f;
   const float score_c = a.score_scale_log2 * q_scale * kv_scale;
-  const LaneOffsets lo = lane_offsets(li, lg);
 
   const int g = blockIdx.x;
   const int it0 = a.plan[a.off_work_indptr + g], it1 = a.plan[a.off_work_indptr + g + 1];
@@ -336,95 +484,143 @@ __global__ __launch_bounds__(kBlockThreads, 2) void decode_kernel(DecodeArgs a) 
     const int kv0 = a.kv_indptr[b], L = a.kv_indptr[b + 1] - kv0;
     const int M = q_b * H;
     if (m * 64 >= M) continue;   // no query row in this tile (ragged block); uniform
-
-    const int mr = m * 64 + wave * 16 + li;
-    const bool row_ok = mr < M;
-    const int tok = row_ok ? mr / H : 0;
-    const int head = row_ok ? mr - tok * H : 0;
-    const int pos_limit = a.causal ? (L - q_b + tok) : (L - 1);
-
-    // Queries: lane holds Q[row li][32 ks + 8 lg .. +7] for ks = 0..17 (the
-    // B operand of S^T = K Q^T).
-    bf16x8 qf[kKSteps];
-    if (row_ok) {
-      const int64_t qrow = ((int64_t)(q0 + tok) * H + head) * kDLat;
-      if constexpr (!Q_FP8) {
-        const bf16x8* src = (const bf16x8*)((const uint16_t*)a.q + qrow + lg * 8);
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = src[ks * 4];
-      } else {
-        const u32x2* src = (const u32x2*)((const unsigned char*)a.q + qrow + lg * 8);
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
-          const u32x2 w = src[ks * 4];
-          qf[ks] = cat(fp8x4_to_bf16(w[0]), fp8x4_to_bf16(w[1]));
-        }
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = bf16x8{};
-    }
-
-    f32x4 oacc[kColTiles];
-#pragma unroll
-    for (int c = 0; c < kColTiles; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_ref = -INFINITY;   // reference max (base 2) of this lane's row
-    float l_part = 0.f;        // this lane's share of the row's softmax sum
-
     const int ntiles = (end - begin + kNT - 1) / kNT;
-    if (ntiles > 0) {
-      int slot_next = load_tile_slot(a.kv_indices, kv0, begin, end, lane);
-      issue_tile<KV_FP8>(kv, slot_next, smem, 0, wave, lane);
-      if (ntiles > 1) slot_next = load_tile_slot(a.kv_indices, kv0, begin + kNT, end, lane);
 
-      // One tile in buffer BUF: wait for it, start the next one into the
-      // other buffer, compute.
-      auto step = [&](int t, auto BUF) {
-        constexpr int buf = decltype(BUF)::value;
-        wait_vm_all();
-        __syncthreads();   // tile t landed for every wave; tile t-1 fully consumed
-        if (t + 1 < ntiles) {
-          issue_tile<KV_FP8>(kv, slot_next, smem, buf ^ 1, wave, lane);
-          if (t + 2 < ntiles)
-            slot_next = load_tile_slot(a.kv_indices, kv0, begin + (t + 2) * kNT, end, lane);
+    // Prologue (all waves): slot lists of tiles 0..3, then the loads of tiles
+    // 0 and 1, each preceded by one slot load so that every later wait count
+    // has the same form.
+    auto prologue = [&](auto&& after_wait) {
+#pragma unroll
+      for (int t = 0; t < 2 * kAhead; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, wave, lane);
+      wait_vm<0>();
+      after_wait();
+#pragma unroll
+      for (int t = 0; t < kAhead; ++t) {
+        issue_slots(a.kv_indices, kv0, begin, end, t + kAhead, smem, wave, lane);
+        if (t < ntiles) {
+          const int slot = read_slots(smem, t, wave, lane);
+          if constexpr (KV_FP8)
+            issue_tile<true>(kv, slot, smem, LY::stage(t), 0, wave, lane);
+          else
+            issue_tile<false>(kv, slot, smem, LY::main(t), LY::rope(t), wave, lane);
         }
-        if constexpr (KV_FP8) {
-          convert_tile(smem, buf, tid);
-          __syncthreads();
-        }
-        compute_tile<LY::main(buf), LY::rope(buf)>(smem, lo, qf, oacc, m_ref, l_part,
-                                                   begin + t * kNT + lg * 4, end, pos_limit,
-                                                   score_c);
-      };
-      for (int t = 0; t < ntiles; t += 2) {
-        step(t, std::integral_constant<int, 0>{});
-        if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
       }
-    }
+    };
 
-    // Epilogue.
-    float l_row = l_part + __shfl_xor(l_part, 16, 64);
-    l_row += __shfl_xor(l_row, 32, 64);
-    if (row_ok) {
-      const bool empty = !(l_row > 0.f);
-      const float inv = empty ? 0.f : kv_scale / l_row;
-      const float lse = empty ? -INFINITY : (m_ref + __log2f(l_row)) * kLn2;
-      if (part < 0) {
-        const int64_t orow = ((int64_t)(q0 + tok) * H + head);
-        uint16_t* dst = a.o + orow * kDV + lg * 4;
+    if (qk_team) {
+      // -------- QK team: rows 16 wave + li
+      const int q = wave;
+      const int mr = m * 64 + q * 16 + li;
+      const bool row_ok = mr < M;
+      const int tok = row_ok ? mr / H : 0;
+      const int head = row_ok ? mr - tok * H : 0;
+      const int pos_limit = a.causal ? (L - q_b + tok) : (L - 1);
+      // lane holds Q[row][32 ks + 8 lg .. +7] for ks = 0..17 (B operand of S^T = K Q^T)
+      bf16x8 qf[kKSteps];
+      if (row_ok) {
+        const int64_t qrow = ((int64_t)(q0 + tok) * H + head) * kDLat;
+        if constexpr (!Q_FP8) {
+          const bf16x8* src = (const bf16x8*)((const uint16_t*)a.q + qrow + lg * 8);
 #pragma unroll
-        for (int c = 0; c < kColTiles; ++c) {
-          const f32x4 v = oacc[c] * inv;
-          const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-          *(bf16x4*)(dst + c * 16) = bv;
+          for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = src[ks * 4];
+        } else {
+          const u32x2* src = (const u32x2*)((const unsigned char*)a.q + qrow + lg * 8);
+#pragma unroll
+          for (int ks = 0; ks < kKSteps; ++ks) {
+            const u32x2 w = src[ks * 4];
+            qf[ks] = cat(fp8x4_to_bf16(w[0]), fp8x4_to_bf16(w[1]));
+          }
         }
-        if (lg == 0) a.lse[orow] = lse;
       } else {
-        const int64_t prow = ((int64_t)part * a.q_len_max + tok) * H + head;
-        float* dst = a.ws_o + prow * kDV + lg * 4;
 #pragma unroll
-        for (int c = 0; c < kColTiles; ++c) *(f32x4*)(dst + c * 16) = oacc[c] * inv;
-        if (lg == 0) a.ws_lse[prow] = lse;
+        for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = bf16x8{};
+      }
+      float m_ref = -INFINITY, l_part = 0.f;
+
+      if (ntiles > 0) {
+        // After the prologue's first full wait the query loads are complete
+        // as well; tell the compiler there, or it would wait for every tile
+        // load in flight before the first MFMA.
+        prologue([&]() {
+#pragma unroll
+          for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
+        });
+        auto step = [&](int t, auto T4) {
+          constexpr int t4 = decltype(T4)::value;   // t % 4
+          loop_step<KV_FP8>(smem, kv, a.kv_indices, kv0, begin, end, t, ntiles, wave, lane, tid);
+          if (t < ntiles)
+            qk_tile<LY::main(t4), LY::rope(t4)>(smem, q, lane, t4 & 1, qf, m_ref, l_part,
+                                                begin + t * kNT + lg * 4, end, pos_limit, score_c);
+        };
+        for (int t = 0; t <= ntiles; t += 4) {   // ntiles + 1 steps; the last one only hands over
+          step(t, std::integral_constant<int, 0>{});
+          if (t + 1 <= ntiles) step(t + 1, std::integral_constant<int, 1>{});
+          if (t + 2 <= ntiles) step(t + 2, std::integral_constant<int, 2>{});
+          if (t + 3 <= ntiles) step(t + 3, std::integral_constant<int, 3>{});
+        }
+        wait_vm<0>();   // slot-list loads beyond the last tile
+      }
+
+      // Epilogue: publish the rows' sums, write their LSE.
+      float l_row = l_part + __shfl_xor(l_part, 16, 64);
+      l_row += __shfl_xor(l_row, 32, 64);
+      __syncthreads();
+      if (lane < 16) lds_store(smem, kOffL + (q * 16 + lane) * 4, l_row);
+      if (row_ok && lg == 0) {
+        const float lse = l_row > 0.f ? (m_ref + __log2f(l_row)) * kLn2 : -INFINITY;
+        if (part < 0) a.lse[(int64_t)(q0 + tok) * H + head] = lse;
+        else a.ws_lse[((int64_t)part * a.q_len_max + tok) * H + head] = lse;
+      }
+      __syncthreads();
+    } else {
+      // -------- PV team: columns 128 p .. 128 p + 127 of all 64 rows
+      const int p = wave - kTeam;
+      f32x4 oacc[kRowBlocks][kWaveColTiles];
+#pragma unroll
+      for (int rb = 0; rb < kRowBlocks; ++rb)
+#pragma unroll
+        for (int c = 0; c < kWaveColTiles; ++c) oacc[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      if (ntiles > 0) {
+        prologue([]() {});
+        auto step = [&](int t, auto T4) {
+          constexpr int t4 = decltype(T4)::value;   // t % 4; PV works on tile t - 1
+          loop_step<KV_FP8>(smem, kv, a.kv_indices, kv0, begin, end, t, ntiles, wave, lane, tid);
+          if (t >= 1) pv_tile<LY::main((t4 + 3) % 4)>(smem, p, lane, (t4 + 1) & 1, oacc);
+        };
+        for (int t = 0; t <= ntiles; t += 4) {
+          step(t, std::integral_constant<int, 0>{});
+          if (t + 1 <= ntiles) step(t + 1, std::integral_constant<int, 1>{});
+          if (t + 2 <= ntiles) step(t + 2, std::integral_constant<int, 2>{});
+          if (t + 3 <= ntiles) step(t + 3, std::integral_constant<int, 3>{});
+        }
+        wait_vm<0>();
+      }
+
+      // Epilogue: normalize with the rows' sums and write this wave's columns.
+      __syncthreads();
+      __syncthreads();
+#pragma unroll
+      for (int rb = 0; rb < kRowBlocks; ++rb) {
+        const int r = m * 64 + rb * 16 + li;
+        if (r >= M) continue;
+        const float l = lds_load<float>(smem, kOffL + (rb * 16 + li) * 4);
+        const float inv = l > 0.f ? kv_scale / l : 0.f;
+        const int rt = r / H, rh = r - rt * H;
+        const int col0 = p * kWaveCols + lg * 4;
+        if (part < 0) {
+          uint16_t* dst = a.o + ((int64_t)(q0 + rt) * H + rh) * kDV + col0;
+#pragma unroll
+          for (int c = 0; c < kWaveColTiles; ++c) {
+            const f32x4 v = oacc[rb][c] * inv;
+            const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+            *(bf16x4*)(dst + c * 16) = bv;
+          }
+        } else {
+          float* dst = a.ws_o + (((int64_t)part * a.q_len_max + rt) * H + rh) * kDV + col0;
+#pragma unroll
+          for (int c = 0; c < kWaveColTiles; ++c) *(f32x4*)(dst + c * 16) = oacc[rb][c] * inv;
+        }
       }
     }
     __syncthreads();   // LDS is reused by the next item
@@ -479,11 +675,11 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Gather test hook: one block per split; every tile goes through the decode
-// kernel's loader (and fp8 conversion) into buffer 0, then is copied out of
-// LDS with the swizzle undone.
+// kernel's loader (and fp8 conversion) into tile 0, then is copied out of LDS
+// with the swizzle undone.
 template <bool KV_FP8>
-__global__ __launch_bounds__(kBlockThreads) void gather_kernel(GatherArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kLdsBytes];
+__global__ __launch_bounds__(kDecodeThreads) void gather_kernel(GatherArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kTilesBytes];
   lds_u8* smem = (lds_u8*)smem_raw;
   using LY = Layout<KV_FP8>;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -496,18 +692,21 @@ __global__ __launch_bounds__(kBlockThreads) void gather_kernel(GatherArgs a) {
   const unsigned char* kv = (const unsigned char*)a.kv;
   for (int key0 = begin; key0 < end; key0 += kNT) {
     const int slot = load_tile_slot(a.kv_indices, kv0, key0, end, lane);
-    issue_tile<KV_FP8>(kv, slot, smem, 0, wave, lane);
+    if constexpr (KV_FP8)
+      issue_tile<true>(kv, slot, smem, Layout<true>::stage(0), 0, wave, lane);
+    else
+      issue_tile<false>(kv, slot, smem, LY::main(0), LY::rope(0), wave, lane);
     wait_vm_all();
     __syncthreads();
     if constexpr (KV_FP8) {
-      convert_tile(smem, 0, tid);
+      convert_tile(smem, Layout<true>::stage(0), LY::main(0), LY::rope(0), tid);
       __syncthreads();
     }
-    for (int p = tid; p < kNT * 72; p += kBlockThreads) {
+    for (int p = tid; p < kNT * 72; p += kDecodeThreads) {
       const int row = p / 72, chunk = p - row * 72;
       if (key0 + row < end) {
-        const int off = chunk < 64 ? LY::main(0) + row * kMainRow + ((chunk ^ swz(row)) << 4)
-                                   : LY::rope(0) + row * kRopeRow + (((chunk - 64) ^ swz(row)) << 4);
+        const int off = chunk < 64 ? LY::main(0) + row * kMainRow + ((chunk ^ swz_main(row)) << 4)
+                                   : LY::rope(0) + row * kRopeRow + (((chunk - 64) ^ swz_rope(row)) << 4);
         const u32x4 v = lds_load<u32x4>(smem, off);
         *(u32x4*)(a.dense + (dense0 + key0 + row) * kDLat + chunk * 8) = v;
       }
@@ -525,7 +724,7 @@ hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, int grid,
   else if (!q_fp8 && kv_fp8) fn = (const void*)decode_kernel<false, true>;
   else if (q_fp8 && !kv_fp8) fn = (const void*)decode_kernel<true, false>;
   else fn = (const void*)decode_kernel<true, true>;
-  return hipLaunchKernel(fn, dim3(grid), dim3(kBlockThreads), args, 0, st);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kDecodeThreads), args, 0, st);
 }
 
 hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, hipStream_t st) {
@@ -537,7 +736,7 @@ hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, 
 hipError_t launch_gather(const GatherArgs& a, bool kv_fp8, int splits, hipStream_t st) {
   void* args[] = {(void*)&a};
   const void* fn = kv_fp8 ? (const void*)gather_kernel<true> : (const void*)gather_kernel<false>;
-  return hipLaunchKernel(fn, dim3(splits), dim3(kBlockThreads), args, 0, st);
+  return hipLaunchKernel(fn, dim3(splits), dim3(kDecodeThreads), args, 0, st);
 }
 
 }  // namespace mla
