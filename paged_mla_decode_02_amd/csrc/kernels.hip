@@ -178,50 +178,91 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Reductions over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48):
+// v_permlane32_swap and v_permlane16_swap exchange halves and odd/even
+// 16-lane rows between two registers, so each step is one VALU swap.
+__device__ __forceinline__ float group_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Tile loader (shared by the decode kernel and the gather test hook).
 
-// Issue one tile's direct-to-LDS loads (8 waves); slot_lane: lane j < 32
-// holds the pool slot of the tile's key j. bf16: wave w loads main rows 8i + w
-// (one 1 KB row per instruction, its slot read from lane j) and rope rows
-// 4w..4w+3 (half a wave). fp8: main rows 2k, 2k + 1 for k = 8i + w (two
-// 512-byte rows per instruction) and rope rows 4w..4w+3 (a quarter wave), into
-// the linear staging tile. Every wave issues the same number of loads.
-template <bool KV_FP8> struct TileLoads { static constexpr int n = KV_FP8 ? 3 : 5; };
+// One tile's direct-to-LDS loads, spread over NW waves (the decode kernel's
+// PV team, NW = 4, or all eight waves of the gather hook); every wave issues
+// the same number n of load instructions, op(i) for i = 0..n-1. slot_lane:
+// lane j < 32 holds the pool slot of the tile's key j.
+//   bf16: op i < 32/NW loads main row j = NW i + w (one 1 KB row per
+//         instruction, its slot wave-uniform); the last op loads rope rows
+//         (32/NW) w .. +32/NW-1, 8 lanes per row.
+//   fp8:  op i < 16/NW loads main rows 2k, 2k + 1 for k = NW i + w (two 512-byte
+//         rows per instruction) into the linear staging tile; the last op
+//         loads rope rows (32/NW) w .. +32/NW-1, 4 lanes per row.
+template <bool KV_FP8, int NW> struct TileDma {
+  static constexpr int kMainOps = (KV_FP8 ? 16 : 32) / NW;
+  static constexpr int n = kMainOps + 1;
+  static constexpr int kRopeRows = kNT / NW;
 
-template <bool KV_FP8>
-__device__ __forceinline__ void issue_tile(const unsigned char* kv, int slot_lane, lds_u8* smem,
-                                           int main_off, int rope_off, int wave, int lane_in) {
-  const int lane = opaque(lane_in);
-  const uint32_t lds0 = lds_addr_of(smem);
-  if constexpr (!KV_FP8) {
-#pragma unroll
-    for (int i = 0; i < kNT / kWaves; ++i) {
-      const int j = kWaves * i + wave;
-      const int slot = __builtin_amdgcn_readlane(slot_lane, j);   // wave-uniform
-      const unsigned char* row = kv + (int64_t)slot * (2 * kDLat);
-      dma16_sbase(row, (uint32_t)((lane ^ (j & 15)) << 4), lds0 + main_off + j * kMainRow);
+  static __device__ __forceinline__ void op(int i, const unsigned char* kv, int slot_lane,
+                                            uint32_t lds0, int main_off, int rope_off, int w,
+                                            int lane) {
+    if constexpr (!KV_FP8) {
+      if (i < kMainOps) {
+        const int j = NW * i + w;
+        const int slot = __builtin_amdgcn_readlane(slot_lane, j);   // wave-uniform
+        const unsigned char* row = kv + (int64_t)slot * (2 * kDLat);
+        dma16_sbase(row, (uint32_t)((lane ^ (j & 15)) << 4), lds0 + main_off + j * kMainRow);
+      } else {
+        const int j = kRopeRows * w + (lane >> 3);
+        const int slot = __shfl(slot_lane, j & 31, 64);
+        const unsigned char* src =
+            kv + (int64_t)slot * (2 * kDLat) + kMainRow + (((lane & 7) ^ swz_rope(j)) << 4);
+        if (lane < 8 * kRopeRows) dma16_vaddr(src, lds0 + rope_off + w * kRopeRows * kRopeRow);
+      }
+    } else {
+      const uint32_t stage = lds0 + main_off;   // staging tile: main then rope
+      if (i < kMainOps) {
+        const int k = NW * i + w;                // rows 2k (lanes 0-31) and 2k + 1
+        const int slot = __shfl(slot_lane, 2 * k + (lane >> 5), 64);
+        dma16_vaddr(kv + (int64_t)slot * kDLat + ((lane & 31) << 4), stage + k * 1024);
+      } else {
+        const int j = kRopeRows * w + (lane >> 2);
+        const int slot = __shfl(slot_lane, j & 31, 64);
+        const unsigned char* src = kv + (int64_t)slot * kDLat + kF8MainRow + ((lane & 3) << 4);
+        if (lane < 4 * kRopeRows)
+          dma16_vaddr(src, stage + kF8MainBytes + w * kRopeRows * kF8RopeRow);
+      }
+      (void)rope_off;
     }
-    const int j = 4 * wave + (lane >> 3);
-    const int slot = __shfl(slot_lane, j & 31, 64);
-    const unsigned char* src =
-        kv + (int64_t)slot * (2 * kDLat) + kMainRow + (((lane & 7) ^ swz_rope(j)) << 4);
-    if (lane < 32) dma16_vaddr(src, lds0 + rope_off + wave * 512);
-  } else {
-    const uint32_t stage = lds0 + main_off;   // staging tile: main then rope
-    const uint32_t off = (uint32_t)((lane & 31) << 4);
-#pragma unroll
-    for (int i = 0; i < 16 / kWaves; ++i) {
-      const int k = kWaves * i + wave;            // rows 2k (lanes 0-31) and 2k + 1
-      const int slot = __shfl(slot_lane, 2 * k + (lane >> 5), 64);
-      dma16_vaddr(kv + (int64_t)slot * kDLat + off, stage + k * 1024);
-    }
-    const int j = 4 * wave + (lane >> 2);         // lanes 0-15: rope rows 4w..4w+3
-    const int slot = __shfl(slot_lane, j & 31, 64);
-    const unsigned char* src = kv + (int64_t)slot * kDLat + kF8MainRow + ((lane & 3) << 4);
-    if (lane < 16) dma16_vaddr(src, stage + kF8MainBytes + wave * 256);
-    (void)rope_off;
   }
+
+  // All n loads of a tile at once.
+  static __device__ __forceinline__ void all(const unsigned char* kv, int slot_lane, lds_u8* smem,
+                                             int main_off, int rope_off, int w, int lane_in) {
+    const int lane = opaque(lane_in);
+#pragma unroll
+    for (int i = 0; i < n; ++i) op(i, kv, slot_lane, lds_addr_of(smem), main_off, rope_off, w, lane);
+  }
+};
+
+// LDS offsets a tile's loads target: bf16 tiles are loaded in place, fp8 tiles
+// into their staging tile.
+template <bool KV_FP8> __device__ __forceinline__ int dma_main(int t) {
+  if constexpr (KV_FP8) return Layout<true>::stage(t);
+  else return Layout<false>::main(t);
+}
+template <bool KV_FP8> __device__ __forceinline__ int dma_rope(int t) {
+  if constexpr (KV_FP8) return 0;
+  else return Layout<false>::rope(t);
 }
 
 // DMA the slot list of tile `tile` (32 int32, keys clamped to the split) into
@@ -353,8 +394,7 @@ __device__ __forceinline__ void qk_tile(lds_u8* smem, int q, int lane_in, int pa
       tmax = fmaxf(tmax, v);
     }
   }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  tmax = group_max(tmax);
   const bool need = tmax > m_ref + kRescaleSlack;
   const float alpha = need ? exp2f(m_ref - tmax) : 1.0f;
   m_ref = need ? tmax : m_ref;
@@ -376,9 +416,12 @@ __device__ __forceinline__ void qk_tile(lds_u8* smem, int q, int lane_in, int pa
 
 // ---------------------------------------------------------------------------
 // PV team: one tile (its P^T and rescale factors in buffer `par`).
-template <int MAIN>
+// issue(c) is called at the top of column tile c's step (c = 0..7): the PV
+// waves spread the next tiles' loads over their MFMAs instead of queueing them
+// all at once.
+template <int MAIN, typename Issue>
 __device__ __forceinline__ void pv_tile(const lds_u8* smem, int p, int lane_in, int par,
-                                        f32x4 (&oacc)[kRowBlocks][kWaveColTiles]) {
+                                        f32x4 (&oacc)[kRowBlocks][kWaveColTiles], Issue&& issue) {
   const int lane = opaque(lane_in);
   const int li = lane & 15, lg = lane >> 4;
   const u32x4 flags = lds_load<u32x4>(smem, kOffFlags + par * 16);
@@ -415,6 +458,7 @@ __device__ __forceinline__ void pv_tile(const lds_u8* smem, int p, int lane_in, 
   vbuf[1] = vfrag(1);
 #pragma unroll
   for (int c = 0; c < kWaveColTiles; ++c) {
+    issue(c);
     if (c + 2 < kWaveColTiles) vbuf[(c + 2) % 3] = vfrag(c + 2);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -426,32 +470,23 @@ __device__ __forceinline__ void pv_tile(const lds_u8* smem, int p, int lane_in, 
 }
 
 // ---------------------------------------------------------------------------
-// Loop step shared by both teams: wait for tile t (if it exists), barrier,
-// (fp8: convert it, barrier), then start the loads of tile t + kAhead and the
-// slot list of tile t + 2 kAhead. After tile t's loads this wave issued one
-// slot load plus, if tile t+1 exists, that tile's loads.
-template <bool KV_FP8>
-__device__ __forceinline__ void loop_step(lds_u8* smem, const unsigned char* kv,
-                                          const int32_t* kv_indices, int kv0, int begin, int end,
-                                          int t, int ntiles, int wave, int lane, int tid) {
-  constexpr int n = TileLoads<KV_FP8>::n;
-  if (t + 1 < ntiles) wait_vm<1 + n>();
-  else if (t < ntiles) wait_vm<1>();
+// Per-step synchronization. Only the PV team loads tiles: before the barrier
+// that publishes tile t each PV wave waits for its own loads of it -- after
+// them it has issued one slot-list load plus, if tile t+1 exists, that tile's
+// n loads. fp8: all eight waves then convert tile t and meet again.
+template <bool KV_FP8, bool PV>
+__device__ __forceinline__ void step_sync(lds_u8* smem, int t, int ntiles, int tid) {
+  constexpr int n = TileDma<KV_FP8, kTeam>::n;
+  if constexpr (PV) {
+    if (t + 1 < ntiles) wait_vm<1 + n>();
+    else if (t < ntiles) wait_vm<1>();
+  }
   __syncthreads();   // tile t landed; tile t-2 and P^T of tile t-2 are free
   if constexpr (KV_FP8) {
     if (t < ntiles) {
       convert_tile(smem, Layout<true>::stage(t), Layout<true>::main(t), Layout<true>::rope(t), tid);
       __syncthreads();
     }
-  }
-  issue_slots(kv_indices, kv0, begin, end, t + 2 * kAhead, smem, wave, lane);
-  if (t + kAhead < ntiles) {
-    const int ta = t + kAhead;
-    const int slot = read_slots(smem, ta, wave, lane);
-    if constexpr (KV_FP8)
-      issue_tile<true>(kv, slot, smem, Layout<true>::stage(ta), 0, wave, lane);
-    else
-      issue_tile<false>(kv, slot, smem, Layout<false>::main(ta), Layout<false>::rope(ta), wave, lane);
   }
 }
 
@@ -486,27 +521,6 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     if (m * 64 >= M) continue;   // no query row in this tile (ragged block); uniform
     const int ntiles = (end - begin + kNT - 1) / kNT;
 
-    // Prologue (all waves): slot lists of tiles 0..3, then the loads of tiles
-    // 0 and 1, each preceded by one slot load so that every later wait count
-    // has the same form.
-    auto prologue = [&](auto&& after_wait) {
-#pragma unroll
-      for (int t = 0; t < 2 * kAhead; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, wave, lane);
-      wait_vm<0>();
-      after_wait();
-#pragma unroll
-      for (int t = 0; t < kAhead; ++t) {
-        issue_slots(a.kv_indices, kv0, begin, end, t + kAhead, smem, wave, lane);
-        if (t < ntiles) {
-          const int slot = read_slots(smem, t, wave, lane);
-          if constexpr (KV_FP8)
-            issue_tile<true>(kv, slot, smem, LY::stage(t), 0, wave, lane);
-          else
-            issue_tile<false>(kv, slot, smem, LY::main(t), LY::rope(t), wave, lane);
-        }
-      }
-    };
-
     if (qk_team) {
       // -------- QK team: rows 16 wave + li
       const int q = wave;
@@ -538,16 +552,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       float m_ref = -INFINITY, l_part = 0.f;
 
       if (ntiles > 0) {
-        // After the prologue's first full wait the query loads are complete
-        // as well; tell the compiler there, or it would wait for every tile
-        // load in flight before the first MFMA.
-        prologue([&]() {
-#pragma unroll
-          for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
-        });
         auto step = [&](int t, auto T4) {
           constexpr int t4 = decltype(T4)::value;   // t % 4
-          loop_step<KV_FP8>(smem, kv, a.kv_indices, kv0, begin, end, t, ntiles, wave, lane, tid);
+          step_sync<KV_FP8, false>(smem, t, ntiles, tid);
           if (t < ntiles)
             qk_tile<LY::main(t4), LY::rope(t4)>(smem, q, lane, t4 & 1, qf, m_ref, l_part,
                                                 begin + t * kNT + lg * 4, end, pos_limit, score_c);
@@ -558,12 +565,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
           if (t + 2 <= ntiles) step(t + 2, std::integral_constant<int, 2>{});
           if (t + 3 <= ntiles) step(t + 3, std::integral_constant<int, 3>{});
         }
-        wait_vm<0>();   // slot-list loads beyond the last tile
       }
 
       // Epilogue: publish the rows' sums, write their LSE.
-      float l_row = l_part + __shfl_xor(l_part, 16, 64);
-      l_row += __shfl_xor(l_row, 32, 64);
+      const float l_row = group_sum(l_part);
       __syncthreads();
       if (lane < 16) lds_store(smem, kOffL + (q * 16 + lane) * 4, l_row);
       if (row_ok && lg == 0) {
@@ -582,17 +587,55 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         for (int c = 0; c < kWaveColTiles; ++c) oacc[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
       if (ntiles > 0) {
-        prologue([]() {});
+        using Dma = TileDma<KV_FP8, kTeam>;
+        // Prologue: slot lists of tiles 0..3, then the loads of tiles 0 and 1,
+        // each preceded by one slot-list load so that every later wait count
+        // has the same form.
+#pragma unroll
+        for (int t = 0; t < 2 * kAhead; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, p, lane);
+        wait_vm<0>();
+#pragma unroll
+        for (int t = 0; t < kAhead; ++t) {
+          issue_slots(a.kv_indices, kv0, begin, end, t + kAhead, smem, p, lane);
+          if (t < ntiles)
+            Dma::all(kv, read_slots(smem, t, p, lane), smem, dma_main<KV_FP8>(t), dma_rope<KV_FP8>(t), p, lane);
+        }
+        // Loads of tile t + 2 (into the buffers tile t - 2 used) and the slot
+        // list of tile t + 4; at step t >= 1 they are spread over the MFMAs of
+        // tile t - 1.
+        auto loads = [&](int t, auto T4, int dlane) {
+          constexpr int t4 = decltype(T4)::value;   // t % 4
+          issue_slots(a.kv_indices, kv0, begin, end, t + 2 * kAhead, smem, p, dlane);
+          const bool have = t + kAhead < ntiles;
+          const int slot = have ? read_slots(smem, t + kAhead, p, dlane) : 0;
+          return [=](int c) {
+            if (have) {
+#pragma unroll
+              for (int i = 0; i < Dma::n; ++i)
+                if (i * kWaveColTiles / Dma::n == c)
+                  Dma::op(i, kv, slot, lds_addr_of(smem), dma_main<KV_FP8>((t4 + kAhead) % 4),
+                          dma_rope<KV_FP8>((t4 + kAhead) % 4), p, dlane);
+            }
+          };
+        };
+        {  // step 0: no PV work yet
+          step_sync<KV_FP8, true>(smem, 0, ntiles, tid);
+          const int dlane = opaque(lane);
+          auto issue = loads(0, std::integral_constant<int, 0>{}, dlane);
+#pragma unroll
+          for (int c = 0; c < kWaveColTiles; ++c) issue(c);
+        }
         auto step = [&](int t, auto T4) {
           constexpr int t4 = decltype(T4)::value;   // t % 4; PV works on tile t - 1
-          loop_step<KV_FP8>(smem, kv, a.kv_indices, kv0, begin, end, t, ntiles, wave, lane, tid);
-          if (t >= 1) pv_tile<LY::main((t4 + 3) % 4)>(smem, p, lane, (t4 + 1) & 1, oacc);
+          step_sync<KV_FP8, true>(smem, t, ntiles, tid);
+          const int dlane = opaque(lane);
+          pv_tile<LY::main((t4 + 3) % 4)>(smem, p, dlane, (t4 + 1) & 1, oacc, loads(t, T4, dlane));
         };
-        for (int t = 0; t <= ntiles; t += 4) {
-          step(t, std::integral_constant<int, 0>{});
-          if (t + 1 <= ntiles) step(t + 1, std::integral_constant<int, 1>{});
-          if (t + 2 <= ntiles) step(t + 2, std::integral_constant<int, 2>{});
-          if (t + 3 <= ntiles) step(t + 3, std::integral_constant<int, 3>{});
+        for (int t = 1; t <= ntiles; t += 4) {
+          step(t, std::integral_constant<int, 1>{});
+          if (t + 1 <= ntiles) step(t + 1, std::integral_constant<int, 2>{});
+          if (t + 2 <= ntiles) step(t + 2, std::integral_constant<int, 3>{});
+          if (t + 3 <= ntiles) step(t + 3, std::integral_constant<int, 0>{});
         }
         wait_vm<0>();
       }
@@ -692,10 +735,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gather_kernel(GatherArgs a) {
   const unsigned char* kv = (const unsigned char*)a.kv;
   for (int key0 = begin; key0 < end; key0 += kNT) {
     const int slot = load_tile_slot(a.kv_indices, kv0, key0, end, lane);
-    if constexpr (KV_FP8)
-      issue_tile<true>(kv, slot, smem, Layout<true>::stage(0), 0, wave, lane);
-    else
-      issue_tile<false>(kv, slot, smem, LY::main(0), LY::rope(0), wave, lane);
+    TileDma<KV_FP8, kWaves>::all(kv, slot, smem, dma_main<KV_FP8>(0), dma_rope<KV_FP8>(0), wave, lane);
     wait_vm_all();
     __syncthreads();
     if constexpr (KV_FP8) {
