@@ -338,19 +338,21 @@ __device__ __forceinline__ KOffsets k_offsets(int li, int lg) {
 template <int MAIN, int ROPE>
 __device__ __forceinline__ void qk_tile(lds_u8* smem, int q, int lane_in, int par,
                                         const bf16x8 (&qf)[kKSteps], float& m_ref, float& l_part,
-                                        int key_base, int end, int pos_limit, float score_c) {
+                                        int key_base, int end, int pos_limit, float score_c,
+                                        bool full) {
   const int lane = opaque(lane_in);
   const KOffsets ko = k_offsets(lane & 15, lane >> 4);
 
-  // S^T: 2 key blocks x 4 independent accumulation chains (k-steps ks, ks+4,
-  // ...), summed at the end. The K fragments of k-step pair g+2 are read while
-  // pair g is multiplied (sched_barrier keeps this order; the wait-count pass
-  // then waits only for the fragments actually consumed).
-  f32x4 sacc[2][4];
+  // S^T: 2 key blocks x 2 independent accumulation chains (even and odd
+  // k-steps), summed at the end. The K fragments of k-step pair g+2 are read
+  // while pair g is multiplied (sched_barrier keeps this order; the wait-count
+  // pass then waits only for the fragments actually consumed).
+  f32x4 sacc[2][2];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sacc[kt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 2; ++c) sacc[kt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   auto kfrag = [&](int ks, int kt) -> bf16x8 {
     if (ks < 16)
       return lds_load<bf16x8>(smem, ko.main[ks & 3] + MAIN + kt * 16 * kMainRow + (ks >> 2) * 256);
@@ -372,38 +374,44 @@ __device__ __forceinline__ void qk_tile(lds_u8* smem, int q, int lane_in, int pa
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const int ks = 2 * g + (f >> 1), kt = f & 1;
-      sacc[kt][ks & 3] =
-          __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[g % 3][f], qf[ks], sacc[kt][ks & 3], 0, 0, 0);
+      sacc[kt][ks & 1] =
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[g % 3][f], qf[ks], sacc[kt][ks & 1], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // Mask and online softmax (key_base: split-relative key of this lane's first
-  // score).
+
+  // Mask and online softmax (key_base: key of this lane's first score). A
+  // tile that every row of the wave sees whole (`full`, wave-uniform) skips
+  // the mask.
   float sv[8];
-  float tmax = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    const f32x4 s = (sacc[kt][0] + sacc[kt][1]) + (sacc[kt][2] + sacc[kt][3]);
+    const f32x4 s = sacc[kt][0] + sacc[kt][1];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = key_base + kt * 16 + r;
-      const bool vis = key < end && key <= pos_limit;
-      const float v = vis ? s[r] * score_c : -INFINITY;
-      sv[kt * 4 + r] = v;
-      tmax = fmaxf(tmax, v);
+    for (int r = 0; r < 4; ++r) sv[kt * 4 + r] = s[r] * score_c;
+  }
+  if (!full) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = key_base + (e >> 2) * 16 + (e & 3);
+      sv[e] = (key < end && key <= pos_limit) ? sv[e] : -INFINITY;
     }
   }
+  float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
   tmax = group_max(tmax);
   const bool need = tmax > m_ref + kRescaleSlack;
-  const float alpha = need ? exp2f(m_ref - tmax) : 1.0f;
+  // v_exp_f32 directly: arguments below -126 give 0 or a denormal, which only
+  // drops weights under 2^-126 of the row maximum.
+  const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - tmax) : 1.0f;
   m_ref = need ? tmax : m_ref;
   l_part *= alpha;
   const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
   bf16x8 pf;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p = exp2f(sv[e] - mu);
+    const float p = __builtin_amdgcn_exp2f(sv[e] - mu);
     l_part += p;
     pf[e] = (__bf16)p;
   }
@@ -528,7 +536,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       const bool row_ok = mr < M;
       const int tok = row_ok ? mr / H : 0;
       const int head = row_ok ? mr - tok * H : 0;
-      const int pos_limit = a.causal ? (L - q_b + tok) : (L - 1);
+      // Rows past the end of the block are computed but never written; they
+      // take the non-causal limit so that they never force the masked path.
+      const int pos_limit = (a.causal && row_ok) ? (L - q_b + tok) : (L - 1);
+      // Rows are ordered token-major, so lane 0 holds the wave's smallest
+      // position limit.
+      const int pos_min = __builtin_amdgcn_readfirstlane(pos_limit);
       // lane holds Q[row][32 ks + 8 lg .. +7] for ks = 0..17 (B operand of S^T = K Q^T)
       bf16x8 qf[kKSteps];
       if (row_ok) {
@@ -555,9 +568,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         auto step = [&](int t, auto T4) {
           constexpr int t4 = decltype(T4)::value;   // t % 4
           step_sync<KV_FP8, false>(smem, t, ntiles, tid);
-          if (t < ntiles)
+          if (t < ntiles) {
+            const int last = begin + t * kNT + kNT - 1;   // last key of the tile
             qk_tile<LY::main(t4), LY::rope(t4)>(smem, q, lane, t4 & 1, qf, m_ref, l_part,
-                                                begin + t * kNT + lg * 4, end, pos_limit, score_c);
+                                                begin + t * kNT + lg * 4, end, pos_limit, score_c,
+                                                last < end && last <= pos_min);
+          }
         };
         for (int t = 0; t <= ntiles; t += 4) {   // ntiles + 1 steps; the last one only hands over
           step(t, std::integral_constant<int, 0>{});
@@ -671,49 +687,98 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Split merge: one block per (request row, query token) x 4 heads; a thread
-// owns 8 output columns of one head.
+// Split merge: one block of four waves per (request row b, query token i,
+// head h) of a row with n > 1 splits (n <= 64). Lane k of every wave reads
+// LSE_k; the wave reduces max and sum with permlane swaps and DPP-free
+// shuffles; wave w then accumulates the weighted partial O_k of splits
+// k = w, w + 4, ... (a lane owns 8 columns, 8 splits' loads in flight) and the
+// four partial sums meet in LDS.
+__device__ __forceinline__ float wave_max(float v) {
+  v = group_max(v);   // over lanes l, l^16, l^32, l^48
+#pragma unroll
+  for (int d = 8; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum(v);
+#pragma unroll
+  for (int d = 8; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
 __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
-  const int b = blockIdx.x / a.q_len_max;
-  const int i = blockIdx.x - b * a.q_len_max;
+  __shared__ f32x4 part[kBlockThreads / 64 - 1][64][2];
+  const int h = blockIdx.x % a.heads;
+  const int bi = blockIdx.x / a.heads;
+  const int b = bi / a.q_len_max;
+  const int i = bi - b * a.q_len_max;
   const int s0 = a.plan[a.off_split_indptr + b];
   const int n = a.plan[a.off_split_indptr + b + 1] - s0;
   if (n <= 1) return;
   const int q0 = a.qo_indptr[b];
   if (i >= a.qo_indptr[b + 1] - q0) return;
-  const int h = blockIdx.y * kMergeHeadsPerBlock + (threadIdx.x >> 6);
-  if (h >= a.heads) return;
-  const int col = (threadIdx.x & 63) * 8;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int part0 = a.plan[a.off_split_part + s0];
   const int64_t stride = (int64_t)a.q_len_max * a.heads;   // partial slots are consecutive
   const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
-
-  float mx = -INFINITY;
-  for (int k = 0; k < n; ++k) mx = fmaxf(mx, a.ws_lse[base + k * stride]);
   const int64_t orow = (int64_t)(q0 + i) * a.heads + h;
-  uint16_t* dst = a.o + orow * kDV + col;
-  if (mx == -INFINITY) {
-    *(u32x4*)dst = u32x4{0u, 0u, 0u, 0u};
-    if ((threadIdx.x & 63) == 0) a.lse[orow] = -INFINITY;
+
+  const float lk = lane < n ? a.ws_lse[base + lane * stride] : -INFINITY;
+  const float mx = wave_max(lk);
+  if (mx == -INFINITY) {   // every split empty: uniform over the block
+    if (w == 0) {
+      *(u32x4*)(a.o + orow * kDV + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+      if (lane == 0) a.lse[orow] = -INFINITY;
+    }
     return;
   }
   const float kLog2e = 1.44269504088896340736f;
-  float tot = 0.f;
-  for (int k = 0; k < n; ++k) tot += exp2f((a.ws_lse[base + k * stride] - mx) * kLog2e);
-  const float lse = mx + __log2f(tot) * kLn2;
+  const float ek = lk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lk - mx) * kLog2e);
+  const float tot = wave_sum(ek);
+  const float wk = ek / tot;   // weight of split `lane`
+
+  const float* src = a.ws_o + base * kDV + lane * 8;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < n; ++k) {
-    const float lk = a.ws_lse[base + k * stride];
-    if (lk == -INFINITY) continue;
-    const float w = exp2f((lk - lse) * kLog2e);
-    const f32x4* src = (const f32x4*)(a.ws_o + (base + k * stride) * kDV + col);
-    acc0 += w * src[0];
-    acc1 += w * src[1];
+  constexpr int kWaves = kBlockThreads / 64;
+  for (int k0 = w; k0 < n; k0 += 8 * kWaves) {
+    f32x4 v[8][2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u * kWaves;
+      if (k < n) {
+        const f32x4* p = (const f32x4*)(src + k * stride * kDV);
+        v[u][0] = p[0];
+        v[u][1] = p[1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u * kWaves;
+      if (k < n) {
+        const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), k));
+        if (c != 0.f) {   // an empty split's partial is never read
+          acc0 += c * v[u][0];
+          acc1 += c * v[u][1];
+        }
+      }
+    }
   }
-  const bf16x8 out = {(__bf16)acc0[0], (__bf16)acc0[1], (__bf16)acc0[2], (__bf16)acc0[3],
-                      (__bf16)acc1[0], (__bf16)acc1[1], (__bf16)acc1[2], (__bf16)acc1[3]};
-  *(bf16x8*)dst = out;
-  if ((threadIdx.x & 63) == 0) a.lse[orow] = lse;
+  if (w > 0) {
+    part[w - 1][lane][0] = acc0;
+    part[w - 1][lane][1] = acc1;
+  }
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int j = 0; j < kWaves - 1; ++j) {
+      acc0 += part[j][lane][0];
+      acc1 += part[j][lane][1];
+    }
+    const bf16x8 out = {(__bf16)acc0[0], (__bf16)acc0[1], (__bf16)acc0[2], (__bf16)acc0[3],
+                        (__bf16)acc1[0], (__bf16)acc1[1], (__bf16)acc1[2], (__bf16)acc1[3]};
+    *(bf16x8*)(a.o + orow * kDV + lane * 8) = out;
+    if (lane == 0) a.lse[orow] = mx + __log2f(tot) * kLn2;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -769,7 +834,7 @@ hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, int grid,
 
 hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, hipStream_t st) {
   void* args[] = {(void*)&a};
-  dim3 grid(rows * q_len_max, (heads + kMergeHeadsPerBlock - 1) / kMergeHeadsPerBlock);
+  dim3 grid(rows * q_len_max * heads);
   return hipLaunchKernel((const void*)merge_kernel, grid, dim3(kBlockThreads), args, 0, st);
 }
 

@@ -64,6 +64,16 @@ int32_t view_plan(const int32_t* plan, PlanView* v) {
   v->off_item_split = off; off += v->W;
   v->off_item_m = off; off += v->W;
   if (off != v->total) return set_error(MLA_ERR_PLAN_MISMATCH, "plan length mismatch");
+  // The merge kernel takes one split per lane of a wave: at most N_MAX = 64
+  // splits per row, and split_indptr must run from 0 to S.
+  if (plan[H_NMAX] != kNMax || plan[v->off_split_indptr] != 0 ||
+      plan[v->off_split_indptr + v->rows] != v->S)
+    return set_error(MLA_ERR_PLAN_MISMATCH, "plan split_indptr is inconsistent");
+  for (int32_t b = 0; b < v->rows; ++b) {
+    const int32_t n = plan[v->off_split_indptr + b + 1] - plan[v->off_split_indptr + b];
+    if (n < 1 || n > kNMax)
+      return set_error(MLA_ERR_PLAN_MISMATCH, "plan has a row with no split or more than 64");
+  }
   return MLA_OK;
 }
 
