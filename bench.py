@@ -57,6 +57,44 @@ def measured_traffic(workload):
     return d.get("bytes_per_launch")
 
 
+def traffic_from_counters(workload, fetch_csv, write_csv, copy_mib):
+    """HBM bytes per mla_decode_fwd call from two rocprofv3 --pmc passes
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) of `bench.py --copy-mib N`.
+    Each counter is divided by what it reads for the known-size device copy
+    (the largest __amd_rocclr_copyBuffer dispatch: copy_mib MiB read and
+    written). Writes profiles/traffic_<workload>.json and returns it."""
+    import csv
+
+    def per_dispatch(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return vals
+
+    out = {"workload": workload, "kernel_sha": kernel_sha(), "copy_mib": copy_mib}
+    total = 0.0
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_dispatch(path, name)
+        copy_kib = max(v for (d, k), v in vals.items() if "copyBuffer" in k)
+        factor = copy_kib / (copy_mib * 1024.0)
+        decode = [v for (d, k), v in vals.items() if "decode_kernel" in k]
+        merge = [v for (d, k), v in vals.items() if "merge_kernel" in k]
+        launches = len(decode)
+        kib = (sum(decode) + sum(merge)) / launches
+        out[name] = {"raw_kib_per_launch": round(kib, 3), "copy_raw_kib": round(copy_kib, 3),
+                     "scale": round(factor, 5), "bytes_per_launch": round(kib * 1024.0 / factor),
+                     "launches": launches, "merge_dispatches": len(merge)}
+        total += kib * 1024.0 / factor
+    out["bytes_per_launch"] = round(total)
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def cpu_baseline(case, budget_s):
     """Time the float64 oracle on whole rows of the workload until about
     budget_s seconds of CPU work (at least one row)."""
@@ -97,7 +135,16 @@ def main():
     ap.add_argument("--workload", default="verify_causal")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work; 0 skips")
     ap.add_argument("--rotate", type=int, default=3, help="disjoint index lists cycled over steps")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before warm-up, one plain device copy of this many MiB: the known-size "
+                         "reference for scaling hardware byte counters")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="only turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--copy-mib run into profiles/traffic_<workload>.json")
     args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(traffic_from_counters(args.workload, *args.traffic_from, args.copy_mib or 256)))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -149,6 +196,14 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         return words
+
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for k in range(args.warmup):
         words = step(k)
