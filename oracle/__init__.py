@@ -19,6 +19,10 @@ What it computes, and where the pages say so:
   call from the real lengths), step by step.
 * ``merge``: the log-sum-exp merge of split partials (ATOM pull request 2462,
   "Dependencies": split and merge).
+* ``cache_write``: the latent cache write -- a token's 512 compressed dims and
+  64 RoPE dims into its slot, each source value taken at its own dtype and
+  rounded to the cache format (vLLM pull request 57942, "Details" and its
+  review thread).
 * ``brute``: pure-Python loops, for tiny cases only.
 
 Readings where the pages are silent are listed in the repository's design
