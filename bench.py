@@ -141,6 +141,10 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="only turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-mib run into profiles/traffic_<workload>.json")
+    ap.add_argument("--op", default="decode", choices=["decode", "cache_write"],
+                    help="decode: the hot path (default); cache_write: the latent cache writer")
+    ap.add_argument("--tokens", type=int, default=65536, help="cache_write: tokens per call")
+    ap.add_argument("--kv-dtype", default="fp8", choices=["fp8", "bf16"], help="cache_write: pool dtype")
     args = ap.parse_args()
     if args.traffic_from:
         print(json.dumps(traffic_from_counters(args.workload, *args.traffic_from, args.copy_mib or 256)))
@@ -152,6 +156,10 @@ def main():
                                    "multi-GPU path in this build (see the design notes on sharding)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+
+    if args.op == "cache_write":
+        bench_cache_write(args)
+        return
 
     import torch
     import paged_mla_decode_02_amd as mla
@@ -276,6 +284,50 @@ def main():
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def bench_cache_write(args):
+    """Latent cache write (mla_cache_write): `tokens` rows of bf16 kv_c [512]
+    and k_pe [64] into random distinct slots of a fp8 (or bf16) pool. HBM-bound:
+    algorithmic bytes = tokens * (576 * 2 read + 576 * elem written + 8 slot)."""
+    import torch
+    import paged_mla_decode_02_amd as mla
+    torch.cuda.set_device(0)
+    mla.load_library()
+    rng = np.random.default_rng(9)
+    T, slots_n = args.tokens, max(4 * args.tokens, 1 << 20)
+    kv_dtype = args.kv_dtype
+    elem = 1 if kv_dtype == "fp8" else 2
+    pool = torch.zeros((slots_n, 576), dtype=torch.uint8 if elem == 1 else torch.int16, device="cuda")
+    kv_c = torch.randn((T, 512), device="cuda").to(torch.bfloat16)
+    k_pe = torch.randn((T, 64), device="cuda").to(torch.bfloat16)
+    slot_sets = [torch.from_numpy(rng.permutation(slots_n)[:T].astype(np.int64)).cuda() for _ in range(3)]
+    scale = torch.tensor([0.05], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for k in range(args.warmup):
+        mla.cache_write(kv_c, k_pe, slot_sets[k % 3], pool, kv_dtype, scale)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for k in range(args.steps):
+        evs[k][0].record(stream)
+        mla.cache_write(kv_c, k_pe, slot_sets[k % 3], pool, kv_dtype, scale)
+        evs[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    alg = T * (576 * 2 + 576 * elem + 8)
+    gbs = alg / (launch_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "latent cache write GB/s", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": "cache_write", "tokens": T, "src": "bf16", "kv_dtype": kv_dtype,
+                   "pool_slots": slots_n},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "cache_write_kernel",
+                     "launch_ms": round(launch_ms, 4), "algorithmic_bytes": alg}}), flush=True)
 
 
 def mla_plan_info(words):

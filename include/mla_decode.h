@@ -153,6 +153,37 @@ MLA_API int32_t mla_debug_gather(const void* kv_pool, mla_dtype kv_dtype, int64_
                          const int32_t* plan_host, const int32_t* plan_dev, int32_t rows,
                          void* dense_out, void* stream);
 
+/* Source element formats of the cache writer's inputs. */
+typedef enum { MLA_SRC_BF16 = 0, MLA_SRC_FP16 = 1, MLA_SRC_FP32 = 2 } mla_src_dtype;
+
+/*
+ * Latent cache write (the step that feeds the decode path: the decode's
+ * KV-cache write of vLLM pull request 57942, Details). For t in [0, tokens):
+ *   pool[slot_mapping[t]][0:512]   = convert(kv_c[t][0:512])
+ *   pool[slot_mapping[t]][512:576] = convert(k_pe[t][0:64])
+ * Each source is read at its own declared dtype and converted, never
+ * reinterpreted: the review thread of that page traces garbage RoPE columns
+ * to an fp32 k_pe tensor written as if it were bf16.
+ *   bf16 pool: round to nearest even (NaN stays a NaN).
+ *   fp8 pool:  v = x / kv_scale in fp32 (one correctly rounded division),
+ *              saturated to +-448, rounded to the nearest e4m3fn value with
+ *              ties to the even code; NaN -> 0x7F; zeros keep their sign.
+ *   kv_c       device, row t at kv_c + t * kv_c_stride elements (stride >= 512)
+ *   k_pe       device, row t at k_pe + t * k_pe_stride elements (stride >= 64)
+ *   slot_mapping  device int64 [tokens]; a negative slot (a padding token) and
+ *              a slot >= num_slots are skipped (nothing is written)
+ *   kv_pool    device [num_slots, 576] of kv_dtype
+ *   kv_scale   device float scalar (fp8), or NULL for 1.0
+ * Tokens with equal slots race (one of them wins). tokens == 0 launches
+ * nothing. Errors: INVALID_ARG (null pointer, bad enum, short stride,
+ * misaligned source, num_slots < 1), HIP.
+ */
+MLA_API int32_t mla_cache_write(const void* kv_c, mla_src_dtype kv_c_dtype, int64_t kv_c_stride,
+                                const void* k_pe, mla_src_dtype k_pe_dtype, int64_t k_pe_stride,
+                                const int64_t* slot_mapping, int32_t tokens, void* kv_pool,
+                                mla_dtype kv_dtype, const float* kv_scale, int64_t num_slots,
+                                void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 MLA_API const char* mla_last_error(void);
 

@@ -61,6 +61,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_decode_fwd.restype = i32
     lib.mla_debug_gather.argtypes = [vp, i32, i64, vp, vp, p32, vp, i32, vp, vp]
     lib.mla_debug_gather.restype = i32
+    lib.mla_cache_write.argtypes = [vp, i32, i64, vp, i32, i64, vp, i32, vp, i32, vp, i64, vp]
+    lib.mla_cache_write.restype = i32
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -151,6 +153,36 @@ def debug_gather(kv_pool, kv_dtype, kv_indptr, kv_indices, plan_host: np.ndarray
         _ptr(kv_pool), _dtype_code(kv_dtype), int(kv_pool.shape[0]), _ptr(kv_indptr),
         _ptr(kv_indices), ph.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(plan_dev), rows,
         _ptr(dense_out), _stream_handle(stream))
+    _check(st)
+
+
+MLA_SRC_BF16, MLA_SRC_FP16, MLA_SRC_FP32 = 0, 1, 2
+
+
+def cache_write(kv_c, k_pe, slot_mapping, kv_pool, kv_dtype, kv_scale=None, stream=None):
+    """Enqueue mla_cache_write. kv_c [T, 512] and k_pe [T, 64] are device
+    tensors of bfloat16, float16 or float32 (rows may be strided, elements
+    contiguous); each is passed with its own dtype. slot_mapping is an int64
+    device tensor [T] (negative = skip); kv_pool holds the stored codes
+    [num_slots, 576]; kv_scale a 1-element float32 device tensor or None."""
+    import torch
+    src = {torch.bfloat16: MLA_SRC_BF16, torch.float16: MLA_SRC_FP16, torch.float32: MLA_SRC_FP32}
+    for name, t, width in (("kv_c", kv_c, 512), ("k_pe", k_pe, 64)):
+        if t.dtype not in src:
+            raise TypeError(f"{name} must be bfloat16, float16 or float32, got {t.dtype}")
+        if t.dim() != 2 or t.shape[1] != width or t.stride(1) != 1:
+            raise ValueError(f"{name} must be [tokens, {width}] with contiguous rows")
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
+        raise TypeError("slot_mapping must be a contiguous int64 tensor")
+    tokens = int(slot_mapping.shape[0])
+    if kv_c.shape[0] != tokens or k_pe.shape[0] != tokens:
+        raise ValueError("kv_c, k_pe and slot_mapping must have the same number of tokens")
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != 576 or not kv_pool.is_contiguous():
+        raise ValueError("kv_pool must be a contiguous [num_slots, 576] tensor")
+    st = load_library().mla_cache_write(
+        _ptr(kv_c), src[kv_c.dtype], int(kv_c.stride(0)), _ptr(k_pe), src[k_pe.dtype],
+        int(k_pe.stride(0)), _ptr(slot_mapping), tokens, _ptr(kv_pool), _dtype_code(kv_dtype),
+        _ptr(kv_scale), int(kv_pool.shape[0]), _stream_handle(stream))
     _check(st)
 
 

@@ -154,3 +154,45 @@ extern "C" int32_t mla_debug_gather(const void* kv_pool, mla_dtype kv_dtype, int
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("gather launch: ") + hipGetErrorString(e));
   return MLA_OK;
 }
+
+extern "C" int32_t mla_cache_write(const void* kv_c, mla_src_dtype kv_c_dtype, int64_t kv_c_stride,
+                                   const void* k_pe, mla_src_dtype k_pe_dtype, int64_t k_pe_stride,
+                                   const int64_t* slot_mapping, int32_t tokens, void* kv_pool,
+                                   mla_dtype kv_dtype, const float* kv_scale, int64_t num_slots,
+                                   void* stream) {
+  clear_error();
+  if (tokens < 0) return set_error(MLA_ERR_INVALID_ARG, "tokens must be >= 0");
+  if (!valid_dtype(kv_dtype)) return set_error(MLA_ERR_INVALID_ARG, "unknown kv_dtype");
+  auto src_size = [](int d) { return d == MLA_SRC_BF16 || d == MLA_SRC_FP16 ? 2 : d == MLA_SRC_FP32 ? 4 : 0; };
+  if (!src_size(kv_c_dtype) || !src_size(k_pe_dtype))
+    return set_error(MLA_ERR_INVALID_ARG, "unknown source dtype (expected MLA_SRC_BF16, MLA_SRC_FP16 or MLA_SRC_FP32)");
+  if (num_slots < 1) return set_error(MLA_ERR_INVALID_ARG, "num_slots must be >= 1");
+  if (kv_c_stride < 512 || k_pe_stride < 64)
+    return set_error(MLA_ERR_INVALID_ARG, "kv_c_stride must be >= 512 and k_pe_stride >= 64");
+  if (tokens == 0) return MLA_OK;
+  if (!kv_c || !k_pe || !slot_mapping || !kv_pool)
+    return set_error(MLA_ERR_INVALID_ARG, "a required pointer is null");
+  if ((uintptr_t)kv_c % src_size(kv_c_dtype) || (uintptr_t)k_pe % src_size(k_pe_dtype) ||
+      (uintptr_t)slot_mapping % 8 || (uintptr_t)kv_pool % 2)
+    return set_error(MLA_ERR_INVALID_ARG, "a pointer is not aligned to its element size");
+  CacheWriteArgs a;
+  a.kv_c = kv_c;
+  a.k_pe = k_pe;
+  a.kv_c_dtype = kv_c_dtype;
+  a.k_pe_dtype = k_pe_dtype;
+  a.kv_c_stride = kv_c_stride;
+  a.k_pe_stride = k_pe_stride;
+  a.slots = slot_mapping;
+  a.tokens = tokens;
+  a.kv_fp8 = kv_dtype == MLA_FP8_E4M3;
+  a.pool = kv_pool;
+  a.kv_scale = kv_scale;
+  a.num_slots = num_slots;
+  // 8-element chunks need every row start and the pool 16-byte aligned.
+  const bool vec = aligned16(kv_c) && aligned16(k_pe) && aligned16(kv_pool) &&
+                   (kv_c_stride * src_size(kv_c_dtype)) % 16 == 0 &&
+                   (k_pe_stride * src_size(k_pe_dtype)) % 16 == 0;
+  hipError_t e = launch_cache_write(a, vec, (hipStream_t)stream);
+  if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("cache write launch: ") + hipGetErrorString(e));
+  return MLA_OK;
+}

@@ -48,11 +48,25 @@ struct GatherArgs {
   uint16_t* dense;          // bf16 [nnz, 576]
 };
 
+struct CacheWriteArgs {
+  const void* kv_c;         // [tokens] rows of 512 at kv_c_stride elements
+  const void* k_pe;         // [tokens] rows of 64 at k_pe_stride elements
+  int32_t kv_c_dtype, k_pe_dtype;   // mla_src_dtype
+  int64_t kv_c_stride, k_pe_stride;
+  const int64_t* slots;     // [tokens]
+  int32_t tokens, kv_fp8;
+  void* pool;               // [num_slots, 576]
+  const float* kv_scale;    // device scalar or null
+  int64_t num_slots;
+};
+
 constexpr int kBlockThreads = 256;   // merge kernel: 4 waves of 64, one block per (row, token, head)
 constexpr int kDecodeThreads = 512;  // decode and gather kernels: 8 waves of 64
 
 hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, int grid, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, bool kv_fp8, int splits, hipStream_t st);
+// vec: every source row and the pool are 16-byte aligned (8-element chunks).
+hipError_t launch_cache_write(const CacheWriteArgs& a, bool vec, hipStream_t st);
 
 }  // namespace mla

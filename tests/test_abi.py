@@ -30,7 +30,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 7
+    assert len(syms) == 8
     handle = ctypes.CDLL(lib_mod.LIB_PATH)
     for s in syms:
         assert hasattr(handle, s), s
@@ -154,3 +154,23 @@ def test_gather_argument_errors(lib):
     assert g(rows=5) == MISMATCH
     assert g(slots=0) == INVALID
     assert g(plan_dev=None) == INVALID
+
+
+def test_cache_write_argument_errors(lib):
+    def c(kv_c=FAKE, kv_c_dtype=0, kv_c_stride=512, k_pe=FAKE, k_pe_dtype=0, k_pe_stride=64,
+          slots=FAKE, tokens=4, pool=FAKE, kv_dtype=0, slots_n=100):
+        return lib.mla_cache_write(kv_c, kv_c_dtype, kv_c_stride, k_pe, k_pe_dtype, k_pe_stride,
+                                   slots, tokens, pool, kv_dtype, None, slots_n, None)
+
+    assert c(tokens=0, kv_c=None, k_pe=None, slots=None, pool=None) == OK   # nothing to do
+    assert c(tokens=-1) == INVALID
+    assert c(kv_c=None) == INVALID
+    assert c(pool=None) == INVALID
+    assert c(kv_c_dtype=3) == INVALID
+    assert c(k_pe_dtype=-1) == INVALID
+    assert c(kv_dtype=2) == INVALID
+    assert c(kv_c_stride=511) == INVALID
+    assert c(k_pe_stride=63) == INVALID
+    assert c(slots_n=0) == INVALID
+    assert c(kv_c=FAKE + 2, kv_c_dtype=2) == INVALID    # fp32 source not 4-byte aligned
+    assert c(slots=FAKE + 4) == INVALID                  # int64 slots not 8-byte aligned
