@@ -141,8 +141,11 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="only turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-mib run into profiles/traffic_<workload>.json")
-    ap.add_argument("--op", default="decode", choices=["decode", "cache_write"],
-                    help="decode: the hot path (default); cache_write: the latent cache writer")
+    ap.add_argument("--op", default="decode", choices=["decode", "cache_write", "dcp"],
+                    help="decode: the hot path (default); cache_write: the latent cache writer; "
+                         "dcp: one decode-context-parallel rank and the shard merge")
+    ap.add_argument("--dcp-world", type=int, default=8, help="dcp: ranks")
+    ap.add_argument("--heads", type=int, default=64, help="dcp: gathered query heads per rank")
     ap.add_argument("--tokens", type=int, default=65536, help="cache_write: tokens per call")
     ap.add_argument("--kv-dtype", default="fp8", choices=["fp8", "bf16"], help="cache_write: pool dtype")
     args = ap.parse_args()
@@ -159,6 +162,9 @@ def main():
 
     if args.op == "cache_write":
         bench_cache_write(args)
+        return
+    if args.op == "dcp":
+        bench_dcp(args)
         return
 
     import torch
@@ -328,6 +334,88 @@ def bench_cache_write(args):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "cache_write_kernel",
                      "launch_ms": round(launch_ms, 4), "algorithmic_bytes": alg}}), flush=True)
+
+
+def bench_dcp(args):
+    """One decode-context-parallel rank at the verify shape: 32 rows, q_len 8,
+    `heads` gathered query heads, bf16, causal; the rows' lengths of the verify
+    workload dealt round-robin over `world` ranks (rank 0 measured: its keys
+    sit at global positions 0, W, 2W, ...). Also times the W-way shard merge
+    (mla_merge_shards) of W bf16 shard results of that shape."""
+    import torch
+    import paged_mla_decode_02_amd as mla
+    from workloads import config_lengths, make_case
+    torch.cuda.set_device(0)
+    mla.load_library()
+    W, H = args.dcp_world, args.heads
+    lens = config_lengths("verify_causal")
+    case = make_case(2, lens, heads=H, q_len=8, q_dtype="bf16", kv_dtype="bf16", causal=True,
+                     pool_slots=524288, name="dcp_verify")
+    idx, loc = [], []
+    for b in range(case.rows):
+        lo, hi = int(case.kv_indptr[b]), int(case.kv_indptr[b + 1])
+        part = np.asarray(case.kv_indices[lo:hi])[0::W]
+        idx.append(part)
+        loc.append(len(part))
+    loc = np.array(loc, np.int32)
+    indptr = torch.from_numpy(np.concatenate([[0], np.cumsum(loc)]).astype(np.int32)).cuda()
+    flat = torch.from_numpy(np.concatenate(idx).astype(np.int32)).cuda()
+    dev = mla.device_inputs(case.q_codes, case.q_scale, case.pool_codes, case.kv_scale,
+                            case.qo_indptr, case.kv_indptr, case.kv_indices)
+    glob = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+    words = mla.plan(loc, H, 8, "bf16")
+    plan_dev = torch.from_numpy(words).cuda()
+    ws = torch.empty(max(mla.workspace_size(words), 16), dtype=torch.uint8, device="cuda")
+    T = case.num_tokens
+    o = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    o_parts = torch.randn((W, T, H, 512), device="cuda").to(torch.bfloat16)
+    lse_parts = torch.randn((W, T, H), device="cuda")
+    om = torch.empty_like(o)
+    lm = torch.empty_like(lse)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        mla.decode_fwd_dcp(dev["q"], "bf16", None, dev["kv_pool"], "bf16", None, dev["qo_indptr"], indptr,
+                           flat, words, plan_dev, case.rows, H, 8, True, float(case.sm_scale), o, lse,
+                           W, 0, glob, ws)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    t_dec = timed(fwd)
+    t_mrg = timed(lambda: mla.merge_shards(o_parts, lse_parts, om, lm))
+    keys = int(loc.sum())
+    qpos = [(int(L) - 8 + i) for L in lens for i in range(8)]
+    pairs = sum(len(range(0, qp + 1, W)) for qp in qpos if qp >= 0)
+    flops = 2.0 * (576 + 512) * H * pairs
+    tf = flops / (t_dec * 1e-3) / 1e12
+    mbytes = W * T * H * (1024 + 4) + T * H * (1024 + 4)
+    gbs = mbytes / (t_mrg * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "DCP shard decode MFMA TFLOP/s (one rank) + shard merge GB/s", "value": round(tf, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_dec + t_mrg, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "dcp_verify_rank0", "dcp_world": W, "heads": H, "rows": case.rows,
+                   "q_len": 8, "local_keys": keys, "splits": int(words[14])},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4), "traffic": None,
+                     "kernel": "decode_kernel (+merge_kernel if split)", "launch_ms": round(t_dec, 4),
+                     "algorithmic_flops": flops},
+        "merge": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "shard_merge_kernel",
+                  "launch_ms": round(t_mrg, 4), "algorithmic_bytes": mbytes}}), flush=True)
 
 
 def mla_plan_info(words):

@@ -63,6 +63,7 @@ extern "C" {
 #define MLA_D_V 512        /* V = the first 512 latent dims */
 #define MLA_MAX_HEADS 128
 #define MLA_MAX_Q_LEN 16
+#define MLA_MAX_DCP_WORLD 64
 
 typedef enum {
   MLA_OK = 0,
@@ -139,6 +140,54 @@ MLA_API int32_t mla_decode_fwd(const void* q, mla_dtype q_dtype, const float* q_
                        const int32_t* plan_dev, int32_t rows, int32_t num_heads,
                        int32_t q_len_max, int32_t causal, float softmax_scale, void* o,
                        float* lse, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Decode of one decode-context-parallel (DCP) shard. With dcp_world ranks the
+ * KV of a row is dealt round-robin: rank dcp_rank holds the keys whose global
+ * position is dcp_rank, dcp_rank + dcp_world, ..., so its local key j (the
+ * j-th entry of its own index list) sits at global position
+ * j * dcp_world + dcp_rank. A q_b-token block at the end of a row of
+ * P = kv_len_global[b] keys in total has token i at global position
+ * P - q_b + i, and the causal mask is taken on global positions (ATOM pull
+ * request 2760, Problem): local key j is visible iff
+ * j * dcp_world + dcp_rank <= P - q_b + i. Non-causal blocks see every local
+ * key. The result is this shard's (O_r, LSE_r) per (token, head); the
+ * shards' results combine with mla_merge_shards.
+ * Arguments as mla_decode_fwd (the plan is built from the shard's local
+ * lengths), plus:
+ *   dcp_world      1..64;  dcp_rank  0..dcp_world-1
+ *   kv_len_global  device int32 [rows], P per row (caller contract: the
+ *                  shard's local length is the number of positions
+ *                  p < P with p mod dcp_world == dcp_rank)
+ * dcp_world = 1, dcp_rank = 0 and P = the local length is mla_decode_fwd.
+ * Errors: those of mla_decode_fwd, and INVALID_ARG for a bad world, rank or
+ * a null kv_len_global.
+ */
+MLA_API int32_t mla_decode_fwd_dcp(const void* q, mla_dtype q_dtype, const float* q_scale,
+                                   const void* kv_pool, mla_dtype kv_dtype, const float* kv_scale,
+                                   int64_t num_slots, const int32_t* qo_indptr,
+                                   const int32_t* kv_indptr, const int32_t* kv_indices,
+                                   const int32_t* plan_host, const int32_t* plan_dev, int32_t rows,
+                                   int32_t num_heads, int32_t q_len_max, int32_t causal,
+                                   float softmax_scale, void* o, float* lse, void* workspace,
+                                   int64_t workspace_bytes, int32_t dcp_world, int32_t dcp_rank,
+                                   const int32_t* kv_len_global, void* stream);
+
+/*
+ * Log-sum-exp merge of `world` shard results (the combine step of DCP; the
+ * same merge as that of split-KV partials):
+ *   LSE = ln sum_r exp(LSE_r),  O = sum_r exp(LSE_r - LSE) * O_r  (bf16)
+ * shards with LSE_r = -inf are skipped; if all are, O = 0 and LSE = -inf.
+ *   o_parts    device bf16 [world, tokens, num_heads, 512], 16-byte aligned
+ *              (shard r's mla_decode_fwd_dcp output at index r)
+ *   lse_parts  device fp32 [world, tokens, num_heads]
+ *   o, lse     device bf16 [tokens, num_heads, 512] (16-byte aligned), fp32
+ *              [tokens, num_heads]
+ * world 1..64. tokens == 0 launches nothing. Errors: INVALID_ARG, HIP.
+ */
+MLA_API int32_t mla_merge_shards(const void* o_parts, const float* lse_parts, int32_t world,
+                                 int32_t tokens, int32_t num_heads, void* o, float* lse,
+                                 void* stream);
 
 /*
  * Test hook: run the decode kernel's own index gather and tile loader over

@@ -61,6 +61,11 @@ def load_library(path: str = LIB_PATH):
     lib.mla_decode_fwd.restype = i32
     lib.mla_debug_gather.argtypes = [vp, i32, i64, vp, vp, p32, vp, i32, vp, vp]
     lib.mla_debug_gather.restype = i32
+    lib.mla_decode_fwd_dcp.argtypes = [vp, i32, vp, vp, i32, vp, i64, vp, vp, vp, p32, vp, i32, i32,
+                                       i32, i32, ctypes.c_float, vp, vp, vp, i64, i32, i32, vp, vp]
+    lib.mla_decode_fwd_dcp.restype = i32
+    lib.mla_merge_shards.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.mla_merge_shards.restype = i32
     lib.mla_cache_write.argtypes = [vp, i32, i64, vp, i32, i64, vp, i32, vp, i32, vp, i64, vp]
     lib.mla_cache_write.restype = i32
     lib.mla_last_error.argtypes = []
@@ -144,6 +149,36 @@ def decode_fwd(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, kv_i
         1 if causal else 0, float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
         _stream_handle(stream))
     _check(st)
+
+
+def decode_fwd_dcp(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, kv_indptr, kv_indices,
+                   plan_host: np.ndarray, plan_dev, rows: int, heads: int, q_len_max: int, causal: bool,
+                   softmax_scale: float, o, lse, dcp_world: int, dcp_rank: int, kv_len_global,
+                   workspace=None, stream=None):
+    """Enqueue mla_decode_fwd_dcp for shard dcp_rank of dcp_world (its own
+    index lists and plan); kv_len_global is an int32 device tensor [rows]."""
+    ph = _host_i32(plan_host)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().mla_decode_fwd_dcp(
+        _ptr(q), _dtype_code(q_dtype), _ptr(q_scale), _ptr(kv_pool), _dtype_code(kv_dtype),
+        _ptr(kv_scale), int(kv_pool.shape[0]), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices),
+        ph.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(plan_dev), rows, heads, q_len_max,
+        1 if causal else 0, float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
+        int(dcp_world), int(dcp_rank), _ptr(kv_len_global), _stream_handle(stream))
+    _check(st)
+
+
+def merge_shards(o_parts, lse_parts, o, lse, stream=None):
+    """Enqueue mla_merge_shards: o_parts bf16 [W, T, H, 512], lse_parts fp32
+    [W, T, H] -> o bf16 [T, H, 512], lse fp32 [T, H]."""
+    W, T, H = int(o_parts.shape[0]), int(o_parts.shape[1]), int(o_parts.shape[2])
+    if tuple(lse_parts.shape) != (W, T, H) or tuple(o.shape) != (T, H, 512) or tuple(lse.shape) != (T, H):
+        raise ValueError("shape mismatch between o_parts, lse_parts, o and lse")
+    for t in (o_parts, lse_parts, o, lse):
+        if not t.is_contiguous():
+            raise ValueError("merge_shards needs contiguous tensors")
+    _check(load_library().mla_merge_shards(_ptr(o_parts), _ptr(lse_parts), W, T, H, _ptr(o), _ptr(lse),
+                                           _stream_handle(stream)))
 
 
 def debug_gather(kv_pool, kv_dtype, kv_indptr, kv_indices, plan_host: np.ndarray, plan_dev,

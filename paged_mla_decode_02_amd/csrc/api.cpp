@@ -37,15 +37,16 @@ int32_t check_plan_for_call(const int32_t* plan_host, const int32_t* plan_dev, i
 
 }  // namespace
 
-extern "C" int32_t mla_decode_fwd(const void* q, mla_dtype q_dtype, const float* q_scale,
-                                  const void* kv_pool, mla_dtype kv_dtype, const float* kv_scale,
-                                  int64_t num_slots, const int32_t* qo_indptr,
-                                  const int32_t* kv_indptr, const int32_t* kv_indices,
-                                  const int32_t* plan_host, const int32_t* plan_dev, int32_t rows,
-                                  int32_t num_heads, int32_t q_len_max, int32_t causal,
-                                  float softmax_scale, void* o, float* lse, void* workspace,
-                                  int64_t workspace_bytes, void* stream) {
-  clear_error();
+namespace {
+
+// Shared by mla_decode_fwd (world 1) and mla_decode_fwd_dcp.
+int32_t decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale, const void* kv_pool,
+                    mla_dtype kv_dtype, const float* kv_scale, int64_t num_slots,
+                    const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                    const int32_t* plan_host, const int32_t* plan_dev, int32_t rows,
+                    int32_t num_heads, int32_t q_len_max, int32_t causal, float softmax_scale,
+                    void* o, float* lse, void* workspace, int64_t workspace_bytes, void* stream,
+                    int32_t dcp_world, int32_t dcp_rank, const int32_t* kv_len_global) {
   if (!q || !kv_pool || !qo_indptr || !kv_indptr || !kv_indices || !plan_host || !o || !lse)
     return set_error(MLA_ERR_INVALID_ARG, "a required pointer is null");
   if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype))
@@ -96,6 +97,9 @@ extern "C" int32_t mla_decode_fwd(const void* q, mla_dtype q_dtype, const float*
   a.q_len_max = q_len_max;
   a.causal = causal;
   a.score_scale_log2 = softmax_scale * 1.44269504088896340736f;
+  a.dcp_world = dcp_world;
+  a.dcp_rank = dcp_rank;
+  a.kv_len_global = kv_len_global;
   a.o = (uint16_t*)o;
   a.lse = lse;
   const int64_t ws_o_elems = (int64_t)v.P * q_len_max * num_heads * MLA_D_V;
@@ -120,6 +124,65 @@ extern "C" int32_t mla_decode_fwd(const void* q, mla_dtype q_dtype, const float*
     e = launch_merge(mg, rows, num_heads, q_len_max, s);
     if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
   }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t mla_decode_fwd(const void* q, mla_dtype q_dtype, const float* q_scale,
+                                  const void* kv_pool, mla_dtype kv_dtype, const float* kv_scale,
+                                  int64_t num_slots, const int32_t* qo_indptr,
+                                  const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  const int32_t* plan_host, const int32_t* plan_dev, int32_t rows,
+                                  int32_t num_heads, int32_t q_len_max, int32_t causal,
+                                  float softmax_scale, void* o, float* lse, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+  clear_error();
+  return decode_impl(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, num_slots, qo_indptr,
+                     kv_indptr, kv_indices, plan_host, plan_dev, rows, num_heads, q_len_max, causal,
+                     softmax_scale, o, lse, workspace, workspace_bytes, stream, 1, 0, nullptr);
+}
+
+extern "C" int32_t mla_decode_fwd_dcp(const void* q, mla_dtype q_dtype, const float* q_scale,
+                                      const void* kv_pool, mla_dtype kv_dtype, const float* kv_scale,
+                                      int64_t num_slots, const int32_t* qo_indptr,
+                                      const int32_t* kv_indptr, const int32_t* kv_indices,
+                                      const int32_t* plan_host, const int32_t* plan_dev,
+                                      int32_t rows, int32_t num_heads, int32_t q_len_max,
+                                      int32_t causal, float softmax_scale, void* o, float* lse,
+                                      void* workspace, int64_t workspace_bytes, int32_t dcp_world,
+                                      int32_t dcp_rank, const int32_t* kv_len_global, void* stream) {
+  clear_error();
+  if (dcp_world < 1 || dcp_world > MLA_MAX_DCP_WORLD)
+    return set_error(MLA_ERR_INVALID_ARG, "dcp_world must be in 1..64");
+  if (dcp_rank < 0 || dcp_rank >= dcp_world)
+    return set_error(MLA_ERR_INVALID_ARG, "dcp_rank must be in 0..dcp_world-1");
+  if (!kv_len_global) return set_error(MLA_ERR_INVALID_ARG, "kv_len_global is null");
+  return decode_impl(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, num_slots, qo_indptr,
+                     kv_indptr, kv_indices, plan_host, plan_dev, rows, num_heads, q_len_max, causal,
+                     softmax_scale, o, lse, workspace, workspace_bytes, stream, dcp_world, dcp_rank,
+                     kv_len_global);
+}
+
+extern "C" int32_t mla_merge_shards(const void* o_parts, const float* lse_parts, int32_t world,
+                                    int32_t tokens, int32_t num_heads, void* o, float* lse,
+                                    void* stream) {
+  clear_error();
+  if (world < 1 || world > MLA_MAX_DCP_WORLD) return set_error(MLA_ERR_INVALID_ARG, "world must be in 1..64");
+  if (tokens < 0 || num_heads < 1 || num_heads > MLA_MAX_HEADS)
+    return set_error(MLA_ERR_INVALID_ARG, "tokens must be >= 0 and num_heads in 1..128");
+  if (tokens == 0) return MLA_OK;
+  if (!o_parts || !lse_parts || !o || !lse) return set_error(MLA_ERR_INVALID_ARG, "a required pointer is null");
+  if (!aligned16(o_parts) || !aligned16(o)) return set_error(MLA_ERR_INVALID_ARG, "o_parts and o must be 16-byte aligned");
+  ShardMergeArgs m;
+  m.o_parts = (const uint16_t*)o_parts;
+  m.lse_parts = lse_parts;
+  m.world = world;
+  m.rows = tokens * num_heads;
+  m.o = (uint16_t*)o;
+  m.lse = lse;
+  hipError_t e = launch_shard_merge(m, (hipStream_t)stream);
+  if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("shard merge launch: ") + hipGetErrorString(e));
   return MLA_OK;
 }
 

@@ -22,6 +22,8 @@ struct DecodeArgs {
   int32_t off_work_indptr, off_item_split, off_item_m;
   int32_t heads, q_len_max, causal;
   float score_scale_log2;   // softmax_scale * log2(e)
+  int32_t dcp_world, dcp_rank;      // round-robin KV shard: local key j at position j * world + rank
+  const int32_t* kv_len_global;     // [rows] keys of each row over all shards, or null (= local)
   uint16_t* o;              // bf16 bits
   float* lse;
   float* ws_o;              // [P, q_len_max, heads, 512] fp32 partial O
@@ -48,6 +50,14 @@ struct GatherArgs {
   uint16_t* dense;          // bf16 [nnz, 576]
 };
 
+struct ShardMergeArgs {
+  const uint16_t* o_parts;  // bf16 [world, rows, 512]
+  const float* lse_parts;   // [world, rows]
+  int32_t world, rows;      // rows = tokens * heads
+  uint16_t* o;              // bf16 [rows, 512]
+  float* lse;               // [rows]
+};
+
 struct CacheWriteArgs {
   const void* kv_c;         // [tokens] rows of 512 at kv_c_stride elements
   const void* k_pe;         // [tokens] rows of 64 at k_pe_stride elements
@@ -66,6 +76,7 @@ constexpr int kDecodeThreads = 512;  // decode and gather kernels: 8 waves of 64
 hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, int grid, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, bool kv_fp8, int splits, hipStream_t st);
+hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t st);
 // vec: every source row and the pool are 16-byte aligned (8-element chunks).
 hipError_t launch_cache_write(const CacheWriteArgs& a, bool vec, hipStream_t st);
 

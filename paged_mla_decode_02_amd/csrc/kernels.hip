@@ -536,9 +536,16 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       const bool row_ok = mr < M;
       const int tok = row_ok ? mr / H : 0;
       const int head = row_ok ? mr - tok * H : 0;
-      // Rows past the end of the block are computed but never written; they
-      // take the non-causal limit so that they never force the masked path.
-      const int pos_limit = (a.causal && row_ok) ? (L - q_b + tok) : (L - 1);
+      // Causal mask on global positions: local key j sits at j * world + rank
+      // of the row's P keys over all shards, token tok at P - q_b + tok; the
+      // visible local keys are j <= (P - q_b + tok - rank) / world (one shard:
+      // j <= L - q_b + tok). Rows past the end of the block are computed but
+      // never written; they take the non-causal limit so that they never
+      // force the masked path.
+      const int P = a.kv_len_global ? a.kv_len_global[b] : L;
+      const int qpos = P - q_b + tok - a.dcp_rank;
+      const int causal_lim = qpos >= 0 ? qpos / a.dcp_world : -1;
+      const int pos_limit = (a.causal && row_ok) ? causal_lim : (L - 1);
       // Rows are ordered token-major, so lane 0 holds the wave's smallest
       // position limit.
       const int pos_min = __builtin_amdgcn_readfirstlane(pos_limit);
@@ -688,11 +695,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
 
 // ---------------------------------------------------------------------------
 // Split merge: one block of four waves per (request row b, query token i,
-// head h) of a row with n > 1 splits (n <= 64). Lane k of every wave reads
-// LSE_k; the wave reduces max and sum with permlane swaps and DPP-free
-// shuffles; wave w then accumulates the weighted partial O_k of splits
-// k = w, w + 4, ... (a lane owns 8 columns, 8 splits' loads in flight) and the
-// four partial sums meet in LDS.
+// heads 4 j .. 4 j + 3) of a row with n > 1 splits (n <= 64). Lane k of a wave
+// reads LSE_k and the wave reduces max and sum. With n <= 8 splits each wave
+// merges one head, all n partials' loads in flight at once; with more, the
+// four waves take every fourth split of one head at a time and add up in
+// LDS. A lane owns 8 output columns.
 __device__ __forceinline__ float wave_max(float v) {
   v = group_max(v);   // over lanes l, l^16, l^32, l^48
 #pragma unroll
@@ -706,10 +713,42 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Weights of the n partials of one (token, head): lane k gets
+// exp(LSE_k - LSE); returns false (and writes O = 0, LSE = -inf) when every
+// split is empty.
+__device__ __forceinline__ bool merge_weights(const MergeArgs& a, int64_t base, int64_t stride, int n,
+                                              int lane, int64_t orow, float& wk, float& lse, bool writer) {
+  const float lk = lane < n ? a.ws_lse[base + lane * stride] : -INFINITY;
+  const float mx = wave_max(lk);
+  if (mx == -INFINITY) {
+    if (writer) {
+      *(u32x4*)(a.o + orow * kDV + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+      if (lane == 0) a.lse[orow] = -INFINITY;
+    }
+    return false;
+  }
+  const float kLog2e = 1.44269504088896340736f;
+  const float ek = lk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lk - mx) * kLog2e);
+  const float tot = wave_sum(ek);
+  wk = ek / tot;
+  lse = mx + __log2f(tot) * kLn2;
+  return true;
+}
+
+__device__ __forceinline__ void store_row(const MergeArgs& a, int64_t orow, int lane, f32x4 acc0, f32x4 acc1,
+                                          float lse) {
+  *(bf16x8*)(a.o + orow * kDV + lane * 8) =
+      bf16x8{(__bf16)acc0[0], (__bf16)acc0[1], (__bf16)acc0[2], (__bf16)acc0[3],
+             (__bf16)acc1[0], (__bf16)acc1[1], (__bf16)acc1[2], (__bf16)acc1[3]};
+  if (lane == 0) a.lse[orow] = lse;
+}
+
 __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
   __shared__ f32x4 part[kBlockThreads / 64 - 1][64][2];
-  const int h = blockIdx.x % a.heads;
-  const int bi = blockIdx.x / a.heads;
+  constexpr int kW = kBlockThreads / 64;
+  const int hgroups = (a.heads + kW - 1) / kW;
+  const int hg = blockIdx.x % hgroups;
+  const int bi = blockIdx.x / hgroups;
   const int b = bi / a.q_len_max;
   const int i = bi - b * a.q_len_max;
   const int s0 = a.plan[a.off_split_indptr + b];
@@ -720,65 +759,114 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int part0 = a.plan[a.off_split_part + s0];
   const int64_t stride = (int64_t)a.q_len_max * a.heads;   // partial slots are consecutive
-  const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
-  const int64_t orow = (int64_t)(q0 + i) * a.heads + h;
 
-  const float lk = lane < n ? a.ws_lse[base + lane * stride] : -INFINITY;
-  const float mx = wave_max(lk);
-  if (mx == -INFINITY) {   // every split empty: uniform over the block
-    if (w == 0) {
-      *(u32x4*)(a.o + orow * kDV + lane * 8) = u32x4{0u, 0u, 0u, 0u};
-      if (lane == 0) a.lse[orow] = -INFINITY;
-    }
-    return;
-  }
-  const float kLog2e = 1.44269504088896340736f;
-  const float ek = lk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lk - mx) * kLog2e);
-  const float tot = wave_sum(ek);
-  const float wk = ek / tot;   // weight of split `lane`
-
-  const float* src = a.ws_o + base * kDV + lane * 8;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  constexpr int kWaves = kBlockThreads / 64;
-  for (int k0 = w; k0 < n; k0 += 8 * kWaves) {
+  if (n <= 8) {   // one wave per head (uniform over the block: n is the row's)
+    const int h = hg * kW + w;
+    if (h >= a.heads) return;
+    const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
+    const int64_t orow = (int64_t)(q0 + i) * a.heads + h;
+    float wk, lse;
+    if (!merge_weights(a, base, stride, n, lane, orow, wk, lse, true)) return;
+    const float* src = a.ws_o + base * kDV + lane * 8;
     f32x4 v[8][2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = k0 + u * kWaves;
+    for (int k = 0; k < 8; ++k)
       if (k < n) {
         const f32x4* p = (const f32x4*)(src + k * stride * kDV);
-        v[u][0] = p[0];
-        v[u][1] = p[1];
+        v[k][0] = p[0];
+        v[k][1] = p[1];
       }
-    }
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = k0 + u * kWaves;
+    for (int k = 0; k < 8; ++k)
       if (k < n) {
         const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), k));
-        if (c != 0.f) {   // an empty split's partial is never read
+        acc0 += c * v[k][0];   // an empty split's partial is 0 and its weight 0
+        acc1 += c * v[k][1];
+      }
+    store_row(a, orow, lane, acc0, acc1, lse);
+    return;
+  }
+
+  for (int hh = 0; hh < kW; ++hh) {   // four waves per head, one head at a time
+    const int h = hg * kW + hh;
+    if (h >= a.heads) break;          // uniform
+    const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
+    const int64_t orow = (int64_t)(q0 + i) * a.heads + h;
+    float wk, lse;
+    if (!merge_weights(a, base, stride, n, lane, orow, wk, lse, w == 0)) continue;   // uniform
+    const float* src = a.ws_o + base * kDV + lane * 8;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = w; k0 < n; k0 += 8 * kW) {
+      f32x4 v[8][2];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u * kW;
+        if (k < n) {
+          const f32x4* p = (const f32x4*)(src + k * stride * kDV);
+          v[u][0] = p[0];
+          v[u][1] = p[1];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u * kW;
+        if (k < n) {
+          const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), k));
           acc0 += c * v[u][0];
           acc1 += c * v[u][1];
         }
       }
     }
-  }
-  if (w > 0) {
-    part[w - 1][lane][0] = acc0;
-    part[w - 1][lane][1] = acc1;
-  }
-  __syncthreads();
-  if (w == 0) {
-#pragma unroll
-    for (int j = 0; j < kWaves - 1; ++j) {
-      acc0 += part[j][lane][0];
-      acc1 += part[j][lane][1];
+    if (w > 0) {
+      part[w - 1][lane][0] = acc0;
+      part[w - 1][lane][1] = acc1;
     }
-    const bf16x8 out = {(__bf16)acc0[0], (__bf16)acc0[1], (__bf16)acc0[2], (__bf16)acc0[3],
-                        (__bf16)acc1[0], (__bf16)acc1[1], (__bf16)acc1[2], (__bf16)acc1[3]};
-    *(bf16x8*)(a.o + orow * kDV + lane * 8) = out;
-    if (lane == 0) a.lse[orow] = mx + __log2f(tot) * kLn2;
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int j = 0; j < kW - 1; ++j) {
+        acc0 += part[j][lane][0];
+        acc1 += part[j][lane][1];
+      }
+      store_row(a, orow, lane, acc0, acc1, lse);
+    }
+    __syncthreads();   // part[] is reused for the next head
   }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of decode-context-parallel shard outputs: one wave per (token, head)
+// row; lane k < world reads LSE_k, the wave reduces max and sum, and every
+// lane accumulates 8 columns of the weighted bf16 shard outputs (a shard with
+// no visible key has O = 0 and weight 0).
+__global__ __launch_bounds__(kBlockThreads) void shard_merge_kernel(ShardMergeArgs a) {
+  const int row = blockIdx.x * (kBlockThreads / 64) + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int lane = threadIdx.x & 63;
+  const float lk = lane < a.world ? a.lse_parts[(int64_t)lane * a.rows + row] : -INFINITY;
+  const float mx = wave_max(lk);
+  uint16_t* dst = a.o + (int64_t)row * kDV + lane * 8;
+  if (mx == -INFINITY) {   // no shard sees a key
+    *(u32x4*)dst = u32x4{0u, 0u, 0u, 0u};
+    if (lane == 0) a.lse[row] = -INFINITY;
+    return;
+  }
+  const float kLog2e = 1.44269504088896340736f;
+  const float ek = lk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lk - mx) * kLog2e);
+  const float tot = wave_sum(ek);
+  const float wk = ek / tot;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int k = 0; k < a.world; ++k) {
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), k));
+    const bf16x8 v = *(const bf16x8*)(a.o_parts + ((int64_t)k * a.rows + row) * kDV + lane * 8);
+    acc0 += c * f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    acc1 += c * f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+  }
+  *(bf16x8*)dst = bf16x8{(__bf16)acc0[0], (__bf16)acc0[1], (__bf16)acc0[2], (__bf16)acc0[3],
+                         (__bf16)acc1[0], (__bf16)acc1[1], (__bf16)acc1[2], (__bf16)acc1[3]};
+  if (lane == 0) a.lse[row] = mx + __log2f(tot) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -834,8 +922,16 @@ hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, int grid,
 
 hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, hipStream_t st) {
   void* args[] = {(void*)&a};
-  dim3 grid(rows * q_len_max * heads);
+  constexpr int kW = kBlockThreads / 64;
+  dim3 grid(rows * q_len_max * ((heads + kW - 1) / kW));
   return hipLaunchKernel((const void*)merge_kernel, grid, dim3(kBlockThreads), args, 0, st);
+}
+
+hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t st) {
+  void* args[] = {(void*)&a};
+  const int per = kBlockThreads / 64;
+  return hipLaunchKernel((const void*)shard_merge_kernel, dim3((a.rows + per - 1) / per),
+                         dim3(kBlockThreads), args, 0, st);
 }
 
 hipError_t launch_gather(const GatherArgs& a, bool kv_fp8, int splits, hipStream_t st) {

@@ -30,7 +30,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 8
+    assert len(syms) == 10
     handle = ctypes.CDLL(lib_mod.LIB_PATH)
     for s in syms:
         assert hasattr(handle, s), s
@@ -174,3 +174,30 @@ def test_cache_write_argument_errors(lib):
     assert c(slots_n=0) == INVALID
     assert c(kv_c=FAKE + 2, kv_c_dtype=2) == INVALID    # fp32 source not 4-byte aligned
     assert c(slots=FAKE + 4) == INVALID                  # int64 slots not 8-byte aligned
+
+
+def test_dcp_argument_errors(lib):
+    P = ctypes.POINTER(ctypes.c_int32)
+    plan = good_plan()
+
+    def d(world=8, rank=3, lens=FAKE, plan=plan):
+        p = np.ascontiguousarray(plan, np.int32)
+        return lib.mla_decode_fwd_dcp(FAKE, 0, None, FAKE, 0, None, 4096, FAKE, FAKE, FAKE,
+                                      p.ctypes.data_as(P), FAKE, ROWS, H, QLEN, 1, 0.1, FAKE, FAKE,
+                                      FAKE, 1 << 30, world, rank, lens, None)
+
+    assert d(world=0) == INVALID
+    assert d(world=65) == INVALID
+    assert d(rank=8) == INVALID
+    assert d(rank=-1) == INVALID
+    assert d(lens=None) == INVALID
+
+    def m(o_parts=FAKE, lse_parts=FAKE, world=4, tokens=3, heads=16, o=FAKE, lse=FAKE):
+        return lib.mla_merge_shards(o_parts, lse_parts, world, tokens, heads, o, lse, None)
+
+    assert m(tokens=0, o_parts=None) == OK
+    assert m(world=0) == INVALID
+    assert m(world=65) == INVALID
+    assert m(heads=129) == INVALID
+    assert m(o=None) == INVALID
+    assert m(o_parts=FAKE + 8) == INVALID
