@@ -173,9 +173,8 @@ def main():
 
     torch.cuda.set_device(0)
     mla.load_library()
-    from workloads import CONFIGS, config_lengths
-    fits = int(CONFIGS[args.workload]["pool_slots"] // max(int(config_lengths(args.workload).sum()), 1))
-    rotate = max(1, min(args.rotate, fits))
+    from workloads import index_set_capacity
+    rotate = max(1, min(args.rotate, index_set_capacity(args.workload)))
     case = make_config(args.workload, extra_index_sets=rotate - 1)
     index_sets = [case.kv_indices] + list(case.alt_kv_indices)
     dev = mla.device_inputs(case.q_codes, case.q_scale, case.pool_codes, case.kv_scale,

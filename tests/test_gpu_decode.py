@@ -72,6 +72,7 @@ CONFIG_SAMPLES = {
     "longctx_split": [0, 3],
     "ragged_persistent_causal": "extremes",
     "ragged_persistent_noncausal": "extremes",
+    "sparse_topk": [0, 17, 63],
 }
 
 

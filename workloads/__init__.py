@@ -159,8 +159,57 @@ def make_case(seed: int, kv_lens: Sequence[int] | None, heads: int, q_len: int,
                 alt_kv_indices=alts)
 
 
-# The five workloads. Each entry: (seed, lens or lens_fn, heads, q_len, q_dtype,
-# kv_dtype, causal, pool slots).
+def make_sparse_case(seed: int, rows: int, ctx: Sequence[int], window: int, topk: int, heads: int,
+                     q_len: int, q_dtype: str, kv_dtype: str, name: str = "sparse",
+                     extra_index_sets: int = 0) -> Case:
+    """Sparse (top-k) index lists over a row-dense pool: row b owns C_b
+    consecutive slots (its context, C_b drawn uniformly in [ctx[0], ctx[1]]);
+    its list is `topk` positions drawn without replacement from the first
+    C_b - window positions, ascending, followed by the last `window` positions
+    (a sliding window plus selected tokens, the DeepSeek-V4 CSA list of ATOM
+    pull request 2462, Summary part 1). Non-causal. Only listed slots get
+    values (the rest of the pool is zero and never read). Extra index sets
+    redraw the top-k part (benchmark rotation).
+
+    Draw order: contexts, top-k positions per row (and per extra set), values
+    of the listed slots, then Q."""
+    rng = np.random.default_rng(seed)
+    C = rng.integers(int(ctx[0]), int(ctx[1]) + 1, rows).astype(np.int64)
+    base = np.concatenate([[0], np.cumsum(C)[:-1]]).astype(np.int64)
+    pool_slots = int(C.sum())
+
+    def draw_lists():
+        out = []
+        for b in range(rows):
+            pre = int(C[b]) - window
+            sel = np.sort(rng.choice(pre, size=min(topk, pre), replace=False)) if pre > 0 else np.zeros(0, np.int64)
+            win = np.arange(max(pre, 0), int(C[b]), dtype=np.int64)
+            out.append(base[b] + np.concatenate([sel, win]))
+        return out
+
+    sets = [draw_lists() for _ in range(1 + extra_index_sets)]
+    lens = np.array([len(x) for x in sets[0]], dtype=np.int64)
+    used = np.unique(np.concatenate([np.concatenate(s) for s in sets]))
+    vals = rng.standard_normal((used.shape[0], D_LATENT), dtype=np.float32)
+    codes, kv_scale = _store(vals, kv_dtype)
+    del vals
+    pool_codes = np.zeros((pool_slots, D_LATENT), dtype=codes.dtype)
+    pool_codes[used] = codes
+    T = rows * q_len
+    q = rng.standard_normal((T, heads, D_LATENT), dtype=np.float32)
+    q_codes, q_scale = _store(q, q_dtype)
+    del q
+    qo_indptr = (np.arange(rows + 1) * q_len).astype(np.int32)
+    kv_indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    flat = [np.concatenate(s).astype(np.int32) for s in sets]
+    return Case(name=name, rows=rows, q_len=q_len, heads=heads, causal=False, q_dtype=q_dtype,
+                kv_dtype=kv_dtype, q_codes=q_codes, q_scale=q_scale, pool_codes=pool_codes,
+                kv_scale=kv_scale, qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=flat[0],
+                sm_scale=SM_SCALE, alt_kv_indices=flat[1:])
+
+
+# The workloads. Each entry: (seed, lens or lens_fn, heads, q_len, q_dtype,
+# kv_dtype, causal, pool slots); "sparse" entries use make_sparse_case.
 def _lens_c2(rng):
     return rng.integers(1024, 8193, 32)
 
@@ -188,12 +237,21 @@ CONFIGS = {
                                      kv_dtype=FP8, causal=True, pool_slots=1048576),
     "ragged_persistent_noncausal": dict(seed=5, lens_fn=_lens_c5, heads=128, q_len=2, q_dtype=BF16,
                                         kv_dtype=FP8, causal=False, pool_slots=1048576),
+    # 64 rows, q_len 2, 128 heads, bf16 Q, fp8 KV: top-k 2048 + window 128 of
+    # 8k..32k-token contexts (sparse index lists, non-causal)
+    "sparse_topk": dict(seed=6, sparse=dict(rows=64, ctx=(8192, 32768), window=128, topk=2048),
+                        heads=128, q_len=2, q_dtype=BF16, kv_dtype=FP8, causal=False, pool_slots=None),
 }
 
 
 def make_config(name: str, extra_index_sets: int = 0) -> Case:
     spec = dict(CONFIGS[name])
     seed = spec.pop("seed")
+    if "sparse" in spec:
+        sp = spec["sparse"]
+        return make_sparse_case(seed, sp["rows"], sp["ctx"], sp["window"], sp["topk"], spec["heads"],
+                                spec["q_len"], spec["q_dtype"], spec["kv_dtype"], name=name,
+                                extra_index_sets=extra_index_sets)
     lens = spec.pop("kv_lens", None)
     return make_case(seed, lens, name=name, extra_index_sets=extra_index_sets, **spec)
 
@@ -201,6 +259,21 @@ def make_config(name: str, extra_index_sets: int = 0) -> Case:
 def config_lengths(name: str) -> np.ndarray:
     """The config's KV lengths without generating the pool (same draw)."""
     spec = CONFIGS[name]
+    if "sparse" in spec:
+        sp = spec["sparse"]
+        C = np.random.default_rng(spec["seed"]).integers(sp["ctx"][0], sp["ctx"][1] + 1, sp["rows"])
+        return np.array([min(sp["topk"], max(int(c) - sp["window"], 0)) + min(sp["window"], int(c))
+                         for c in C], dtype=np.int64)
     if "kv_lens" in spec:
         return np.asarray(spec["kv_lens"], dtype=np.int64)
     return np.asarray(spec["lens_fn"](np.random.default_rng(spec["seed"])), dtype=np.int64)
+
+
+def index_set_capacity(name: str) -> int:
+    """How many index lists (the first plus alternates) the config can draw
+    for benchmark rotation: disjoint lists for the dense configs, redrawn
+    top-k lists for the sparse one."""
+    spec = CONFIGS[name]
+    if "sparse" in spec:
+        return 3
+    return max(1, int(spec["pool_slots"] // max(int(config_lengths(name).sum()), 1)))
