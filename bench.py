@@ -364,7 +364,7 @@ def bench_dcp(args):
     glob = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
     words = mla.plan(loc, H, 8, "bf16")
     plan_dev = torch.from_numpy(words).cuda()
-    ws = torch.empty(max(mla.workspace_size(words), 16), dtype=torch.uint8, device="cuda")
+    ws = mla.alloc_workspace(words)
     T = case.num_tokens
     o = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((T, H), dtype=torch.float32, device="cuda")

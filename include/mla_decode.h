@@ -83,6 +83,15 @@ typedef enum { MLA_BF16 = 0, MLA_FP8_E4M3 = 1 } mla_dtype;
  * UNIFORM. */
 typedef enum { MLA_PLAN_AUTO = 0, MLA_PLAN_UNIFORM = 1, MLA_PLAN_LENGTH_AWARE = 2 } mla_plan_mode;
 
+/* OR into the plan mode to have split rows (at most 16 splits) merged inside
+ * the decode kernel by the last of their splits to finish each 64-row tile,
+ * instead of by a second kernel: one launch instead of two. It costs an L2
+ * write-back per work item and an L2 invalidation per merged tile (the L2s
+ * of the MI355X's eight XCDs are not coherent with each other), and on the
+ * measured workloads it is slower than the second kernel; the plan records
+ * the request in its header mode word. */
+#define MLA_PLAN_MERGE_IN_KERNEL 0x100
+
 /* Upper bound on the int32 words mla_decode_plan can write for these sizes.
  * Host only; never fails for rows >= 1, heads in [1,128], q_len_max in [1,16],
  * num_cus >= 1. */
@@ -106,15 +115,35 @@ MLA_API int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t nu
                         int32_t q_len_max, mla_dtype kv_dtype, mla_plan_mode mode,
                         int32_t num_cus, int32_t* plan, int64_t plan_words);
 
-/* Workspace bytes mla_decode_fwd needs for this plan (0 when no row is
- * split): P * q_len_max * heads * (512 + 1) * 4 bytes of fp32 partials.
- * plan: host words from mla_decode_plan. Errors: INVALID_ARG, PLAN_MISMATCH
- * (bad magic or version). */
+/* Workspace bytes mla_decode_fwd needs for this plan: 0 when no row is
+ * split, else the fp32 partials, P * q_len_max * heads * (512 + 1) * 4 bytes,
+ * preceded for an MLA_PLAN_MERGE_IN_KERNEL plan by 256 KiB of split-arrival
+ * counters. plan: host words from mla_decode_plan. Errors: INVALID_ARG,
+ * PLAN_MISMATCH (bad magic or version). */
 MLA_API int32_t mla_decode_workspace_size(const int32_t* plan, int64_t* bytes_out);
+
+/* For an MLA_PLAN_MERGE_IN_KERNEL plan: zero the workspace's counter region
+ * (its first 256 KiB). Call once after allocating a workspace (or allocate it
+ * zeroed); every completed mla_decode_fwd leaves the region zero again, so
+ * one workspace serves any number of later calls and plans. Enqueued on
+ * `stream` as a kernel (no memset), so it may also be captured in a graph.
+ * Other plans need no initialization (nothing is launched). Errors:
+ * INVALID_ARG, PLAN_MISMATCH, WORKSPACE (too small for this plan), HIP. */
+MLA_API int32_t mla_decode_workspace_init(const int32_t* plan, void* workspace,
+                                          int64_t workspace_bytes, void* stream);
 
 /*
  * Enqueue the decode: one decode kernel over the plan's G workgroups, then,
- * if any row is split, one merge kernel. No host synchronization.
+ * if any row is split, one merge kernel (with an MLA_PLAN_MERGE_IN_KERNEL
+ * plan, rows with at most 16 splits are merged inside the decode kernel, the
+ * split-and-merge of the persistent kernel of ATOM pull request 2462,
+ * Dependencies, and the merge kernel only runs for rows with more). No host
+ * synchronization.
+ * A UNIFORM plan takes each split's key range from the live lengths
+ * (split k of n covers [k L / n, (k + 1) L / n) of L = kv_indptr[b+1] -
+ * kv_indptr[b]), so a plan built once stays valid when the lengths change:
+ * a call captured in a graph can be replayed after the index lists are
+ * updated in place (rows, q_len_max and the plan words fixed).
  *   q          device, [qo_indptr[rows], num_heads, 576] of q_dtype, 16-byte aligned
  *   q_scale    device float scalar, or NULL for 1.0 (fp8 Q needs its scale)
  *   kv_pool    device, [num_slots, 576] of kv_dtype, 16-byte aligned
@@ -127,7 +156,9 @@ MLA_API int32_t mla_decode_workspace_size(const int32_t* plan, int64_t* bytes_ou
  *   o          device bf16 [qo_indptr[rows], num_heads, 512], 16-byte aligned
  *   lse        device fp32 [qo_indptr[rows], num_heads]
  *   workspace  device, >= mla_decode_workspace_size bytes, 16-byte aligned
- *              (may be NULL when that size is 0); contents are scratch
+ *              (may be NULL when that size is 0), its counter region zero
+ *              (mla_decode_workspace_init); the rest is scratch. Calls that
+ *              overlap on one workspace race
  *   stream     hipStream_t (NULL = the default stream)
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, PLAN_MISMATCH (plan header
  * differs from rows / num_heads / q_len_max / kv_dtype, or a plan from a

@@ -41,7 +41,8 @@ Steps:
    that chiplet's workgroup with the least (load, id), load being the sum of
    its item costs; a workgroup runs its items in the order they came.
 9. Words (int32): a 20-word header [magic 0x4D4C4150, version 1, R, H,
-   q_len_max, kv_dtype, C, mode_used, M_UNIT, u, N_MAX, MIN_SPLIT_KEYS,
+   q_len_max, kv_dtype, C, mode_used (| 0x100 when the caller asked for the
+   merge inside the decode kernel), M_UNIT, u, N_MAX, MIN_SPLIT_KEYS,
    ITEM_OVERHEAD, OCC, S, W, G, P, 20, total words], then split_indptr[R+1],
    split_row[S], split_begin[S], split_end[S], split_part[S],
    work_indptr[G+1], item_split[W], item_m[W].
@@ -59,6 +60,9 @@ OCC = 2
 XCDS = 8
 
 MODE_AUTO, MODE_UNIFORM, MODE_LENGTH_AWARE = 0, 1, 2
+# Bit 8 of the mode: the caller asks for the split merge inside the decode
+# kernel. It is recorded in the header's mode word and changes nothing else.
+MERGE_IN_KERNEL = 0x100
 KV_BF16, KV_FP8 = 0, 1
 
 
@@ -89,7 +93,8 @@ def plan_ref(kv_lens, H, q_len_max, kv_dtype, mode, C):
 
     # 1-2
     u = cdiv(H * q_len_max, M_UNIT)
-    mode_used = choose_mode(mode, kv_dtype, H, R)
+    flag = mode & MERGE_IN_KERNEL
+    mode_used = choose_mode(mode & ~MERGE_IN_KERNEL, kv_dtype, H, R)
 
     # 3-4: split count per row
     if mode_used == MODE_UNIFORM:
@@ -168,7 +173,7 @@ def plan_ref(kv_lens, H, q_len_max, kv_dtype, mode, C):
         work_indptr.append(len(item_split))
 
     total = HEADER_WORDS + (R + 1) + 4 * S + (G + 1) + 2 * W
-    header = [MAGIC, VERSION, R, H, q_len_max, kv_dtype, C, mode_used, M_UNIT, u,
+    header = [MAGIC, VERSION, R, H, q_len_max, kv_dtype, C, mode_used | flag, M_UNIT, u,
               N_MAX, MIN_SPLIT_KEYS, ITEM_OVERHEAD, OCC, S, W, G, P, HEADER_WORDS, total]
     words = (header + split_indptr + split_row + split_begin + split_end + split_part
              + work_indptr + item_split + item_m)

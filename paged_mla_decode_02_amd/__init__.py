@@ -56,6 +56,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_decode_plan.restype = i32
     lib.mla_decode_workspace_size.argtypes = [p32, ctypes.POINTER(i64)]
     lib.mla_decode_workspace_size.restype = i32
+    lib.mla_decode_workspace_init.argtypes = [p32, vp, i64, vp]
+    lib.mla_decode_workspace_init.restype = i32
     lib.mla_decode_fwd.argtypes = [vp, i32, vp, vp, i32, vp, i64, vp, vp, vp, p32, vp, i32, i32,
                                    i32, i32, ctypes.c_float, vp, vp, vp, i64, vp]
     lib.mla_decode_fwd.restype = i32
@@ -122,6 +124,23 @@ def workspace_size(plan_words: np.ndarray) -> int:
     _check(load_library().mla_decode_workspace_size(w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                                    ctypes.byref(n)))
     return n.value
+
+
+PLAN_MERGE_IN_KERNEL = 0x100
+
+
+def workspace_init(plan_words: np.ndarray, workspace, stream=None):
+    """Enqueue mla_decode_workspace_init (zero the split counters)."""
+    w = _host_i32(plan_words)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().mla_decode_workspace_init(w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                                    _ptr(workspace), nbytes, _stream_handle(stream)))
+
+
+def alloc_workspace(plan_words: np.ndarray, device="cuda", min_bytes: int = 16):
+    """A zeroed workspace tensor (uint8) for this plan, ready for decode_fwd."""
+    import torch
+    return torch.zeros(max(workspace_size(plan_words), min_bytes), dtype=torch.uint8, device=device)
 
 
 def _ptr(t) -> Optional[int]:
@@ -267,7 +286,8 @@ class MlaDecoder:
         if nbytes == 0:
             return None
         if self._ws is None or self._ws.numel() < nbytes:
-            self._ws = self.torch.empty(nbytes, dtype=self.torch.uint8, device=self.device)
+            # zeroed: the counter region must start at zero; calls keep it so
+            self._ws = self.torch.zeros(nbytes, dtype=self.torch.uint8, device=self.device)
         return self._ws
 
     def run(self, inputs: dict, kv_lens, o, lse, words: Optional[np.ndarray] = None):

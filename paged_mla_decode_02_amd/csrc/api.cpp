@@ -66,7 +66,7 @@ int32_t decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale, cons
   PlanView v;
   int32_t st = check_plan_for_call(plan_host, plan_dev, rows, num_heads, q_len_max, kv_dtype, &v);
   if (st != MLA_OK) return st;
-  const int64_t need = (int64_t)v.P * q_len_max * num_heads * (MLA_D_V + 1) * 4;
+  const int64_t need = mla::workspace_bytes(v);
   if (need > 0) {
     if (!workspace) return set_error(MLA_ERR_WORKSPACE, "this plan needs a workspace");
     if (workspace_bytes < need)
@@ -103,13 +103,24 @@ int32_t decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale, cons
   a.o = (uint16_t*)o;
   a.lse = lse;
   const int64_t ws_o_elems = (int64_t)v.P * q_len_max * num_heads * MLA_D_V;
-  a.ws_o = need > 0 ? (float*)workspace : nullptr;
-  a.ws_lse = need > 0 ? (float*)workspace + ws_o_elems : nullptr;
+  float* partials = need > 0 ? (float*)((char*)workspace + workspace_counter_bytes(v)) : nullptr;
+  a.ws_o = partials;
+  a.ws_lse = need > 0 ? partials + ws_o_elems : nullptr;
+  a.counters = need > 0 ? (int32_t*)workspace : nullptr;
+  a.off_split_indptr = (int32_t)v.off_split_indptr;
+  a.u = v.u;
+  // split rows with up to kMaxInKernelSplits splits merge inside the decode
+  // kernel when every (row, M tile) has a counter
+  a.inkernel_max_splits =
+      (need > 0 && v.merge_in_kernel && (int64_t)rows * v.u <= kWsCounters) ? kMaxInKernelSplits : 1;
+  // a UNIFORM plan's split ranges follow from the live lengths (k L / n), so
+  // such a plan stays valid when the lengths change (graph replay)
+  a.uniform_ranges = v.mode == MLA_PLAN_UNIFORM;
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_decode(a, q_dtype == MLA_FP8_E4M3, kv_dtype == MLA_FP8_E4M3, v.G, s);
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
-  if (v.P > 0) {
+  if (v.P > 0 && v.max_splits > a.inkernel_max_splits) {
     MergeArgs mg;
     mg.qo_indptr = qo_indptr;
     mg.plan = plan_dev;
@@ -119,6 +130,7 @@ int32_t decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale, cons
     mg.q_len_max = q_len_max;
     mg.ws_o = a.ws_o;
     mg.ws_lse = a.ws_lse;
+    mg.skip_upto = a.inkernel_max_splits;
     mg.o = a.o;
     mg.lse = lse;
     e = launch_merge(mg, rows, num_heads, q_len_max, s);
@@ -212,6 +224,8 @@ extern "C" int32_t mla_debug_gather(const void* kv_pool, mla_dtype kv_dtype, int
   g.off_split_row = (int32_t)v.off_split_row;
   g.off_split_begin = (int32_t)v.off_split_begin;
   g.off_split_end = (int32_t)v.off_split_end;
+  g.off_split_indptr = (int32_t)v.off_split_indptr;
+  g.uniform_ranges = v.mode == MLA_PLAN_UNIFORM;
   g.dense = (uint16_t*)dense_out;
   hipError_t e = launch_gather(g, kv_dtype == MLA_FP8_E4M3, v.S, (hipStream_t)stream);
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("gather launch: ") + hipGetErrorString(e));
@@ -257,5 +271,22 @@ extern "C" int32_t mla_cache_write(const void* kv_c, mla_src_dtype kv_c_dtype, i
                    (k_pe_stride * src_size(k_pe_dtype)) % 16 == 0;
   hipError_t e = launch_cache_write(a, vec, (hipStream_t)stream);
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("cache write launch: ") + hipGetErrorString(e));
+  return MLA_OK;
+}
+
+extern "C" int32_t mla_decode_workspace_init(const int32_t* plan_host, void* workspace,
+                                             int64_t workspace_bytes_, void* stream) {
+  clear_error();
+  PlanView v;
+  int32_t st = view_plan(plan_host, &v);
+  if (st != MLA_OK) return st;
+  const int64_t need = mla::workspace_bytes(v);
+  if (need == 0 || !v.merge_in_kernel) return MLA_OK;   // no counters to zero
+  if (!workspace) return set_error(MLA_ERR_WORKSPACE, "this plan needs a workspace");
+  if (workspace_bytes_ < need)
+    return set_error(MLA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  if (!aligned16(workspace)) return set_error(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  hipError_t e = launch_zero((uint32_t*)workspace, kWsCounters, (hipStream_t)stream);
+  if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("workspace init launch: ") + hipGetErrorString(e));
   return MLA_OK;
 }

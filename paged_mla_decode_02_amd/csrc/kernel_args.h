@@ -23,6 +23,10 @@ struct DecodeArgs {
   int32_t heads, q_len_max, causal;
   float score_scale_log2;   // softmax_scale * log2(e)
   int32_t dcp_world, dcp_rank;      // round-robin KV shard: local key j at position j * world + rank
+  int32_t* counters;        // [rows * u] split arrivals per (row, M tile); zero between calls
+  int32_t off_split_indptr, u;
+  int32_t inkernel_max_splits;   // rows with 1 < n <= this many splits merge in the decode kernel
+  int32_t uniform_ranges;   // split k of n covers [k L / n, (k + 1) L / n) of the live length L
   const int32_t* kv_len_global;     // [rows] keys of each row over all shards, or null (= local)
   uint16_t* o;              // bf16 bits
   float* lse;
@@ -39,6 +43,7 @@ struct MergeArgs {
   const float* ws_lse;
   uint16_t* o;
   float* lse;
+  int32_t skip_upto;        // rows with at most this many splits were merged in the decode kernel
 };
 
 struct GatherArgs {
@@ -46,7 +51,8 @@ struct GatherArgs {
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
   const int32_t* plan;
-  int32_t off_split_row, off_split_begin, off_split_end;
+  int32_t off_split_row, off_split_begin, off_split_end, off_split_indptr;
+  int32_t uniform_ranges;
   uint16_t* dense;          // bf16 [nnz, 576]
 };
 
@@ -77,6 +83,7 @@ hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, int grid,
 hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, bool kv_fp8, int splits, hipStream_t st);
 hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t st);
+hipError_t launch_zero(uint32_t* p, int32_t words, hipStream_t st);
 // vec: every source row and the pool are 16-byte aligned (8-element chunks).
 hipError_t launch_cache_write(const CacheWriteArgs& a, bool vec, hipStream_t st);
 

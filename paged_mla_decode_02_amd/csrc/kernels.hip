@@ -101,7 +101,9 @@ constexpr int kOffAlpha = kOffP + 2 * kRowBlocks * 64 * 16;   // [2][64] f32 res
 constexpr int kOffFlags = kOffAlpha + 2 * 64 * 4;     // [2][4] u32 "any rescale" per QK wave
 constexpr int kOffL = kOffFlags + 2 * 16;             // [64] f32 row sums (epilogue)
 constexpr int kOffSlots = kOffL + 64 * 4;             // [8 waves][4][32] int32
-constexpr int kSmemBytes = kOffSlots + kWaves * kSlotRing * kNT * 4;   // 160544
+constexpr int kOffMisc = kOffSlots + kWaves * kSlotRing * kNT * 4;     // [4] u32 (merge flag)
+constexpr int kSmemBytes = kOffMisc + 16;                                // 160560
+constexpr int kMaxInKernelSplits = 16;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
@@ -498,7 +500,61 @@ __device__ __forceinline__ void step_sync(lds_u8* smem, int t, int ntiles, int t
   }
 }
 
-template <bool Q_FP8, bool KV_FP8>
+// In-kernel merge of one (row b, M tile m): rows m 64 .. m 64 + 63 of the
+// row's block, n <= kMaxInKernelSplits fp32 partials each (consecutive
+// partial slots from part0). Thread tid takes 8 (row, 8-column chunk) pairs.
+__device__ __forceinline__ void merge_tile(const DecodeArgs& a, int b, int m, int M, int n, int part0,
+                                           int q0, int tid) {
+  const int H = a.heads;
+  const int64_t stride = (int64_t)a.q_len_max * H;   // between consecutive partial slots
+  const float kLog2e = 1.44269504088896340736f;
+  for (int i = 0; i < 64 * 64 / kDecodeThreads; ++i) {
+    const int pair = tid + i * kDecodeThreads;
+    const int rr = pair >> 6, c = pair & 63;
+    const int r = m * 64 + rr;
+    if (r >= M) continue;
+    const int tok = r / H, h = r - tok * H;
+    const int64_t base = ((int64_t)part0 * a.q_len_max + tok) * H + h;
+    const int64_t orow = (int64_t)(q0 + tok) * H + h;
+    float lk[kMaxInKernelSplits];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMaxInKernelSplits; ++k) {
+      lk[k] = k < n ? a.ws_lse[base + k * stride] : -INFINITY;
+      mx = fmaxf(mx, lk[k]);
+    }
+    uint16_t* dst = a.o + orow * kDV + c * 8;
+    if (mx == -INFINITY) {   // no split sees a key
+      *(u32x4*)dst = u32x4{0u, 0u, 0u, 0u};
+      if (c == 0) a.lse[orow] = -INFINITY;
+      continue;
+    }
+    float tot = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxInKernelSplits; ++k) {
+      lk[k] = lk[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lk[k] - mx) * kLog2e);
+      tot += lk[k];
+    }
+    const float inv = 1.0f / tot;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kMaxInKernelSplits; ++k) {
+      if (k < n) {
+        const f32x4* src = (const f32x4*)(a.ws_o + (base + k * stride) * kDV + c * 8);
+        const float wk = lk[k] * inv;   // an empty split's partial is 0 and its weight 0
+        acc0 += wk * src[0];
+        acc1 += wk * src[1];
+      }
+    }
+    *(bf16x8*)dst = bf16x8{(__bf16)acc0[0], (__bf16)acc0[1], (__bf16)acc0[2], (__bf16)acc0[3],
+                           (__bf16)acc1[0], (__bf16)acc1[1], (__bf16)acc1[2], (__bf16)acc1[3]};
+    if (c == 0) a.lse[orow] = mx + __log2f(tot) * kLn2;
+  }
+}
+
+// MERGE: the variant for in-kernel-merge plans (the default variant carries
+// none of that code, which would cost the hot loops registers).
+template <bool Q_FP8, bool KV_FP8, bool MERGE>
 __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmemBytes];
   lds_u8* smem = (lds_u8*)smem_raw;
@@ -520,11 +576,19 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     const int s = a.plan[a.off_item_split + it];
     const int m = a.plan[a.off_item_m + it];
     const int b = a.plan[a.off_split_row + s];
-    const int begin = a.plan[a.off_split_begin + s];
-    const int end = a.plan[a.off_split_end + s];
     const int part = a.plan[a.off_split_part + s];
     const int q0 = a.qo_indptr[b], q_b = a.qo_indptr[b + 1] - q0;
     const int kv0 = a.kv_indptr[b], L = a.kv_indptr[b + 1] - kv0;
+    const int s0 = a.plan[a.off_split_indptr + b];
+    const int nsplit = a.plan[a.off_split_indptr + b + 1] - s0;
+    int begin, end;
+    if (a.uniform_ranges) {   // split k of n covers [k L / n, (k + 1) L / n) of the live length
+      begin = (int)((int64_t)(s - s0) * L / nsplit);
+      end = (int)((int64_t)(s - s0 + 1) * L / nsplit);
+    } else {
+      begin = a.plan[a.off_split_begin + s];
+      end = a.plan[a.off_split_end + s];
+    }
     const int M = q_b * H;
     if (m * 64 >= M) continue;   // no query row in this tile (ragged block); uniform
     const int ntiles = (end - begin + kNT - 1) / kNT;
@@ -690,6 +754,30 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       }
     }
     __syncthreads();   // LDS is reused by the next item
+
+    // A split row with few splits is merged here by the last of its splits
+    // to finish this M tile: every thread releases its partial stores, one
+    // counts the arrival, and the last arrival reads the other splits'
+    // partials after an acquire and writes the tile's O and LSE, then
+    // re-zeroes the counter for the next call.
+    if (MERGE && part >= 0 && nsplit <= a.inkernel_max_splits) {
+      wait_vm_all();     // this thread's partial stores have reached L2
+      __syncthreads();
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // one L2 write-back for the block
+        const int old = __hip_atomic_fetch_add(a.counters + b * a.u + m, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        lds_store(smem, kOffMisc, (uint32_t)(old == nsplit - 1));
+      }
+      __syncthreads();
+      if (lds_load<uint32_t>(smem, kOffMisc) != 0u) {   // uniform
+        if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // invalidates for the block
+        __syncthreads();
+        merge_tile(a, b, m, M, nsplit, a.plan[a.off_split_part + s0], q0, tid);
+        if (tid == 0) a.counters[b * a.u + m] = 0;
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -753,7 +841,7 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
   const int i = bi - b * a.q_len_max;
   const int s0 = a.plan[a.off_split_indptr + b];
   const int n = a.plan[a.off_split_indptr + b + 1] - s0;
-  if (n <= 1) return;
+  if (n <= a.skip_upto) return;   // unsplit, or merged in the decode kernel
   const int q0 = a.qo_indptr[b];
   if (i >= a.qo_indptr[b + 1] - q0) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -869,6 +957,13 @@ __global__ __launch_bounds__(kBlockThreads) void shard_merge_kernel(ShardMergeAr
   if (lane == 0) a.lse[row] = mx + __log2f(tot) * kLn2;
 }
 
+// Fills a buffer with zeros (the workspace's split counters); a kernel, not a
+// memset, so that it may sit in a captured graph.
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int32_t words) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < words) p[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------
 // Gather test hook: one block per split; every tile goes through the decode
 // kernel's loader (and fp8 conversion) into tile 0, then is copied out of LDS
@@ -882,8 +977,15 @@ __global__ __launch_bounds__(kDecodeThreads) void gather_kernel(GatherArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = blockIdx.x;
   const int b = a.plan[a.off_split_row + s];
-  const int begin = a.plan[a.off_split_begin + s], end = a.plan[a.off_split_end + s];
   const int kv0 = a.kv_indptr[b];
+  int begin = a.plan[a.off_split_begin + s], end = a.plan[a.off_split_end + s];
+  if (a.uniform_ranges) {   // same ranges as the decode kernel
+    const int s0 = a.plan[a.off_split_indptr + b];
+    const int n = a.plan[a.off_split_indptr + b + 1] - s0;
+    const int L = a.kv_indptr[b + 1] - kv0;
+    begin = (int)((int64_t)(s - s0) * L / n);
+    end = (int)((int64_t)(s - s0 + 1) * L / n);
+  }
   const int64_t dense0 = (int64_t)(kv0 - a.kv_indptr[0]);
   const unsigned char* kv = (const unsigned char*)a.kv;
   for (int key0 = begin; key0 < end; key0 += kNT) {
@@ -910,13 +1012,17 @@ __global__ __launch_bounds__(kDecodeThreads) void gather_kernel(GatherArgs a) {
 
 }  // namespace
 
+template <bool MERGE>
+const void* decode_fn(bool q_fp8, bool kv_fp8) {
+  if (!q_fp8 && !kv_fp8) return (const void*)decode_kernel<false, false, MERGE>;
+  if (!q_fp8 && kv_fp8) return (const void*)decode_kernel<false, true, MERGE>;
+  if (q_fp8 && !kv_fp8) return (const void*)decode_kernel<true, false, MERGE>;
+  return (const void*)decode_kernel<true, true, MERGE>;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, int grid, hipStream_t st) {
   void* args[] = {(void*)&a};
-  const void* fn;
-  if (!q_fp8 && !kv_fp8) fn = (const void*)decode_kernel<false, false>;
-  else if (!q_fp8 && kv_fp8) fn = (const void*)decode_kernel<false, true>;
-  else if (q_fp8 && !kv_fp8) fn = (const void*)decode_kernel<true, false>;
-  else fn = (const void*)decode_kernel<true, true>;
+  const void* fn = a.inkernel_max_splits > 1 ? decode_fn<true>(q_fp8, kv_fp8) : decode_fn<false>(q_fp8, kv_fp8);
   return hipLaunchKernel(fn, dim3(grid), dim3(kDecodeThreads), args, 0, st);
 }
 
@@ -925,6 +1031,11 @@ hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, 
   constexpr int kW = kBlockThreads / 64;
   dim3 grid(rows * q_len_max * ((heads + kW - 1) / kW));
   return hipLaunchKernel((const void*)merge_kernel, grid, dim3(kBlockThreads), args, 0, st);
+}
+
+hipError_t launch_zero(uint32_t* p, int32_t words, hipStream_t st) {
+  void* args[] = {(void*)&p, (void*)&words};
+  return hipLaunchKernel((const void*)zero_kernel, dim3((words + 255) / 256), dim3(256), args, 0, st);
 }
 
 hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t st) {

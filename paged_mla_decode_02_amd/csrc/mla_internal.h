@@ -21,6 +21,16 @@ constexpr int32_t kItemOverhead = 64;
 constexpr int32_t kOcc = 2;
 constexpr int32_t kXcds = 8;
 
+// Workspace layout: the fp32 partial O and LSE of the split rows; with an
+// in-kernel-merge plan, a fixed region of split-arrival counters (one per
+// request row and M tile, zero between calls) comes first. With such a plan,
+// rows with at most kMaxInKernelSplits splits are merged inside the decode
+// kernel by the last of their splits to finish; rows with more (and every
+// split row when rows * u exceeds the counters) go to the merge kernel.
+constexpr int64_t kWsCounterBytes = 256 * 1024;
+constexpr int32_t kWsCounters = (int32_t)(kWsCounterBytes / 4);
+constexpr int32_t kMaxInKernelSplits = 16;
+
 enum HeaderField : int {
   H_MAGIC = 0, H_VERSION, H_ROWS, H_HEADS, H_QLEN, H_KVDTYPE, H_CUS, H_MODE, H_MUNIT, H_U,
   H_NMAX, H_MINSPLIT, H_OVERHEAD, H_OCC, H_S, H_W, H_G, H_P, H_HWORDS, H_TOTAL
@@ -29,12 +39,21 @@ enum HeaderField : int {
 // Offsets (in words) of the plan's arrays, from its header.
 struct PlanView {
   int32_t rows, heads, q_len_max, kv_dtype, mode, m_unit, u, S, W, G, P, total;
+  int32_t max_splits;   // largest split count of a row
+  bool merge_in_kernel; // the caller asked for the split merge inside the decode kernel
   int64_t off_split_indptr, off_split_row, off_split_begin, off_split_end, off_split_part,
       off_work_indptr, off_item_split, off_item_m;
 };
 
 // Parses and checks a plan header; returns MLA_OK or an error (message set).
 int32_t view_plan(const int32_t* plan, PlanView* v);
+
+// Workspace bytes a plan needs (0 when no row is split).
+inline int64_t workspace_counter_bytes(const PlanView& v) { return v.merge_in_kernel ? kWsCounterBytes : 0; }
+inline int64_t workspace_bytes(const PlanView& v) {
+  if (v.P == 0) return 0;
+  return workspace_counter_bytes(v) + (int64_t)v.P * v.q_len_max * v.heads * (MLA_D_V + 1) * 4;
+}
 
 int32_t set_error(int32_t status, const std::string& msg);
 void clear_error();

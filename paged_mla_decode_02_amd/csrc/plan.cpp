@@ -43,7 +43,8 @@ int32_t view_plan(const int32_t* plan, PlanView* v) {
   v->heads = plan[H_HEADS];
   v->q_len_max = plan[H_QLEN];
   v->kv_dtype = plan[H_KVDTYPE];
-  v->mode = plan[H_MODE];
+  v->mode = plan[H_MODE] & ~MLA_PLAN_MERGE_IN_KERNEL;
+  v->merge_in_kernel = (plan[H_MODE] & MLA_PLAN_MERGE_IN_KERNEL) != 0;
   v->m_unit = plan[H_MUNIT];
   v->u = plan[H_U];
   v->S = plan[H_S];
@@ -69,10 +70,12 @@ int32_t view_plan(const int32_t* plan, PlanView* v) {
   if (plan[H_NMAX] != kNMax || plan[v->off_split_indptr] != 0 ||
       plan[v->off_split_indptr + v->rows] != v->S)
     return set_error(MLA_ERR_PLAN_MISMATCH, "plan split_indptr is inconsistent");
+  v->max_splits = 0;
   for (int32_t b = 0; b < v->rows; ++b) {
     const int32_t n = plan[v->off_split_indptr + b + 1] - plan[v->off_split_indptr + b];
     if (n < 1 || n > kNMax)
       return set_error(MLA_ERR_PLAN_MISMATCH, "plan has a row with no split or more than 64");
+    v->max_splits = n > v->max_splits ? n : v->max_splits;
   }
   return MLA_OK;
 }
@@ -108,7 +111,9 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
     return set_error(MLA_ERR_UNSUPPORTED, "q_len_max must be in 1..16");
   if (kv_dtype != MLA_BF16 && kv_dtype != MLA_FP8_E4M3)
     return set_error(MLA_ERR_INVALID_ARG, "unknown kv_dtype");
-  if (mode != MLA_PLAN_AUTO && mode != MLA_PLAN_UNIFORM && mode != MLA_PLAN_LENGTH_AWARE)
+  const int32_t flag = (int32_t)mode & MLA_PLAN_MERGE_IN_KERNEL;
+  const int32_t base_mode = (int32_t)mode & ~MLA_PLAN_MERGE_IN_KERNEL;
+  if (base_mode != MLA_PLAN_AUTO && base_mode != MLA_PLAN_UNIFORM && base_mode != MLA_PLAN_LENGTH_AWARE)
     return set_error(MLA_ERR_INVALID_ARG, "unknown plan mode");
   if (num_cus < 1) return set_error(MLA_ERR_INVALID_ARG, "num_cus must be >= 1");
 
@@ -121,7 +126,7 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
   if (sum_len > INT32_MAX) return set_error(MLA_ERR_UNSUPPORTED, "total KV length exceeds int32");
 
   const int64_t u = cdiv((int64_t)num_heads * q_len_max, kMUnit);
-  int32_t used = mode;
+  int32_t used = base_mode;
   if (used == MLA_PLAN_AUTO)
     used = (kv_dtype == MLA_FP8_E4M3 && num_heads == 128 && rows >= 15 && rows <= 32768)
                ? MLA_PLAN_LENGTH_AWARE
@@ -209,7 +214,7 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
   if (total > plan_words) return set_error(MLA_ERR_INVALID_ARG, "plan buffer too small");
   int32_t* w = plan;
   const int32_t header[kHeaderWords] = {kPlanMagic, kPlanVersion, rows, num_heads, q_len_max,
-                                        (int32_t)kv_dtype, num_cus, used, kMUnit, (int32_t)u,
+                                        (int32_t)kv_dtype, num_cus, used | flag, kMUnit, (int32_t)u,
                                         kNMax, kMinSplitKeys, kItemOverhead, kOcc, S, W, G, P,
                                         kHeaderWords, (int32_t)total};
   std::memcpy(w, header, sizeof(header));
@@ -232,6 +237,6 @@ extern "C" int32_t mla_decode_workspace_size(const int32_t* plan, int64_t* bytes
   PlanView v;
   int32_t st = view_plan(plan, &v);
   if (st != MLA_OK) return st;
-  *bytes_out = (int64_t)v.P * v.q_len_max * v.heads * (MLA_D_V + 1) * 4;
+  *bytes_out = workspace_bytes(v);
   return MLA_OK;
 }

@@ -30,7 +30,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 10
+    assert len(syms) == 11
     handle = ctypes.CDLL(lib_mod.LIB_PATH)
     for s in syms:
         assert hasattr(handle, s), s
@@ -135,6 +135,9 @@ def test_plan_argument_errors(lib):
 def test_workspace_size_formula(lib):
     w = lib_mod.plan([1000, 300, 5000, 0], 128, 1, 1, lib_mod.PLAN_LENGTH_AWARE, 4)
     assert lib_mod.workspace_size(w) == 4 * 1 * 128 * 513 * 4      # P = 4 partial slots
+    w = lib_mod.plan([1000, 300, 5000, 0], 128, 1, 1,
+                     lib_mod.PLAN_LENGTH_AWARE | lib_mod.PLAN_MERGE_IN_KERNEL, 4)
+    assert lib_mod.workspace_size(w) == 256 * 1024 + 4 * 1 * 128 * 513 * 4   # + split counters
     w = lib_mod.plan([100, 200], 16, 1, 0, lib_mod.PLAN_UNIFORM, 1)  # one split per row
     assert lib_mod.workspace_size(w) == 0
 
@@ -201,3 +204,17 @@ def test_dcp_argument_errors(lib):
     assert m(heads=129) == INVALID
     assert m(o=None) == INVALID
     assert m(o_parts=FAKE + 8) == INVALID
+
+
+def test_workspace_init_errors(lib):
+    P = ctypes.POINTER(ctypes.c_int32)
+    split = np.ascontiguousarray(lib_mod.plan([1000, 300, 5000, 0], 128, 1, 1,
+                                              lib_mod.PLAN_LENGTH_AWARE | lib_mod.PLAN_MERGE_IN_KERNEL, 4), np.int32)
+    unsplit = np.ascontiguousarray(lib_mod.plan([100, 200], 16, 1, 0, lib_mod.PLAN_UNIFORM, 1), np.int32)
+    need = lib_mod.workspace_size(split)
+    assert lib.mla_decode_workspace_init(unsplit.ctypes.data_as(P), None, 0, None) == OK   # nothing to do
+    assert lib.mla_decode_workspace_init(split.ctypes.data_as(P), None, need, None) == WORKSPACE
+    assert lib.mla_decode_workspace_init(split.ctypes.data_as(P), FAKE, need - 1, None) == WORKSPACE
+    assert lib.mla_decode_workspace_init(split.ctypes.data_as(P), FAKE + 4, need, None) == INVALID
+    bad = split.copy(); bad[0] ^= 1
+    assert lib.mla_decode_workspace_init(bad.ctypes.data_as(P), FAKE, need, None) == MISMATCH

@@ -130,7 +130,7 @@ def test_cache_write_then_decode(mla):
     o = torch.full((T, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
     plan_dev = torch.from_numpy(words).cuda()
-    ws = torch.empty(max(mla.workspace_size(words), 16), dtype=torch.uint8, device="cuda")
+    ws = mla.alloc_workspace(words)
     mla.decode_fwd(dev["q"], "bf16", None, dev["kv_pool"], "fp8", dev["kv_scale"], dev["qo_indptr"],
                    dev["kv_indptr"], dev["kv_indices"], words, plan_dev, 1, H, 1, True,
                    float(np.float32(1 / np.sqrt(192))), o, lse, ws)

@@ -41,7 +41,7 @@ def _run_shard(mla, case, world, rank, dev, o, lse):
     flat, indptr, lens = _shard_lists(case, world, rank)
     words = mla.plan(lens, case.heads, case.q_len, case.kv_dtype)
     plan_dev = torch.from_numpy(words).cuda()
-    ws = torch.empty(max(mla.workspace_size(words), 16), dtype=torch.uint8, device="cuda")
+    ws = mla.alloc_workspace(words)
     glob = torch.from_numpy(np.asarray(case.kv_lens, np.int32)).cuda()
     mla.decode_fwd_dcp(dev["q"], case.q_dtype, dev["q_scale"], dev["kv_pool"], case.kv_dtype,
                        dev["kv_scale"], dev["qo_indptr"], torch.from_numpy(indptr).cuda(),

@@ -44,7 +44,7 @@ def test_random_plans_match_oracle():
         H = int(rng.choice([1, 7, 16, 32, 64, 96, 128, int(rng.integers(1, 129))]))
         q = int(rng.integers(1, 17))
         C = int(rng.choice([1, 3, 8, 20, 64, 256, 304]))
-        mode = int(rng.integers(0, 3))
+        mode = int(rng.integers(0, 3)) | (0x100 if rng.random() < 0.25 else 0)   # in-kernel merge flag
         kv = int(rng.integers(0, 2))
         _same([int(x) for x in lens], H, q, kv, mode, C)
 
