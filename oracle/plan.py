@@ -10,9 +10,10 @@ and 15 <= rows <= 32768. The constants and tie-breaks below are this
 library's own choice (spec version 1); the library's C++ planner must produce
 the same int32 words.
 
-Constants: M_UNIT 64 query rows per work item, N_MAX 64 splits per row,
-MIN_SPLIT_KEYS 256, ITEM_OVERHEAD 64, OCC 2 resident work items per compute
-unit, XCDS 8 (the chiplets whose L2 a launch spreads over).
+Constants: M_UNIT 128 query rows per work item, N_MAX 64 splits per row,
+MIN_SPLIT_KEYS 256, ITEM_OVERHEAD 64, OCC 1 resident work item per compute
+unit (a decode workgroup takes nearly all of a CU's LDS), XCDS 8 (the
+chiplets whose L2 a launch spreads over).
 All arithmetic is integer; cdiv(a, b) = (a + b - 1) // b.
 
 Steps:
@@ -52,11 +53,11 @@ import numpy as np
 MAGIC = 0x4D4C4150
 VERSION = 1
 HEADER_WORDS = 20
-M_UNIT = 64
+M_UNIT = 128
 N_MAX = 64
 MIN_SPLIT_KEYS = 256
 ITEM_OVERHEAD = 64
-OCC = 2
+OCC = 1
 XCDS = 8
 
 MODE_AUTO, MODE_UNIFORM, MODE_LENGTH_AWARE = 0, 1, 2

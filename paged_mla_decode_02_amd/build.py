@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
-SOURCES = ["plan.cpp", "error.cpp", "api.cpp", "kernels.hip", "cache_write.hip"]
+SOURCES = ["plan.cpp", "error.cpp", "api.cpp", "decode.hip", "kernels.hip", "cache_write.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are turned off for all device code (the compiler would
@@ -54,6 +54,10 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         cmd = [cc] + lang + common + DEVICE_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
         objs.append(obj)
         procs.append(cmd)
+    # the decode kernel's device assembly, for the QK-chain check below
+    asm = os.path.join(OBJDIR, "decode.gfx950.s")
+    procs.append([cc, "-x", "hip"] + common + DEVICE_FLAGS +
+                 ["--cuda-device-only", "-S", os.path.join(CSRC, "decode.hip"), "-o", asm])
     # compile (a few in parallel)
     running = []
     for cmd in procs:
@@ -64,10 +68,24 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             _wait(running.pop(0), verbose)
     for r in running:
         _wait(r, verbose)
+    _check_decode_asm(asm)
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_decode_asm(path):
+    sys.path.insert(0, PKG)
+    try:
+        from asm_check import check_qk_chains
+    finally:
+        sys.path.pop(0)
+    with open(path) as f:
+        chains, bad = check_qk_chains(f.read())
+    if chains == 0 or bad:
+        raise RuntimeError(f"decode.hip: the generated code breaks the QK accumulator chains "
+                           f"({chains} chains; offending lines of {path}):\n" + "\n".join(bad[:20]))
 
 
 def _wait(item, verbose):

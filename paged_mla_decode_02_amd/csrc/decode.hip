@@ -1,0 +1,815 @@
+// Paged MLA decode kernel for CDNA4 (gfx950), and the gather test hook that
+// runs its tile loader.
+//
+// One workgroup of four waves (one per SIMD) runs a work item at a time: 128
+// query rows (token i, head h, ordered i * heads + h) of one request row
+// against one split of its keys. Keys stream through LDS in tiles of 32
+// latent rows: the tile's slots come from the row's page-size-1 index list
+// (vLLM pull request 53001, Purpose: one row per request, one flat index
+// list); each latent row is fetched once with 16-byte loads straight into LDS
+// and serves all 128 query rows, i.e. all heads, since MLA has a single latent
+// KV head.
+//
+// Every wave does all three stages of the attention:
+//   QK        wave w owns query rows 32w..32w+31 and keeps their queries (576
+//             dims, bf16; fp8 Q is converted at load) in registers. For tile t
+//             it computes S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys are
+//             the MFMA M side, the 576-dim latent the contraction).
+//   softmax   the mask -- causal on positions: token i of a q_b-token block
+//             sits at L - q_b + i and sees keys j <= L - q_b + i (ATOM pull
+//             request 2760, Problem); non-causal: only the split's range (vLLM
+//             pull request 53001, Purpose) -- and the exponentials in base 2
+//             against a per-row reference max, fixed at the row's first
+//             visible tile, so the accumulated O is never rescaled (a tile
+//             that would overflow the reference makes the item run again
+//             with each row's true max). The wave publishes P^T of its rows in
+//             LDS.
+//   PV        wave w owns output columns 128w..128w+127 of all 128 rows and
+//             accumulates O^T += V^T P^T, V being the first 512 dims of the
+//             same LDS tile (no second load), read transposed with
+//             ds_read_b64_tr_b16; each V^T fragment feeds the four 32-row
+//             blocks.
+// A wave holds 32 query rows, so every 1 KB K fragment it reads from LDS feeds
+// a 32x32x16 MFMA. The lane layout of an S^T accumulator is exactly the B
+// operand of the PV MFMA once the keys of a 16-key half are taken in the order
+// {4g..4g+3, 8+4g..8+4g+3} for lane half g, so P never needs a register
+// shuffle; the V^T reads use the same key order.
+//
+// The three stages form a software pipeline with one barrier per tile: step t
+// runs QK(t), the softmax of tile t-1 and PV(t-2), slot by slot -- each of the
+// 36 QK MFMAs is paired with one of the 32 PV MFMAs, and the softmax's VALU
+// work, the LDS reads for later slots and the next tile's loads are spread
+// between them -- so the matrix core, the VALU and the LDS work at the same
+// time inside one wave.
+//
+// fp8 KV is fetched as fp8 (half the HBM bytes) into a staging tile and
+// converted once per tile to a bf16 tile (exact: every e4m3fn value is a bf16
+// value), so the compute core is the same for all dtypes. Scales are applied
+// to the fp32 scores and to O.
+//
+// The epilogue writes bf16 O and the natural-log LSE when the row has one
+// split, or the split's fp32 partial (O_k, LSE_k) to the workspace; the merge
+// kernel then combines a row's partials by log-sum-exp ([DSV4] Tuned ASM FP8
+// decode with split plans, ATOM pull request 2462, Dependencies).
+//
+// LDS tile layout (bf16): a "main" array of 32 rows x 1024 bytes (latent dims
+// 0..511, which are also V) and a "rope" array of 32 rows x 128 bytes (dims
+// 512..575). One wave-wide 16-byte direct-to-LDS load covers exactly one main
+// row, so its pool slot is wave-uniform. Rows are 1 KB apart, so every row
+// starts in bank 0: main chunk c (16 bytes) of key row i is stored at
+// c ^ s(i) inside its aligned group of 16 chunks, s(i) = 4 (i & 3) +
+// ((i >> 2) & 3), and rope chunk c at c ^ ((i >> 1) & 7). s is a bijection
+// on 0..15, so a K fragment read (16 keys per 16-lane group, one chunk each)
+// covers all banks; it also moves the two low row bits into the chunk's
+// 64-byte sector, so the four keys of one transposed V read land in four
+// different sectors. The swizzle is applied on the global side of each load
+// (the LDS side of a direct load is fixed to consecutive 16-byte chunks).
+//
+// Loads run one tile ahead: step t issues tile t+1's loads first, and every
+// wave waits for its own before the barrier that ends the step. The loads are
+// inline assembly, so the compiler neither waits for them early nor tracks
+// them.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernel_args.h"
+
+namespace mla {
+namespace {
+
+using namespace dev;
+
+constexpr int kDLat = 576;
+constexpr int kDV = 512;
+constexpr int kNT = 32;                       // keys per tile
+constexpr int kMainRow = 1024;                // bf16 bytes of dims 0..511
+constexpr int kRopeRow = 128;                 // bf16 bytes of dims 512..575
+constexpr int kMainBytes = kNT * kMainRow;    // 32768
+constexpr int kRopeBytes = kNT * kRopeRow;    // 4096
+constexpr int kF8MainRow = 512, kF8RopeRow = 64;
+constexpr int kF8MainBytes = kNT * kF8MainRow;        // 16384
+constexpr int kF8TileBytes = kF8MainBytes + kNT * kF8RopeRow;  // 18432
+constexpr int kKSteps = kDLat / 16;           // 36 QK k-steps (32 main + 4 rope)
+constexpr int kWaves = kDecodeThreads / 64;   // 4
+constexpr int kRows = 128;                    // query rows per work item
+constexpr int kRowBlocks = kRows / 32;        // 4 blocks of 32 rows (one per wave)
+constexpr int kWaveCols = kDV / kWaves;       // 128 output columns per wave
+constexpr int kColTiles = kWaveCols / 32;     // 4
+constexpr int kSlotRing = 4;                  // per-wave ring of tile slot lists
+constexpr int kPBytes = kRowBlocks * 2 * 64 * 16;     // P^T of one tile: [4 row blocks][2 key halves][64 lanes] bf16x8
+// bf16 KV: main tiles t-1 (PV), t (QK), t+1, t+2 (loads in flight) and rope
+// tiles t, t+1, t+2. fp8 KV: fp8 staging tiles t, t+1, t+2, bf16 main tiles
+// t-1, t and rope tiles t-1, t.
+constexpr int kBf16MainBufs = 4, kBf16RopeBufs = 3, kF8StageBufs = 3;
+constexpr int kTilesEnd = 143360;             // end of the tile region for either KV dtype
+static_assert(kBf16MainBufs * kMainBytes + kBf16RopeBufs * kRopeBytes <= kTilesEnd, "bf16 tiles");
+static_assert(kF8StageBufs * kF8TileBytes + 2 * kMainBytes + 2 * kRopeBytes <= kTilesEnd, "fp8 tiles");
+constexpr int kOffP = kTilesEnd;                      // [2] P^T buffers (tiles of even / odd index)
+constexpr int kOffL = kOffP + 2 * kPBytes;            // [128] f32 row sums (epilogue)
+constexpr int kOffSlots = kOffL + kRows * 4;          // [4 waves][4][32] int32
+constexpr int kOffMisc = kOffSlots + kWaves * kSlotRing * kNT * 4;     // [4] u32 (restart, merge flags)
+constexpr int kSmemBytes = kOffMisc + 16;                                // 162320
+constexpr int kMaxInKernelSplits = 16;
+constexpr float kRefSlack = 64.0f;       // base-2 headroom above a row's reference max
+static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
+static_assert(kRows == 128, "the plan's M unit");
+
+// LDS offsets of tile t's buffers.
+template <bool KV_FP8> struct Layout;
+template <> struct Layout<false> {
+  static __device__ __forceinline__ int main(int t) { return (t & 3) * kMainBytes; }
+  static __device__ __forceinline__ int rope(int t) { return kBf16MainBufs * kMainBytes + (t % 3) * kRopeBytes; }
+};
+template <> struct Layout<true> {
+  static __device__ __forceinline__ int stage(int t) { return (t % 3) * kF8TileBytes; }
+  static __device__ __forceinline__ int main(int t) { return kF8StageBufs * kF8TileBytes + (t & 1) * kMainBytes; }
+  static __device__ __forceinline__ int rope(int t) {
+    return kF8StageBufs * kF8TileBytes + 2 * kMainBytes + (t & 1) * kRopeBytes;
+  }
+};
+__device__ __forceinline__ int p_buf(int t) { return kOffP + (t & 1) * kPBytes; }
+
+__device__ __forceinline__ int swz_main(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int swz_rope(int row) { return (row >> 1) & 7; }
+
+// ---------------------------------------------------------------------------
+// Tile loader (shared by the decode kernel and the gather test hook).
+
+// One tile's direct-to-LDS loads, spread over the four waves; every wave
+// issues the same number n of load instructions, op(i) for i = 0..n-1.
+// slot_lane: lane j < 32 holds the pool slot of the tile's key j.
+//   bf16: op i < 8 loads main row j = 4 i + w (one 1 KB row per instruction,
+//         its slot wave-uniform); op 8 loads rope rows 8w .. 8w+7, 8 lanes
+//         per row.
+//   fp8:  op i < 4 loads main rows 2k, 2k + 1 for k = 4 i + w (two 512-byte
+//         rows per instruction) into the linear staging tile; op 4 loads rope
+//         rows 8w .. 8w+7, 4 lanes per row.
+template <bool KV_FP8> struct TileDma {
+  static constexpr int kMainOps = (KV_FP8 ? 16 : 32) / kWaves;
+  static constexpr int n = kMainOps + 1;
+  static constexpr int kRopeRows = kNT / kWaves;
+
+  static __device__ __forceinline__ void op(int i, const unsigned char* kv, int slot_lane,
+                                            uint32_t lds0, int main_off, int rope_off, int w,
+                                            int lane) {
+    if constexpr (!KV_FP8) {
+      if (i < kMainOps) {
+        const int j = kWaves * i + w;
+        const int slot = __builtin_amdgcn_readlane(slot_lane, j);   // wave-uniform
+        const unsigned char* row = kv + (int64_t)slot * (2 * kDLat);
+        dma16_sbase(row, (uint32_t)((lane ^ swz_main(j)) << 4), lds0 + main_off + j * kMainRow);
+      } else {
+        const int j = kRopeRows * w + (lane >> 3);
+        const int slot = __shfl(slot_lane, j & 31, 64);
+        const unsigned char* src =
+            kv + (int64_t)slot * (2 * kDLat) + kMainRow + (((lane & 7) ^ swz_rope(j)) << 4);
+        dma16_vaddr(src, lds0 + rope_off + w * kRopeRows * kRopeRow);
+      }
+    } else {
+      const uint32_t stage = lds0 + main_off;   // staging tile: main then rope
+      if (i < kMainOps) {
+        const int k = kWaves * i + w;            // rows 2k (lanes 0-31) and 2k + 1
+        const int slot = __shfl(slot_lane, 2 * k + (lane >> 5), 64);
+        dma16_vaddr(kv + (int64_t)slot * kDLat + ((lane & 31) << 4), stage + k * 1024);
+      } else {
+        const int j = kRopeRows * w + (lane >> 2);
+        const int slot = __shfl(slot_lane, j & 31, 64);
+        const unsigned char* src = kv + (int64_t)slot * kDLat + kF8MainRow + ((lane & 3) << 4);
+        if (lane < 4 * kRopeRows)
+          dma16_vaddr(src, stage + kF8MainBytes + w * kRopeRows * kF8RopeRow);
+      }
+      (void)rope_off;
+    }
+  }
+
+  // All n loads of a tile at once.
+  static __device__ __forceinline__ void all(const unsigned char* kv, int slot_lane, lds_u8* smem,
+                                             int main_off, int rope_off, int w, int lane_in) {
+    const int lane = opaque(lane_in);
+#pragma unroll
+    for (int i = 0; i < n; ++i) op(i, kv, slot_lane, lds_addr_of(smem), main_off, rope_off, w, lane);
+  }
+};
+
+// LDS offsets a tile's loads target: bf16 tiles are loaded in place, fp8 tiles
+// into their staging tile.
+template <bool KV_FP8> __device__ __forceinline__ int dma_main(int t) {
+  if constexpr (KV_FP8) return Layout<true>::stage(t);
+  else return Layout<false>::main(t);
+}
+template <bool KV_FP8> __device__ __forceinline__ int dma_rope(int t) {
+  if constexpr (KV_FP8) return 0;
+  else return Layout<false>::rope(t);
+}
+
+// DMA the slot list of tile `tile` (32 int32, keys clamped to the split) into
+// this wave's private ring entry (one load, lanes 0-31).
+__device__ __forceinline__ void issue_slots(const int32_t* kv_indices, int kv0, int begin, int end,
+                                            int tile, lds_u8* smem, int wave, int lane) {
+  int key = begin + tile * kNT + (lane & 31);
+  key = key < end ? key : end - 1;
+  const uint32_t dst =
+      lds_addr_of(smem) + kOffSlots + (wave * kSlotRing + (tile % kSlotRing)) * kNT * 4;
+  if (lane < 32) dma4_vaddr(kv_indices + kv0 + key, dst);
+}
+
+__device__ __forceinline__ int read_slots(const lds_u8* smem, int tile, int wave, int lane) {
+  return lds_load<int>(smem, kOffSlots + (wave * kSlotRing + (tile % kSlotRing)) * kNT * 4 +
+                                 (lane & 31) * 4);
+}
+
+// Slot of key (lane & 31) of a tile, straight from global memory (used by the
+// gather hook, which loads one tile at a time).
+__device__ __forceinline__ int load_tile_slot(const int32_t* kv_indices, int kv0, int key0, int end,
+                                              int lane) {
+  int key = key0 + (lane & 31);
+  key = key < end ? key : end - 1;
+  return kv_indices[kv0 + key];
+}
+
+// fp8 staging tile -> swizzled bf16 tile (256 threads): a 16-byte fp8 chunk
+// becomes two bf16 chunks.
+__device__ __forceinline__ void convert_tile(lds_u8* smem, int stage, int main_off, int rope_off,
+                                             int tid) {
+#pragma unroll
+  for (int i = 0; i < 1024 / kDecodeThreads; ++i) {
+    const int p = i * kDecodeThreads + tid;
+    const int row = p >> 5, c = p & 31;
+    const u32x4 w = lds_load<u32x4>(smem, stage + row * kF8MainRow + c * 16);
+    const int base = main_off + row * kMainRow;
+    lds_store(smem, base + (((2 * c) ^ swz_main(row)) << 4),
+              cat(fp8x4_to_bf16(w[0]), fp8x4_to_bf16(w[1])));
+    lds_store(smem, base + (((2 * c + 1) ^ swz_main(row)) << 4),
+              cat(fp8x4_to_bf16(w[2]), fp8x4_to_bf16(w[3])));
+  }
+  if (tid < 128) {
+    const int row = tid >> 2, c = tid & 3;
+    const u32x4 w = lds_load<u32x4>(smem, stage + kF8MainBytes + row * kF8RopeRow + c * 16);
+    const int base = rope_off + row * kRopeRow;
+    lds_store(smem, base + (((2 * c) ^ swz_rope(row)) << 4),
+              cat(fp8x4_to_bf16(w[0]), fp8x4_to_bf16(w[1])));
+    lds_store(smem, base + (((2 * c + 1) ^ swz_rope(row)) << 4),
+              cat(fp8x4_to_bf16(w[2]), fp8x4_to_bf16(w[3])));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// QK MFMAs. They go through inline assembly so that their accumulators are
+// VGPRs: the compiler gives every MFMA of a kernel the same accumulator
+// class, and the AGPRs are all taken by the PV accumulators. The 36 products
+// of a tile form one accumulation chain, and a product whose srcC is exactly
+// the previous product's result may issue right behind it (the matrix core
+// forwards the accumulator); padding between two links with wait states
+// costs about 30 cycles per product, so only the last link of a chain waits
+// inside its own statement until its result can be read by the VALU (12 wait
+// states for v_mfma_f32_32x32x16_bf16). The compiler does not know when an
+// assembly MFMA's result arrives, so nothing else may read or write the
+// accumulator between two links: the library build checks the generated code
+// for that. The destination of a multi-pass MFMA may not overlap its A or B
+// operand, hence the early clobber on the first product of a chain (in the
+// others the accumulator is an input too, so it cannot share registers with
+// them).
+__device__ __forceinline__ void mfma_qk_first(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk_last(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3" : "+v"(d) : "v"(a), "v"(b));
+}
+
+// Per-lane LDS addressing, fixed for a work item.
+//   K fragment (A operand of S^T = K Q^T), k-step ks: lane l holds key
+//   i = l & 31, dims 16 ks + 8 (l >> 5) .. +7 -- main chunk 2 ks + h of row i,
+//   stored at (2 ks) ^ xm with xm = h ^ swz_main(i), or rope chunk
+//   2 (ks - 32) + h at (2 (ks - 32)) ^ xr.
+//   V^T fragment (A operand of O^T += V^T P^T), column tile ct, key half kk:
+//   lane l takes column 32 (4w + ct) + (l & 31) and keys 16 kk + {4g..4g+3,
+//   8+4g..8+4g+3}, g = l >> 5, as two transposed reads q = 0, 1. In each,
+//   source lane li = l & 15 of a 16-lane block points at key
+//   16 kk + 8 q + kb (kb = 4 g + li / 4) and columns 4 (li % 4) .. +3 of the
+//   block's 16: logical chunk 16 w + 4 ct + c0 (c0 = 2 ((l >> 4) & 1) + (li & 3) / 2)
+//   of that key, stored at chunk 16 w + ((4 ct + c0) ^ swz_main(8 q + kb)) =
+//   16 w + 4 (ct ^ r) + (c0 ^ (2 q + g)) with r = li >> 2: the four keys of a
+//   half-wave's read sit in the four different 64-byte bank sectors, and its
+//   32 lanes cover all 64 banks once.
+struct LaneAddr {
+  int krow, xm, rrow, xr;   // K
+  int va;                   // V: kb * 1024 + 256 w + 64 r + 16 (c0 ^ g) + 8 (li & 1)
+  int pl;                   // P: lane * 16
+  int w;
+};
+__device__ __forceinline__ LaneAddr lane_addr(int lane, int w) {
+  LaneAddr a;
+  const int i = lane & 31, h = lane >> 5;
+  a.krow = i * kMainRow;
+  a.xm = h ^ swz_main(i);
+  a.rrow = i * kRopeRow;
+  a.xr = h ^ swz_rope(i);
+  const int li = lane & 15, g16 = (lane >> 4) & 1, g = lane >> 5;
+  const int kb = 4 * g + (li >> 2), c0 = 2 * g16 + ((li & 3) >> 1);
+  a.va = kb * kMainRow + 256 * w + 64 * (li >> 2) + 16 * (c0 ^ g) + 8 * (li & 1);
+  a.pl = lane * 16;
+  a.w = w;
+  return a;
+}
+
+__device__ __forceinline__ bf16x8 k_frag(const lds_u8* smem, const LaneAddr& la, int kmain, int krope, int ks) {
+  if (ks < 32)
+    return lds_load<bf16x8>(smem, kmain + la.krow + (ks >> 3) * 256 + (((2 * (ks & 7)) ^ la.xm) << 4));
+  return lds_load<bf16x8>(smem, krope + la.rrow + (((2 * (ks - 32)) ^ la.xr) << 4));
+}
+
+// V^T fragment for PV MFMAs (kk, ct): two transposed 8-byte reads. The XOR
+// constants select the column tile (bits 6-7) and, for q = 1, flip
+// c0 ^ g into c0 ^ (2 + g) (bit 5).
+__device__ __forceinline__ bf16x8 v_frag(const lds_u8* smem, const LaneAddr& la, int vmain, int kk, int ct) {
+  const int base = vmain + 16 * kMainRow * kk;
+  const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(smem + base + (la.va ^ (ct << 6))));
+  const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(smem + base + 8 * kMainRow + (la.va ^ ((ct << 6) | 32))));
+  return cat(__builtin_bit_cast(bf16x4, v0), __builtin_bit_cast(bf16x4, v1));
+}
+
+__device__ __forceinline__ bf16x8 p_frag(const lds_u8* smem, const LaneAddr& la, int pbuf, int rb, int kk) {
+  return lds_load<bf16x8>(smem, pbuf + (rb * 2 + kk) * 1024 + la.pl);
+}
+
+// Softmax of one tile on this wave's rows, in pieces that the pipelined step
+// spreads over its MFMA slots. S^T register r of lane l is row l & 31, key
+// key0 + 8 (r / 4) + r % 4 with key0 = tile start + 4 (l >> 5). A key is
+// visible iff it is below the split's end and at most the row's position
+// limit: lim = min(end - 1, pos_limit) - key0 (one compare per score). A
+// row's reference max m_ref is its first visible tile's max (in base 2) and
+// then stays fixed; a tile more than kRefSlack above it sets `over` (the item
+// is recomputed with the row's true max, m_seen).
+struct Softmax {
+  float tmax, mu;
+  bf16x8 pf[2];
+};
+struct RowState {
+  float m_ref, m_seen, l_part;
+  bool over;
+};
+// piece 0..3: scale and mask 4 scores, running max; piece 4: row max, the
+// reference; pieces 5..12: two exponentials each.
+__device__ __forceinline__ void softmax_piece(int piece, Softmax& sm, f32x16& s, float score_c, int lim,
+                                              RowState& rs) {
+  // The scores are scaled and masked in place (s is dead after this tile).
+  if (piece < 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * piece + e;
+      const float v = s[r] * score_c;
+      s[r] = (8 * (r >> 2) + (r & 3) <= lim) ? v : -INFINITY;
+    }
+    const float m4 = fmaxf(fmaxf(s[4 * piece], s[4 * piece + 1]), fmaxf(s[4 * piece + 2], s[4 * piece + 3]));
+    sm.tmax = piece == 0 ? m4 : fmaxf(sm.tmax, m4);
+  } else if (piece == 4) {
+    const float tmax = half_max(sm.tmax);
+    rs.m_seen = fmaxf(rs.m_seen, tmax);
+    // Until a row has seen a visible key its O and l are exactly zero, so its
+    // reference may start at this tile's max without rescaling anything.
+    if (rs.m_ref == -INFINITY) rs.m_ref = tmax;
+    rs.over = rs.over || (tmax > rs.m_ref + kRefSlack);
+    sm.mu = rs.m_ref == -INFINITY ? 0.0f : rs.m_ref;
+  } else if (piece < 13) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 2 * (piece - 5) + e;
+      // v_exp_f32 directly: arguments below -126 give 0 or a denormal, which
+      // only drops weights under 2^-126 of the row's reference.
+      const float pr = __builtin_amdgcn_exp2f(s[r] - sm.mu);
+      rs.l_part += pr;
+      sm.pf[r >> 3][r & 7] = (__bf16)pr;
+    }
+  }
+}
+constexpr int kSoftmaxPieces = 13;
+
+// ---------------------------------------------------------------------------
+// In-kernel merge of one (row b, M tile m): rows m 128 .. m 128 + 127 of the
+// row's block, n <= kMaxInKernelSplits fp32 partials each (consecutive
+// partial slots from part0). Thread tid takes 32 (row, 8-column chunk) pairs.
+__device__ __forceinline__ void merge_tile(const DecodeArgs& a, int m, int M, int n, int part0,
+                                           int q0, int tid) {
+  const int H = a.heads;
+  const int64_t stride = (int64_t)a.q_len_max * H;   // between consecutive partial slots
+  for (int i = 0; i < kRows * 64 / kDecodeThreads; ++i) {
+    const int pair = tid + i * kDecodeThreads;
+    const int rr = pair >> 6, c = pair & 63;
+    const int r = m * kRows + rr;
+    if (r >= M) continue;
+    const int tok = r / H, h = r - tok * H;
+    const int64_t base = ((int64_t)part0 * a.q_len_max + tok) * H + h;
+    const int64_t orow = (int64_t)(q0 + tok) * H + h;
+    float lk[kMaxInKernelSplits];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMaxInKernelSplits; ++k) {
+      lk[k] = k < n ? a.ws_lse[base + k * stride] : -INFINITY;
+      mx = fmaxf(mx, lk[k]);
+    }
+    uint16_t* dst = a.o + orow * kDV + c * 8;
+    if (mx == -INFINITY) {   // no split sees a key
+      *(u32x4*)dst = u32x4{0u, 0u, 0u, 0u};
+      if (c == 0) a.lse[orow] = -INFINITY;
+      continue;
+    }
+    float tot = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxInKernelSplits; ++k) {
+      lk[k] = lk[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lk[k] - mx) * kLog2e);
+      tot += lk[k];
+    }
+    const float inv = 1.0f / tot;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kMaxInKernelSplits; ++k) {
+      if (k < n) {
+        const f32x4* src = (const f32x4*)(a.ws_o + (base + k * stride) * kDV + c * 8);
+        const float wk = lk[k] * inv;   // an empty split's partial is 0 and its weight 0
+        acc0 += wk * src[0];
+        acc1 += wk * src[1];
+      }
+    }
+    *(bf16x8*)dst = bf16x8{(__bf16)acc0[0], (__bf16)acc0[1], (__bf16)acc0[2], (__bf16)acc0[3],
+                           (__bf16)acc1[0], (__bf16)acc1[1], (__bf16)acc1[2], (__bf16)acc1[3]};
+    if (c == 0) a.lse[orow] = mx + __log2f(tot) * kLn2;
+  }
+}
+
+// PV product p (0..31) of a tile: key half kk = p / 16, column tile
+// ct = (p / 4) % 4, row block rb = p % 4. Each V^T fragment feeds four
+// products and is read four products ahead; the key-half-1 P^T fragment of a
+// row block replaces key half 0's after its last use.
+__device__ __forceinline__ void pv_product(const lds_u8* smem, const LaneAddr& la, int vmain, int pbuf, int p,
+                                           bf16x8 (&vb)[2], bf16x8 (&pb)[kRowBlocks],
+                                           f32x16 (&oacc)[kRowBlocks][kColTiles]) {
+  const int kk = p >> 4, ct = (p >> 2) & 3, rb = p & 3;
+  if (rb == 0 && p + 4 < 32) vb[((p >> 2) + 1) & 1] = v_frag(smem, la, vmain, (p + 4) >> 4, ((p + 4) >> 2) & 3);
+  oacc[rb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[(p >> 2) & 1], pb[rb], oacc[rb][ct], 0, 0, 0);
+  if (kk == 0 && ct == 3) pb[rb] = p_frag(smem, la, pbuf, rb, 1);
+}
+
+// One pipeline step: QK(t) with the K tile in (kmain, krope) into s, then the
+// softmax of tile t (masked by lim) published as P^T in pwrite; PV(t-1) with V
+// in vmain and P^T in pbuf. dma(i), i < NDMA, issues later tiles' loads. The first kPvEarly PV products are paired with the 36 QK products
+// (one QK product per slot); the rest run between the softmax's pieces once
+// the scores are complete. A sched_barrier ends every slot, so the compiler
+// keeps this order; K fragments are read kKDepth products ahead.
+constexpr int kKDepth = 5;
+constexpr int kPvEarly = 20;
+template <bool QK, bool PV, int NDMA, typename Dma>
+__device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, const bf16x8 (&qf)[kKSteps],
+                                              int kmain, int krope, f32x16& s_acc, Softmax& sm, float score_c,
+                                              int lim, RowState& rs, int pwrite, int vmain, int pbuf,
+                                              f32x16 (&oacc)[kRowBlocks][kColTiles], Dma&& dma) {
+  bf16x8 kb[kKDepth];
+  bf16x8 pb[kRowBlocks];
+  bf16x8 vb[2];
+  if constexpr (QK) {
+#pragma unroll
+    for (int d = 0; d < kKDepth; ++d) kb[d] = k_frag(smem, la, kmain, krope, d);
+  }
+  if constexpr (PV) {
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) pb[rb] = p_frag(smem, la, pbuf, rb, 0);
+    vb[0] = v_frag(smem, la, vmain, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < kKSteps; ++s) {
+    if (s < NDMA) dma(s);
+    if constexpr (QK) {
+      const bf16x8 a = kb[s % kKDepth];
+      if (s + kKDepth < kKSteps) kb[s % kKDepth] = k_frag(smem, la, kmain, krope, s + kKDepth);
+      if (s == 0) mfma_qk_first(s_acc, a, qf[s]);
+      else if (s + 1 < kKSteps) mfma_qk(s_acc, a, qf[s]);
+      else mfma_qk_last(s_acc, a, qf[s]);
+    }
+    if constexpr (PV) {
+      if (s < kPvEarly) pv_product(smem, la, vmain, pbuf, s, vb, pb, oacc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  constexpr int kTail = (32 - kPvEarly) > kSoftmaxPieces ? (32 - kPvEarly) : kSoftmaxPieces;
+#pragma unroll
+  for (int j = 0; j < kTail; ++j) {
+    if constexpr (PV) {
+      if (kPvEarly + j < 32) pv_product(smem, la, vmain, pbuf, kPvEarly + j, vb, pb, oacc);
+    }
+    if constexpr (QK) {
+      if (j < kSoftmaxPieces) softmax_piece(j, sm, s_acc, score_c, lim, rs);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (QK) {   // publish P^T of this wave's rows (read after the step's barrier)
+    lds_store(smem, pwrite + (la.w * 2 + 0) * 1024 + la.pl, sm.pf[0]);
+    lds_store(smem, pwrite + (la.w * 2 + 1) * 1024 + la.pl, sm.pf[1]);
+  }
+}
+
+// MERGE: the variant for in-kernel-merge plans (the default variant carries
+// none of that code, which would cost the hot loops registers).
+template <bool Q_FP8, bool KV_FP8, bool MERGE>
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmemBytes];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  using LY = Layout<KV_FP8>;
+  using Dma = TileDma<KV_FP8>;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.heads;
+  const unsigned char* kv = (const unsigned char*)a.kv;
+  const float q_scale = a.q_scale ? *a.q_scale : 1.0f;
+  const float kv_scale = a.kv_scale ? *a.kv_scale : 1.0f;
+  const float score_c = a.score_scale_log2 * q_scale * kv_scale;
+
+  const int g = blockIdx.x;
+  const int it0 = a.plan[a.off_work_indptr + g], it1 = a.plan[a.off_work_indptr + g + 1];
+  for (int it = it0; it < it1; ++it) {
+    const int s = a.plan[a.off_item_split + it];
+    const int m = a.plan[a.off_item_m + it];
+    const int b = a.plan[a.off_split_row + s];
+    const int part = a.plan[a.off_split_part + s];
+    const int q0 = a.qo_indptr[b], q_b = a.qo_indptr[b + 1] - q0;
+    const int kv0 = a.kv_indptr[b], L = a.kv_indptr[b + 1] - kv0;
+    const int s0 = a.plan[a.off_split_indptr + b];
+    const int nsplit = a.plan[a.off_split_indptr + b + 1] - s0;
+    int begin, end;
+    if (a.uniform_ranges) {   // split k of n covers [k L / n, (k + 1) L / n) of the live length
+      begin = (int)((int64_t)(s - s0) * L / nsplit);
+      end = (int)((int64_t)(s - s0 + 1) * L / nsplit);
+    } else {
+      begin = a.plan[a.off_split_begin + s];
+      end = a.plan[a.off_split_end + s];
+    }
+    const int M = q_b * H;
+    if (m * kRows >= M) continue;   // no query row in this tile (ragged block); uniform
+    const int ntiles = (end - begin + kNT - 1) / kNT;
+
+    // ---- this wave's query rows: m 128 + 32 w + (lane & 31)
+    const int mr = m * kRows + 32 * w + (lane & 31);
+    const bool row_ok = mr < M;
+    const int tok = row_ok ? mr / H : 0;
+    const int head = row_ok ? mr - tok * H : 0;
+    // Causal mask on global positions: local key j sits at j * world + rank
+    // of the row's P keys over all shards, token tok at P - q_b + tok; the
+    // visible local keys are j <= (P - q_b + tok - rank) / world (one shard:
+    // j <= L - q_b + tok). Rows past the end of the block are computed but
+    // never written; they take the non-causal limit.
+    const int Pk = a.kv_len_global ? a.kv_len_global[b] : L;
+    const int qpos = Pk - q_b + tok - a.dcp_rank;
+    const int causal_lim = qpos >= 0 ? qpos / a.dcp_world : -1;
+    const int pos_limit = (a.causal && row_ok) ? causal_lim : (L - 1);
+    const int key_last = min(end - 1, pos_limit);   // last visible key of this row in the split
+    // lane holds Q[row][16 ks + 8 (lane >> 5) .. +7] for ks = 0..35 (B operand of S^T = K Q^T)
+    bf16x8 qf[kKSteps];
+    if (row_ok) {
+      const int64_t qrow = ((int64_t)(q0 + tok) * H + head) * kDLat + 8 * (lane >> 5);
+      if constexpr (!Q_FP8) {
+        const bf16x8* src = (const bf16x8*)((const uint16_t*)a.q + qrow);
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = src[ks * 2];
+      } else {
+        const u32x2* src = (const u32x2*)((const unsigned char*)a.q + qrow);
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+          const u32x2 v = src[ks * 2];
+          qf[ks] = cat(fp8x4_to_bf16(v[0]), fp8x4_to_bf16(v[1]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = bf16x8{};
+    }
+
+    // Pass 0 fixes each row's reference at its first visible tile's max. In
+    // the rare case that a later tile exceeds it by more than kRefSlack, the
+    // item runs once more with every row's reference at its true max.
+    RowState rs{-INFINITY, -INFINITY, 0.f, false};
+    f32x16 oacc[kRowBlocks][kColTiles];
+    for (int pass = 0; pass < 2; ++pass) {
+      rs.l_part = 0.f;
+      rs.over = false;
+#pragma unroll
+      for (int rb = 0; rb < kRowBlocks; ++rb)
+#pragma unroll
+        for (int ct = 0; ct < kColTiles; ++ct) oacc[rb][ct] = f32x16{};
+      if (ntiles > 0) {
+        // Prologue: slot lists of tiles 0..3, then the loads of tiles 0 and
+        // 1, each preceded by one slot-list load so that every later wait
+        // count has the same form; tile 0 lands.
+#pragma unroll
+        for (int t = 0; t < 4; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, w, lane);
+        wait_vm<0>();
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          issue_slots(a.kv_indices, kv0, begin, end, t + 2, smem, w, lane);
+          if (t < ntiles)
+            Dma::all(kv, read_slots(smem, t, w, lane), smem, dma_main<KV_FP8>(t), dma_rope<KV_FP8>(t), w, lane);
+        }
+        if (ntiles > 1) wait_vm<1 + Dma::n>();
+        else wait_vm<1>();
+        __syncthreads();
+        if constexpr (KV_FP8) {
+          convert_tile(smem, LY::stage(0), LY::main(0), LY::rope(0), tid);
+          __syncthreads();
+        }
+
+        f32x16 s_acc;
+        Softmax sm;
+        // Step t: QK(t) and the softmax of tile t if t < ntiles, PV(t-1) if
+        // t >= 1; the loads of tile t+2 are issued first. The step ends with
+        // P(t) stored, this wave's loads of tile t+1 landed and one barrier.
+        // DMA: this step issues tile t+2's loads (t + 2 < ntiles); it is a
+        // template flag, so the hot loop carries no per-load branch.
+        auto run_step = [&](int t, auto QKc, auto PVc, auto DMAc) {
+          constexpr bool DO_QK = decltype(QKc)::value, DO_PV = decltype(PVc)::value;
+          constexpr bool DO_DMA = decltype(DMAc)::value;
+          const int dlane = opaque(lane);
+          issue_slots(a.kv_indices, kv0, begin, end, t + 4, smem, w, dlane);
+          constexpr bool have = DO_DMA;
+          const int slot = have ? read_slots(smem, t + 2, w, dlane) : 0;
+          const int dm = dma_main<KV_FP8>(t + 2), dr = dma_rope<KV_FP8>(t + 2);
+          auto dma = [&](int i) {
+            Dma::op(i, kv, slot, lds_addr_of(smem), dm, dr, w, dlane);
+          };
+          const int lim = key_last - (begin + t * kNT + 4 * (lane >> 5));
+          const LaneAddr la_s = lane_addr(dlane, w);
+          pipeline_step<DO_QK, DO_PV, DO_DMA ? Dma::n : 0>(smem, la_s, qf, LY::main(t), LY::rope(t), s_acc, sm,
+                                                            score_c, lim, rs, p_buf(t), LY::main(t + 11), p_buf(t + 1),
+                                                            oacc, dma);
+          if (have) wait_vm<1 + Dma::n>();
+          else wait_vm<1>();
+          __syncthreads();   // tile t+1 landed; P(t) published; tile t-1 and P(t-1) are free
+          if constexpr (KV_FP8) {
+            if (t + 1 < ntiles) {
+              convert_tile(smem, LY::stage(t + 1), LY::main(t + 1), LY::rope(t + 1), tid);
+              __syncthreads();
+            }
+          }
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        // ntiles + 1 steps: 0 .. ntiles
+        if (ntiles > 2) run_step(0, T_{}, F_{}, T_{});
+        else run_step(0, T_{}, F_{}, F_{});
+        for (int t = 1; t + 2 < ntiles; ++t) run_step(t, T_{}, T_{}, T_{});
+        for (int t = ntiles > 3 ? ntiles - 2 : 1; t < ntiles; ++t) run_step(t, T_{}, T_{}, F_{});
+        run_step(ntiles, F_{}, T_{}, F_{});
+        wait_vm<0>();
+      }
+      // Did any row of the item overflow its reference? (uniform)
+      if (lane == 0) lds_store(smem, kOffMisc + 4 * w, (uint32_t)(__ballot(rs.over) != 0));
+      __syncthreads();
+      const u32x4 ov = lds_load<u32x4>(smem, kOffMisc);
+      __syncthreads();
+      if ((ov[0] | ov[1] | ov[2] | ov[3]) == 0u) break;
+      rs.m_ref = rs.m_seen;   // pass 1: no tile can exceed the true max
+    }
+
+    // Epilogue: the rows' sums and LSE, then O normalized and written.
+    const float l_row = half_sum(rs.l_part);
+    if (lane < 32) lds_store(smem, kOffL + (w * 32 + lane) * 4, l_row);
+    if (row_ok && lane < 32) {
+      const float lse = l_row > 0.f ? (rs.m_ref + __log2f(l_row)) * kLn2 : -INFINITY;
+      if (part < 0) a.lse[(int64_t)(q0 + tok) * H + head] = lse;
+      else a.ws_lse[((int64_t)part * a.q_len_max + tok) * H + head] = lse;
+    }
+    __syncthreads();
+    const int hh = lane >> 5;
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+      const int r = m * kRows + rb * 32 + (lane & 31);
+      if (r >= M) continue;
+      const float l = lds_load<float>(smem, kOffL + (rb * 32 + (lane & 31)) * 4);
+      const float inv = l > 0.f ? kv_scale / l : 0.f;
+      const int rt = r / H, rh = r - rt * H;
+      const int col0 = w * kWaveCols + 4 * hh;
+      if (part < 0) {
+        uint16_t* dst = a.o + ((int64_t)(q0 + rt) * H + rh) * kDV + col0;
+#pragma unroll
+        for (int ct = 0; ct < kColTiles; ++ct)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const f32x16& v = oacc[rb][ct];
+            const bf16x4 bv = {(__bf16)(v[4 * gq] * inv), (__bf16)(v[4 * gq + 1] * inv),
+                               (__bf16)(v[4 * gq + 2] * inv), (__bf16)(v[4 * gq + 3] * inv)};
+            *(bf16x4*)(dst + 32 * ct + 8 * gq) = bv;
+          }
+      } else {
+        float* dst = a.ws_o + (((int64_t)part * a.q_len_max + rt) * H + rh) * kDV + col0;
+#pragma unroll
+        for (int ct = 0; ct < kColTiles; ++ct)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const f32x16& v = oacc[rb][ct];
+            *(f32x4*)(dst + 32 * ct + 8 * gq) =
+                f32x4{v[4 * gq] * inv, v[4 * gq + 1] * inv, v[4 * gq + 2] * inv, v[4 * gq + 3] * inv};
+          }
+      }
+    }
+    __syncthreads();   // LDS is reused by the next item
+
+    // A split row with few splits is merged here by the last of its splits
+    // to finish this M tile: every thread releases its partial stores, one
+    // counts the arrival, and the last arrival reads the other splits'
+    // partials after an acquire and writes the tile's O and LSE, then
+    // re-zeroes the counter for the next call.
+    if (MERGE && part >= 0 && nsplit <= a.inkernel_max_splits) {
+      wait_vm_all();     // this thread's partial stores have reached L2
+      __syncthreads();
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // one L2 write-back for the block
+        const int old = __hip_atomic_fetch_add(a.counters + b * a.u + m, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        lds_store(smem, kOffMisc, (uint32_t)(old == nsplit - 1));
+      }
+      __syncthreads();
+      if (lds_load<uint32_t>(smem, kOffMisc) != 0u) {   // uniform
+        if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // invalidates for the block
+        __syncthreads();
+        merge_tile(a, m, M, nsplit, a.plan[a.off_split_part + s0], q0, tid);
+        if (tid == 0) a.counters[b * a.u + m] = 0;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gather test hook: one block per split; every tile goes through the decode
+// kernel's loader (and fp8 conversion) into tile 0, then is copied out of LDS
+// with the swizzle undone.
+template <bool KV_FP8>
+__global__ __launch_bounds__(kDecodeThreads) void gather_kernel(GatherArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kTilesEnd];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  using LY = Layout<KV_FP8>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = blockIdx.x;
+  const int b = a.plan[a.off_split_row + s];
+  const int kv0 = a.kv_indptr[b];
+  int begin = a.plan[a.off_split_begin + s], end = a.plan[a.off_split_end + s];
+  if (a.uniform_ranges) {   // same ranges as the decode kernel
+    const int s0 = a.plan[a.off_split_indptr + b];
+    const int n = a.plan[a.off_split_indptr + b + 1] - s0;
+    const int L = a.kv_indptr[b + 1] - kv0;
+    begin = (int)((int64_t)(s - s0) * L / n);
+    end = (int)((int64_t)(s - s0 + 1) * L / n);
+  }
+  const int64_t dense0 = (int64_t)(kv0 - a.kv_indptr[0]);
+  const unsigned char* kv = (const unsigned char*)a.kv;
+  for (int key0 = begin; key0 < end; key0 += kNT) {
+    const int slot = load_tile_slot(a.kv_indices, kv0, key0, end, lane);
+    TileDma<KV_FP8>::all(kv, slot, smem, dma_main<KV_FP8>(0), dma_rope<KV_FP8>(0), wave, lane);
+    wait_vm_all();
+    __syncthreads();
+    if constexpr (KV_FP8) {
+      convert_tile(smem, Layout<true>::stage(0), LY::main(0), LY::rope(0), tid);
+      __syncthreads();
+    }
+    for (int p = tid; p < kNT * 72; p += kDecodeThreads) {
+      const int row = p / 72, chunk = p - row * 72;
+      if (key0 + row < end) {
+        const int off = chunk < 64 ? LY::main(0) + row * kMainRow + ((chunk ^ swz_main(row)) << 4)
+                                   : LY::rope(0) + row * kRopeRow + (((chunk - 64) ^ swz_rope(row)) << 4);
+        const u32x4 v = lds_load<u32x4>(smem, off);
+        *(u32x4*)(a.dense + (dense0 + key0 + row) * kDLat + chunk * 8) = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+template <bool MERGE>
+const void* decode_fn(bool q_fp8, bool kv_fp8) {
+  if (!q_fp8 && !kv_fp8) return (const void*)decode_kernel<false, false, MERGE>;
+  if (!q_fp8 && kv_fp8) return (const void*)decode_kernel<false, true, MERGE>;
+  if (q_fp8 && !kv_fp8) return (const void*)decode_kernel<true, false, MERGE>;
+  return (const void*)decode_kernel<true, true, MERGE>;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, int grid, hipStream_t st) {
+  void* args[] = {(void*)&a};
+  const void* fn = a.inkernel_max_splits > 1 ? decode_fn<true>(q_fp8, kv_fp8) : decode_fn<false>(q_fp8, kv_fp8);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kDecodeThreads), args, 0, st);
+}
+
+hipError_t launch_gather(const GatherArgs& a, bool kv_fp8, int splits, hipStream_t st) {
+  void* args[] = {(void*)&a};
+  const void* fn = kv_fp8 ? (const void*)gather_kernel<true> : (const void*)gather_kernel<false>;
+  return hipLaunchKernel(fn, dim3(splits), dim3(kDecodeThreads), args, 0, st);
+}
+
+}  // namespace mla

@@ -77,7 +77,7 @@ struct CacheWriteArgs {
 };
 
 constexpr int kBlockThreads = 256;   // merge kernel: 4 waves of 64, one block per (row, token, head)
-constexpr int kDecodeThreads = 512;  // decode and gather kernels: 8 waves of 64
+constexpr int kDecodeThreads = 256;  // decode and gather kernels: 4 waves of 64, one per SIMD
 
 hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, int grid, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, hipStream_t st);

@@ -14,11 +14,11 @@ namespace mla {
 constexpr int32_t kPlanMagic = 0x4D4C4150;
 constexpr int32_t kPlanVersion = 1;
 constexpr int32_t kHeaderWords = 20;
-constexpr int32_t kMUnit = 64;
+constexpr int32_t kMUnit = 128;
 constexpr int32_t kNMax = 64;
 constexpr int32_t kMinSplitKeys = 256;
 constexpr int32_t kItemOverhead = 64;
-constexpr int32_t kOcc = 2;
+constexpr int32_t kOcc = 1;
 constexpr int32_t kXcds = 8;
 
 // Workspace layout: the fp32 partial O and LSE of the split rows; with an
