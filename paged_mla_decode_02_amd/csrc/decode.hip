@@ -115,6 +115,7 @@ constexpr int kMaxInKernelSplits = 16;
 constexpr float kRefSlack = 64.0f;       // base-2 headroom above a row's reference max
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
 static_assert(kRows == 128, "the plan's M unit");
+static_assert(64 * kDV * 4 <= kTilesEnd, "epilogue staging of 64 fp32 rows");
 
 // LDS offsets of tile t's buffers.
 template <bool KV_FP8> struct Layout;
@@ -684,39 +685,65 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       else a.ws_lse[((int64_t)part * a.q_len_max + tok) * H + head] = lse;
     }
     __syncthreads();
-    const int hh = lane >> 5;
+    // O leaves through LDS so that the stores are whole rows: the item's
+    // query rows r = m 128 .. m 128 + 127 are consecutive rows of O (index
+    // q0 H + r) and of its partial slot (index (part q_len_max) H + r). Two
+    // halves of 64 rows; a half is staged as fp32 [64][512] in the tile region,
+    // 16-byte chunk c of row r at c ^ (r & 15).
+    {
+      // Opaque copies: the addresses below are recomputed here rather than
+      // hoisted out of the item loop and kept live across it.
+      const int el = opaque(lane), et = opaque(tid);
+      const int hh = el >> 5;
+      const int64_t orow0 = part < 0 ? (int64_t)q0 * H + (int64_t)m * kRows
+                                     : (int64_t)part * a.q_len_max * H + (int64_t)m * kRows;
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
-      const int r = m * kRows + rb * 32 + (lane & 31);
-      if (r >= M) continue;
-      const float l = lds_load<float>(smem, kOffL + (rb * 32 + (lane & 31)) * 4);
-      const float inv = l > 0.f ? kv_scale / l : 0.f;
-      const int rt = r / H, rh = r - rt * H;
-      const int col0 = w * kWaveCols + 4 * hh;
-      if (part < 0) {
-        uint16_t* dst = a.o + ((int64_t)(q0 + rt) * H + rh) * kDV + col0;
+      for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct)
+        for (int r2 = 0; r2 < 2; ++r2) {
+          const int rb = 2 * half + r2;
+          const int r = 32 * r2 + (el & 31);   // row within the half
+          const float l = lds_load<float>(smem, kOffL + (rb * 32 + (el & 31)) * 4);
+          const float inv = l > 0.f ? kv_scale / l : 0.f;
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const f32x16& v = oacc[rb][ct];
-            const bf16x4 bv = {(__bf16)(v[4 * gq] * inv), (__bf16)(v[4 * gq + 1] * inv),
-                               (__bf16)(v[4 * gq + 2] * inv), (__bf16)(v[4 * gq + 3] * inv)};
-            *(bf16x4*)(dst + 32 * ct + 8 * gq) = bv;
+          for (int ct = 0; ct < kColTiles; ++ct)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const f32x16& v = oacc[rb][ct];
+              const int c = 32 * w + 8 * ct + 2 * gq + hh;   // columns 4c .. 4c+3
+              lds_store(smem, r * 2048 + ((c ^ (r & 15)) << 4),
+                        f32x4{v[4 * gq] * inv, v[4 * gq + 1] * inv, v[4 * gq + 2] * inv, v[4 * gq + 3] * inv});
+            }
+        }
+        __syncthreads();
+        const int nrows = min(64, M - (m * kRows + 64 * half));   // rows of this half inside the block
+        if (part < 0) {
+          // bf16: thread takes 8 columns (two chunks) of a row per store
+#pragma unroll 4
+          for (int i = 0; i < 64 * 64 / kDecodeThreads; ++i) {
+            const int p2 = i * kDecodeThreads + et;
+            const int r = p2 >> 6, c2 = p2 & 63;
+            if (r < nrows) {
+              const f32x4 x0 = lds_load<f32x4>(smem, r * 2048 + (((2 * c2) ^ (r & 15)) << 4));
+              const f32x4 x1 = lds_load<f32x4>(smem, r * 2048 + (((2 * c2 + 1) ^ (r & 15)) << 4));
+              *(bf16x8*)(a.o + (orow0 + 64 * half + r) * kDV + 8 * c2) =
+                  bf16x8{(__bf16)x0[0], (__bf16)x0[1], (__bf16)x0[2], (__bf16)x0[3],
+                         (__bf16)x1[0], (__bf16)x1[1], (__bf16)x1[2], (__bf16)x1[3]};
+            }
           }
-      } else {
-        float* dst = a.ws_o + (((int64_t)part * a.q_len_max + rt) * H + rh) * kDV + col0;
-#pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const f32x16& v = oacc[rb][ct];
-            *(f32x4*)(dst + 32 * ct + 8 * gq) =
-                f32x4{v[4 * gq] * inv, v[4 * gq + 1] * inv, v[4 * gq + 2] * inv, v[4 * gq + 3] * inv};
+        } else {
+#pragma unroll 4
+          for (int i = 0; i < 64 * 128 / kDecodeThreads; ++i) {
+            const int p2 = i * kDecodeThreads + et;
+            const int r = p2 >> 7, c = p2 & 127;
+            if (r < nrows)
+              *(f32x4*)(a.ws_o + (orow0 + 64 * half + r) * kDV + 4 * c) =
+                  lds_load<f32x4>(smem, r * 2048 + ((c ^ (r & 15)) << 4));
           }
+        }
+        __syncthreads();
       }
     }
-    __syncthreads();   // LDS is reused by the next item
 
     // A split row with few splits is merged here by the last of its splits
     // to finish this M tile: every thread releases its partial stores, one
