@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--workload", default="verify_causal")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work; 0 skips")
     ap.add_argument("--rotate", type=int, default=3, help="disjoint index lists cycled over steps")
+    ap.add_argument("--plan", default="length_aware", choices=["auto", "uniform", "length_aware"],
+                    help="split plan mode (the uniform plan is also timed beside it)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warm-up, one plain device copy of this many MiB: the known-size "
                          "reference for scaling hardware byte counters")
@@ -181,8 +183,10 @@ def main():
                             case.qo_indptr, case.kv_indptr, case.kv_indices)
     idx_dev = [dev["kv_indices"]] + [torch.from_numpy(i).cuda() for i in index_sets[1:]]
     inputs = [dict(dev, kv_indices=t) for t in idx_dev]
+    plan_modes = {"auto": mla.PLAN_AUTO, "uniform": mla.PLAN_UNIFORM,
+                  "length_aware": mla.PLAN_LENGTH_AWARE}
     dec = mla.MlaDecoder(case.heads, case.q_len, case.q_dtype, case.kv_dtype, case.causal,
-                         float(case.sm_scale))
+                         float(case.sm_scale), mode=plan_modes[args.plan])
     T = case.num_tokens
     o = torch.empty((T, case.heads, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((T, case.heads), dtype=torch.float32, device="cuda")
@@ -193,7 +197,7 @@ def main():
     # rows cached; the fill is outside the decode's events but inside the step.
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if len(inputs) < 2 else None
 
-    def step(k, ev=None):
+    def step(k, ev=None, dec=dec):
         words = dec.make_plan(kv_lens)                 # A1: host plan
         plan_dev = dec.upload_plan(words)              # A2: upload
         ws = dec.workspace(words)
@@ -241,6 +245,22 @@ def main():
     fwd_p = [float(x) for x in np.percentile(fwd_ms, [10, 50, 90])]
 
     plan_info = mla_plan_info(words)
+    # The uniform plan (its split count depends only on the row count, the
+    # longest row and the config) timed the same way, for comparison.
+    uniform = None
+    if plan_info["mode"] != "uniform":
+        dec_u = mla.MlaDecoder(case.heads, case.q_len, case.q_dtype, case.kv_dtype, case.causal,
+                               float(case.sm_scale), mode=mla.PLAN_UNIFORM)
+        for k in range(args.warmup):
+            words_u = step(k, dec=dec_u)
+        evs_u = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        for k in range(args.steps):
+            words_u = step(k, evs_u[k], dec=dec_u)
+        torch.cuda.synchronize()
+        info_u = mla_plan_info(words_u)
+        uniform = {"launch_ms": round(float(np.mean([a.elapsed_time(b) for a, b in evs_u])), 4),
+                   "splits": info_u["S"], "workgroups": info_u["G"]}
     elem = 2 if case.kv_dtype == "bf16" else 1
     keys = int(kv_lens.sum())
     kv_bytes = keys * 576 * elem
@@ -286,6 +306,10 @@ def main():
         "mfma_tflops": round(tflops_step, 2),
         "roofline": roof,
     }
+    if uniform is not None:
+        ach = flops / (uniform["launch_ms"] * 1e-3) / 1e12
+        uniform["mfma_frac"] = round(ach / MFMA_PEAK_TFLOPS[compute_dtype], 4)
+        out["uniform_plan"] = uniform
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -10,10 +10,10 @@ and 15 <= rows <= 32768. The constants and tie-breaks below are this
 library's own choice (spec version 1); the library's C++ planner must produce
 the same int32 words.
 
-Constants: M_UNIT 128 query rows per work item, N_MAX 64 splits per row,
-MIN_SPLIT_KEYS 256, ITEM_OVERHEAD 64, OCC 1 resident work item per compute
-unit (a decode workgroup takes nearly all of a CU's LDS), XCDS 8 (the
-chiplets whose L2 a launch spreads over).
+Constants: M_UNIT 128 query rows per work item, N_MAX 256 splits per row,
+MIN_SPLIT_KEYS 256, ITEM_OVERHEAD 128 (a work item's fixed cost, in keys),
+OCC 1 resident work item per compute unit (a decode workgroup takes nearly
+all of a CU's LDS), XCDS 8 (the chiplets whose L2 a launch spreads over).
 All arithmetic is integer; cdiv(a, b) = (a + b - 1) // b.
 
 Steps:
@@ -22,25 +22,38 @@ Steps:
 2. Mode. AUTO means LENGTH_AWARE iff kv is fp8, H == 128 and
    15 <= R <= 32768 (the persistent gate), else UNIFORM.
 3. UNIFORM: n = clamp(min(cdiv(OCC*C, R*u), cdiv(max L, MIN_SPLIT_KEYS)), 1,
-   N_MAX); every row gets n splits.
-4. LENGTH_AWARE: T = max(MIN_SPLIT_KEYS, cdiv(u * sum L, OCC*C));
-   n_b = clamp(cdiv(L_b, T), 1, N_MAX).
-5. split_indptr is the running sum of n_b. Split k of row b (global id
-   split_indptr[b] + k) covers keys [k*L_b // n_b, (k+1)*L_b // n_b); empty
-   ranges are legal. Splits of rows with n_b > 1 get partial-buffer slots
-   0, 1, 2, ... in split order; the others get -1.
-6. Split cost = (end - begin) + ITEM_OVERHEAD. Splits are ranked by
-   (-cost, split id). Rank k goes to chiplet k mod X, with X = XCDS for
-   UNIFORM and min(XCDS, G) for LENGTH_AWARE. Each chiplet's item list is its
-   splits in rank order, each followed by its M tiles m = 0..u-1.
+   N_MAX); every row gets n splits; split k of row b covers keys
+   [k*L_b // n, (k+1)*L_b // n) (empty ranges are legal).
+4. LENGTH_AWARE cuts the concatenated key ranges of all rows into lanes of
+   equal cost. A lane is u workgroups on one chiplet that run the same splits,
+   one M tile each, so the u tiles of a split read its keys from one L2 at
+   about the same time. X starts at XCDS and halves while (OCC*C) // X < u;
+   n_x = (OCC*C) // X slots per chiplet; lam = max(1, n_x // u) lanes per
+   chiplet; LAMBDA = X * lam lanes. Lane l (chiplet x = l mod X, k = l // X)
+   has members j = 0..u-1, workgroup x + X*(k*u + j).
+   Lane capacity T = max(MIN_SPLIT_KEYS,
+   cdiv(sum L + ITEM_OVERHEAD*(R + LAMBDA), LAMBDA),
+   cdiv(max L, N_MAX - 1) + ITEM_OVERHEAD). A split costs its keys plus
+   ITEM_OVERHEAD. Walk the rows in order with lane l = 0 and cap = T: a row
+   with L_b = 0 gets one empty split [0, 0) in lane l; otherwise, while keys
+   s < L_b remain: if cap <= ITEM_OVERHEAD and l < LAMBDA - 1, move to the
+   next lane (cap = T); the split takes n = L_b - s keys in the last lane,
+   else n = min(L_b - s, cap - ITEM_OVERHEAD); cap -= n + ITEM_OVERHEAD.
+   Split ids follow creation order (rows in order, keys ascending).
+5. split_indptr is the running count of splits per row. Splits of rows with
+   more than one split get partial-buffer slots 0, 1, 2, ... in split order;
+   the others get -1.
+6. UNIFORM: split cost = (end - begin) + ITEM_OVERHEAD. Splits are ranked by
+   (-cost, split id). Rank k goes to chiplet k mod XCDS. Each chiplet's item
+   list is its splits in rank order, each followed by its M tiles
+   m = 0..u-1.
 7. UNIFORM: one item per workgroup, G = W = S*u. Workgroup ids are dealt to
    chiplets round-robin (id mod XCDS), so for j < n_min (the shortest
    chiplet list) workgroup XCDS*j + x runs item j of chiplet x; the remaining
    items, taken by (j, x), fill the ids from XCDS*n_min upward in order.
-8. LENGTH_AWARE: G = min(OCC*C, W) persistent workgroups; workgroup g belongs
-   to chiplet g mod X. Each chiplet's items, in list order, go one by one to
-   that chiplet's workgroup with the least (load, id), load being the sum of
-   its item costs; a workgroup runs its items in the order they came.
+8. LENGTH_AWARE: member j of lane l runs (s, j) for the lane's splits s in
+   order. G = 1 + the largest workgroup id that has an item; the other
+   workgroups below G have none.
 9. Words (int32): a 20-word header [magic 0x4D4C4150, version 1, R, H,
    q_len_max, kv_dtype, C, mode_used (| 0x100 when the caller asked for the
    merge inside the decode kernel), M_UNIT, u, N_MAX, MIN_SPLIT_KEYS,
@@ -51,12 +64,12 @@ Steps:
 import numpy as np
 
 MAGIC = 0x4D4C4150
-VERSION = 1
+VERSION = 2
 HEADER_WORDS = 20
 M_UNIT = 128
-N_MAX = 64
+N_MAX = 256
 MIN_SPLIT_KEYS = 256
-ITEM_OVERHEAD = 64
+ITEM_OVERHEAD = 128
 OCC = 1
 XCDS = 8
 
@@ -97,50 +110,72 @@ def plan_ref(kv_lens, H, q_len_max, kv_dtype, mode, C):
     flag = mode & MERGE_IN_KERNEL
     mode_used = choose_mode(mode & ~MERGE_IN_KERNEL, kv_dtype, H, R)
 
-    # 3-4: split count per row
+    # 3-5: splits (row, key range), partial slots
+    split_row, split_begin, split_end = [], [], []
+    lane_splits = None
     if mode_used == MODE_UNIFORM:
         n = clamp(min(cdiv(OCC * C, R * u), cdiv(max(lens), MIN_SPLIT_KEYS)), 1, N_MAX)
-        nsplit = [n] * R
+        for b, L in enumerate(lens):
+            for k in range(n):
+                split_row.append(b)
+                split_begin.append(k * L // n)
+                split_end.append((k + 1) * L // n)
     else:
-        T = max(MIN_SPLIT_KEYS, cdiv(u * sum(lens), OCC * C))
-        nsplit = [clamp(cdiv(L, T), 1, N_MAX) for L in lens]
-
-    # 5: CSR of splits, key ranges, partial slots
+        X = XCDS
+        while X > 1 and (OCC * C) // X < u:
+            X //= 2
+        lam = max(1, ((OCC * C) // X) // u)
+        n_lanes = X * lam
+        T = max(MIN_SPLIT_KEYS, cdiv(sum(lens) + ITEM_OVERHEAD * (R + n_lanes), n_lanes),
+                cdiv(max(lens), N_MAX - 1) + ITEM_OVERHEAD)
+        lane_splits = [[] for _ in range(n_lanes)]
+        lane, cap = 0, T
+        for b, L in enumerate(lens):
+            if L == 0:
+                lane_splits[lane].append(len(split_row))
+                split_row.append(b)
+                split_begin.append(0)
+                split_end.append(0)
+                continue
+            pos = 0
+            while pos < L:
+                if cap <= ITEM_OVERHEAD and lane < n_lanes - 1:
+                    lane, cap = lane + 1, T
+                take = L - pos if lane == n_lanes - 1 else min(L - pos, cap - ITEM_OVERHEAD)
+                lane_splits[lane].append(len(split_row))
+                split_row.append(b)
+                split_begin.append(pos)
+                split_end.append(pos + take)
+                pos += take
+                cap -= take + ITEM_OVERHEAD
+    S = len(split_row)
+    nsplit = [0] * R
+    for b in split_row:
+        nsplit[b] += 1
     split_indptr = [0]
     for nb in nsplit:
         split_indptr.append(split_indptr[-1] + nb)
-    S = split_indptr[-1]
-    split_row, split_begin, split_end, split_part = [], [], [], []
+    split_part = []
     next_slot = 0
-    for b, (L, nb) in enumerate(zip(lens, nsplit)):
-        for k in range(nb):
-            split_row.append(b)
-            split_begin.append(k * L // nb)
-            split_end.append((k + 1) * L // nb)
-            if nb > 1:
-                split_part.append(next_slot)
-                next_slot += 1
-            else:
-                split_part.append(-1)
+    for s_id in range(S):
+        if nsplit[split_row[s_id]] > 1:
+            split_part.append(next_slot)
+            next_slot += 1
+        else:
+            split_part.append(-1)
     P = next_slot
-
-    # 6: ranking and chiplet lists
     W = S * u
-    cost = [split_end[s] - split_begin[s] + ITEM_OVERHEAD for s in range(S)]
-    ranked = sorted(range(S), key=lambda s: (-cost[s], s))
+
+    # 6-8: work items and workgroups
     if mode_used == MODE_UNIFORM:
         G = W
         X = XCDS
-    else:
-        G = min(OCC * C, W)
-        X = min(XCDS, G)
-    lists = [[] for _ in range(X)]
-    for k, s in enumerate(ranked):
-        for m in range(u):
-            lists[k % X].append((s, m))
-
-    # 7-8: workgroups
-    if mode_used == MODE_UNIFORM:
+        cost = [split_end[s_id] - split_begin[s_id] + ITEM_OVERHEAD for s_id in range(S)]
+        ranked = sorted(range(S), key=lambda s_id: (-cost[s_id], s_id))
+        lists = [[] for _ in range(X)]
+        for k, s_id in enumerate(ranked):
+            for m in range(u):
+                lists[k % X].append((s_id, m))
         order = [None] * W
         n_min = min(len(lst) for lst in lists)
         for x in range(X):
@@ -156,14 +191,14 @@ def plan_ref(kv_lens, H, q_len_max, kv_dtype, mode, C):
         assert nxt == W
         groups = [[it] for it in order]
     else:
-        groups = [[] for _ in range(G)]
-        load = [0] * G
-        for x in range(X):
-            members = [g for g in range(G) if g % X == x]
-            for (s, m) in lists[x]:
-                g = min(members, key=lambda g: (load[g], g))
-                groups[g].append((s, m))
-                load[g] += cost[s]
+        by_wg = {}
+        for lane, splits in enumerate(lane_splits):
+            x, k = lane % X, lane // X
+            for j in range(u):
+                if splits:
+                    by_wg[x + X * (k * u + j)] = [(s_id, j) for s_id in splits]
+        G = 1 + max(by_wg)
+        groups = [by_wg.get(g, []) for g in range(G)]
 
     work_indptr = [0]
     item_split, item_m = [], []

@@ -15,21 +15,31 @@ namespace {
 using namespace dev;
 
 constexpr int kDV = 512;
+constexpr int kMergeLanes = 4;   // splits per lane: n <= 256
 
 // ---------------------------------------------------------------------------
 // Split merge: one block of four waves per (request row b, query token i,
-// heads 4 j .. 4 j + 3) of a row with n > 1 splits (n <= 64). Lane k of a wave
-// reads LSE_k and the wave reduces max and sum. With n <= 8 splits each wave
+// heads 4 j .. 4 j + 3) of a row with n > 1 splits (n <= 256). Lane l of a
+// wave reads LSE_k for k = l + 64 i and the wave reduces max and sum. With n <= 8 splits each wave
 // merges one head, all n partials' loads in flight at once; with more, the
 // four waves take every fourth split of one head at a time and add up in
 // LDS. A lane owns 8 output columns.
-// Weights of the n partials of one (token, head): lane k gets
-// exp(LSE_k - LSE); returns false (and writes O = 0, LSE = -inf) when every
+// Weights of the n partials of one (token, head): lane l gets
+// exp(LSE_k - LSE) for its splits k; returns false (and writes O = 0, LSE = -inf) when every
 // split is empty.
 __device__ __forceinline__ bool merge_weights(const MergeArgs& a, int64_t base, int64_t stride, int n,
-                                              int lane, int64_t orow, float& wk, float& lse, bool writer) {
-  const float lk = lane < n ? a.ws_lse[base + lane * stride] : -INFINITY;
-  const float mx = wave_max(lk);
+                                              int lane, int64_t orow, float (&wk)[kMergeLanes], float& lse,
+                                              bool writer) {
+  // Lane l holds split k = l + 64 i in slot i (up to 256 splits).
+  float lk[kMergeLanes];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kMergeLanes; ++i) {
+    const int k = lane + 64 * i;
+    lk[i] = k < n ? a.ws_lse[base + k * stride] : -INFINITY;
+    mx = fmaxf(mx, lk[i]);
+  }
+  mx = wave_max(mx);
   if (mx == -INFINITY) {
     if (writer) {
       *(u32x4*)(a.o + orow * kDV + lane * 8) = u32x4{0u, 0u, 0u, 0u};
@@ -38,11 +48,24 @@ __device__ __forceinline__ bool merge_weights(const MergeArgs& a, int64_t base, 
     return false;
   }
   const float kLog2e = 1.44269504088896340736f;
-  const float ek = lk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lk - mx) * kLog2e);
-  const float tot = wave_sum(ek);
-  wk = ek / tot;
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMergeLanes; ++i) {
+    wk[i] = lk[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lk[i] - mx) * kLog2e);
+    part += wk[i];
+  }
+  const float tot = wave_sum(part);
+#pragma unroll
+  for (int i = 0; i < kMergeLanes; ++i) wk[i] /= tot;
   lse = mx + __log2f(tot) * kLn2;
   return true;
+}
+
+// Weight of split k (wave-uniform k < 256) from merge_weights' registers.
+__device__ __forceinline__ float weight_of(const float (&wk)[kMergeLanes], int k) {
+  const int i = k >> 6;   // uniform
+  const float v = i == 0 ? wk[0] : i == 1 ? wk[1] : i == 2 ? wk[2] : wk[3];
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), k & 63));
 }
 
 __device__ __forceinline__ void store_row(const MergeArgs& a, int64_t orow, int lane, f32x4 acc0, f32x4 acc1,
@@ -75,7 +98,7 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
     if (h >= a.heads) return;
     const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
     const int64_t orow = (int64_t)(q0 + i) * a.heads + h;
-    float wk, lse;
+    float wk[kMergeLanes], lse;
     if (!merge_weights(a, base, stride, n, lane, orow, wk, lse, true)) return;
     const float* src = a.ws_o + base * kDV + lane * 8;
     f32x4 v[8][2];
@@ -90,7 +113,7 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       if (k < n) {
-        const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), k));
+        const float c = weight_of(wk, k);
         acc0 += c * v[k][0];   // an empty split's partial is 0 and its weight 0
         acc1 += c * v[k][1];
       }
@@ -103,7 +126,7 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
     if (h >= a.heads) break;          // uniform
     const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
     const int64_t orow = (int64_t)(q0 + i) * a.heads + h;
-    float wk, lse;
+    float wk[kMergeLanes], lse;
     if (!merge_weights(a, base, stride, n, lane, orow, wk, lse, w == 0)) continue;   // uniform
     const float* src = a.ws_o + base * kDV + lane * 8;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -122,7 +145,7 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
       for (int u = 0; u < 8; ++u) {
         const int k = k0 + u * kW;
         if (k < n) {
-          const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), k));
+          const float c = weight_of(wk, k);
           acc0 += c * v[u][0];
           acc1 += c * v[u][1];
         }

@@ -8,16 +8,16 @@
 
 namespace mla {
 
-// Plan spec version 1 constants. The decode kernel's tile is compiled for
+// Plan spec version 2 constants. The decode kernel's tile is compiled for
 // kMUnit query rows; the planner writes the same value into every plan header
 // and the launcher refuses a plan whose header differs.
 constexpr int32_t kPlanMagic = 0x4D4C4150;
-constexpr int32_t kPlanVersion = 1;
+constexpr int32_t kPlanVersion = 2;
 constexpr int32_t kHeaderWords = 20;
 constexpr int32_t kMUnit = 128;
-constexpr int32_t kNMax = 64;
+constexpr int32_t kNMax = 256;
 constexpr int32_t kMinSplitKeys = 256;
-constexpr int32_t kItemOverhead = 64;
+constexpr int32_t kItemOverhead = 128;
 constexpr int32_t kOcc = 1;
 constexpr int32_t kXcds = 8;
 

@@ -1,4 +1,4 @@
-// Host split planner (plan spec version 1).
+// Host split planner (plan spec version 2).
 //
 // A plan is a split count and split_indptr per request row, built on the host
 // next to the decode CSR ([DSV4] Tuned ASM FP8 decode with split plans, ATOM
@@ -8,14 +8,15 @@
 // lengths on every call, as the persistent decode kernel of the same page does
 // (Summary part 2), whose gate (fp8 KV, 128 heads, 15..32768 rows) AUTO uses.
 //
-// On top of the splits the plan fixes the launch: work items are (split, tile
-// of 64 query rows); splits are ranked longest first and dealt to the eight
-// chiplets (XCDs), so that all M tiles of one split -- which read the same
-// keys -- run on one chiplet and share its L2. UNIFORM launches one workgroup
+// On top of the splits the plan fixes the launch. Work items are (split,
+// tile of 128 query rows); all M tiles of one split read the same keys, so
+// they run on one chiplet (XCD) and share its L2. UNIFORM ranks splits
+// longest first, deals them to the eight chiplets and launches one workgroup
 // per item, ordering workgroup ids so that the hardware's round-robin
-// dispatch over chiplets lands each chiplet's items on it; LENGTH_AWARE
-// launches min(2 x CUs, items) persistent workgroups and gives each chiplet's
-// items to its least-loaded workgroup.
+// dispatch over chiplets lands each chiplet's items on it. LENGTH_AWARE cuts
+// the concatenated key ranges of all rows into lanes of equal cost -- a lane
+// being u workgroups of one chiplet that run the same splits, one M tile
+// each -- and launches those workgroups persistently.
 #include <algorithm>
 #include <cstring>
 #include <numeric>
@@ -65,8 +66,8 @@ int32_t view_plan(const int32_t* plan, PlanView* v) {
   v->off_item_split = off; off += v->W;
   v->off_item_m = off; off += v->W;
   if (off != v->total) return set_error(MLA_ERR_PLAN_MISMATCH, "plan length mismatch");
-  // The merge kernel takes one split per lane of a wave: at most N_MAX = 64
-  // splits per row, and split_indptr must run from 0 to S.
+  // The merge kernel takes up to four splits per lane of a wave: at most
+  // N_MAX = 256 splits per row, and split_indptr must run from 0 to S.
   if (plan[H_NMAX] != kNMax || plan[v->off_split_indptr] != 0 ||
       plan[v->off_split_indptr + v->rows] != v->S)
     return set_error(MLA_ERR_PLAN_MISMATCH, "plan split_indptr is inconsistent");
@@ -74,7 +75,7 @@ int32_t view_plan(const int32_t* plan, PlanView* v) {
   for (int32_t b = 0; b < v->rows; ++b) {
     const int32_t n = plan[v->off_split_indptr + b + 1] - plan[v->off_split_indptr + b];
     if (n < 1 || n > kNMax)
-      return set_error(MLA_ERR_PLAN_MISMATCH, "plan has a row with no split or more than 64");
+      return set_error(MLA_ERR_PLAN_MISMATCH, "plan has a row with no split or more than 256");
     v->max_splits = n > v->max_splits ? n : v->max_splits;
   }
   return MLA_OK;
@@ -92,10 +93,12 @@ extern "C" int32_t mla_decode_plan_capacity(int32_t rows, int32_t num_cus, int32
   if (num_heads < 1 || num_heads > MLA_MAX_HEADS || q_len_max < 1 || q_len_max > MLA_MAX_Q_LEN)
     return set_error(MLA_ERR_UNSUPPORTED, "heads must be 1..128 and q_len_max 1..16");
   const int64_t u = cdiv((int64_t)num_heads * q_len_max, kMUnit);
-  // UNIFORM: S <= rows * N_MAX; LENGTH_AWARE: S <= rows + OCC * CUs.
+  // UNIFORM: S <= rows * N_MAX and G = W; LENGTH_AWARE: S <= rows + lanes - 1
+  // <= rows + OCC * CUs and G <= max(OCC * CUs, u).
   const int64_t s_max = std::max<int64_t>((int64_t)rows * kNMax, (int64_t)rows + (int64_t)kOcc * num_cus);
   const int64_t w_max = s_max * u;
-  *words_out = kHeaderWords + (rows + 1) + 4 * s_max + (w_max + 1) + 2 * w_max;
+  const int64_t g_max = std::max<int64_t>(w_max, std::max<int64_t>((int64_t)kOcc * num_cus, u));
+  *words_out = kHeaderWords + (rows + 1) + 4 * s_max + (g_max + 1) + 2 * w_max;
   return MLA_OK;
 }
 
@@ -132,55 +135,91 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
                ? MLA_PLAN_LENGTH_AWARE
                : MLA_PLAN_UNIFORM;
 
-  // Split counts.
-  std::vector<int32_t> nsplit(rows);
+  // Splits: (row, key range), in creation order.
+  std::vector<int32_t> srow, sbeg, send;
+  std::vector<std::vector<int32_t>> lane_splits;   // LENGTH_AWARE
+  int32_t X = kXcds;
   if (used == MLA_PLAN_UNIFORM) {
     int64_t n = std::min(cdiv((int64_t)kOcc * num_cus, (int64_t)rows * u), cdiv(max_len, kMinSplitKeys));
     n = std::clamp<int64_t>(n, 1, kNMax);
-    std::fill(nsplit.begin(), nsplit.end(), (int32_t)n);
-  } else {
-    const int64_t T = std::max<int64_t>(kMinSplitKeys, cdiv(u * sum_len, (int64_t)kOcc * num_cus));
+    if ((int64_t)rows * n > INT32_MAX) return set_error(MLA_ERR_UNSUPPORTED, "too many splits");
+    srow.reserve(rows * n);
     for (int32_t b = 0; b < rows; ++b)
-      nsplit[b] = (int32_t)std::clamp<int64_t>(cdiv(kv_lens[b], T), 1, kNMax);
-  }
-
-  // Split CSR, key ranges, partial slots.
-  std::vector<int32_t> split_indptr(rows + 1, 0);
-  for (int32_t b = 0; b < rows; ++b) split_indptr[b + 1] = split_indptr[b] + nsplit[b];
-  const int32_t S = split_indptr[rows];
-  std::vector<int32_t> srow(S), sbeg(S), send(S), spart(S);
-  int32_t P = 0;
-  for (int32_t b = 0; b < rows; ++b) {
-    const int64_t L = kv_lens[b], n = nsplit[b];
-    for (int64_t k = 0; k < n; ++k) {
-      const int32_t s = split_indptr[b] + (int32_t)k;
-      srow[s] = b;
-      sbeg[s] = (int32_t)(k * L / n);
-      send[s] = (int32_t)((k + 1) * L / n);
-      spart[s] = n > 1 ? P++ : -1;
+      for (int64_t k = 0; k < n; ++k) {
+        srow.push_back(b);
+        sbeg.push_back((int32_t)(k * kv_lens[b] / n));
+        send.push_back((int32_t)((k + 1) * kv_lens[b] / n));
+      }
+  } else {
+    // Lanes: u workgroups of one chiplet that run the same splits, one M
+    // tile each; the concatenated key ranges of all rows are cut into lanes
+    // of equal cost (keys + kItemOverhead per split).
+    const int64_t slots = (int64_t)kOcc * num_cus;
+    while (X > 1 && slots / X < u) X /= 2;
+    const int64_t lam = std::max<int64_t>(1, (slots / X) / u);
+    const int64_t n_lanes = X * lam;
+    const int64_t T = std::max({(int64_t)kMinSplitKeys,
+                                cdiv(sum_len + (int64_t)kItemOverhead * (rows + n_lanes), n_lanes),
+                                cdiv(max_len, kNMax - 1) + kItemOverhead});
+    lane_splits.resize(n_lanes);
+    int64_t lane = 0, cap = T;
+    for (int32_t b = 0; b < rows; ++b) {
+      const int64_t L = kv_lens[b];
+      if (L == 0) {
+        lane_splits[lane].push_back((int32_t)srow.size());
+        srow.push_back(b);
+        sbeg.push_back(0);
+        send.push_back(0);
+        continue;
+      }
+      for (int64_t pos = 0; pos < L;) {
+        if (cap <= kItemOverhead && lane < n_lanes - 1) {
+          ++lane;
+          cap = T;
+        }
+        const int64_t take = lane == n_lanes - 1 ? L - pos : std::min(L - pos, cap - kItemOverhead);
+        lane_splits[lane].push_back((int32_t)srow.size());
+        srow.push_back(b);
+        sbeg.push_back((int32_t)pos);
+        send.push_back((int32_t)(pos + take));
+        pos += take;
+        cap -= take + kItemOverhead;
+      }
     }
   }
+  const int32_t S = (int32_t)srow.size();
 
-  // Rank splits longest first and deal them to chiplets.
+  // Split CSR and partial slots.
+  std::vector<int32_t> split_indptr(rows + 1, 0);
+  for (int32_t s = 0; s < S; ++s) ++split_indptr[srow[s] + 1];
+  for (int32_t b = 0; b < rows; ++b) split_indptr[b + 1] += split_indptr[b];
+  std::vector<int32_t> spart(S);
+  int32_t P = 0;
+  for (int32_t s = 0; s < S; ++s)
+    spart[s] = split_indptr[srow[s] + 1] - split_indptr[srow[s]] > 1 ? P++ : -1;
+
   const int64_t W64 = (int64_t)S * u;
   if (W64 > INT32_MAX) return set_error(MLA_ERR_UNSUPPORTED, "too many work items");
   const int32_t W = (int32_t)W64;
-  const int32_t G = used == MLA_PLAN_UNIFORM ? W : (int32_t)std::min<int64_t>((int64_t)kOcc * num_cus, W);
-  const int32_t X = used == MLA_PLAN_UNIFORM ? kXcds : std::min(kXcds, G);
-  std::vector<int64_t> cost(S);
-  for (int32_t s = 0; s < S; ++s) cost[s] = (int64_t)send[s] - sbeg[s] + kItemOverhead;
-  std::vector<int32_t> rank(S);
-  std::iota(rank.begin(), rank.end(), 0);
-  std::stable_sort(rank.begin(), rank.end(), [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
-  std::vector<std::vector<Item>> chiplet(X);
-  for (int32_t k = 0; k < S; ++k)
-    for (int32_t m = 0; m < (int32_t)u; ++m) chiplet[k % X].push_back({rank[k], m});
 
   // Workgroups.
-  std::vector<int32_t> work_indptr(G + 1, 0);
+  int32_t G = 0;
+  std::vector<int32_t> work_indptr;
   std::vector<Item> items;
   items.reserve(W);
   if (used == MLA_PLAN_UNIFORM) {
+    // Rank splits longest first and deal them to chiplets; workgroup ids are
+    // ordered so that the hardware's round-robin dispatch over chiplets lands
+    // each chiplet's items on it.
+    G = W;
+    std::vector<int64_t> cost(S);
+    for (int32_t s = 0; s < S; ++s) cost[s] = (int64_t)send[s] - sbeg[s] + kItemOverhead;
+    std::vector<int32_t> rank(S);
+    std::iota(rank.begin(), rank.end(), 0);
+    std::stable_sort(rank.begin(), rank.end(), [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+    std::vector<std::vector<Item>> chiplet(X);
+    for (int32_t k = 0; k < S; ++k)
+      for (int32_t m = 0; m < (int32_t)u; ++m) chiplet[k % X].push_back({rank[k], m});
     std::vector<Item> by_id(W);
     size_t n_min = SIZE_MAX, n_max = 0;
     for (auto& c : chiplet) { n_min = std::min(n_min, c.size()); n_max = std::max(n_max, c.size()); }
@@ -191,21 +230,30 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
       for (int32_t x = 0; x < X; ++x)
         if (j < chiplet[x].size()) by_id[next++] = chiplet[x][j];
     items = by_id;
+    work_indptr.resize(G + 1);
     for (int32_t g = 0; g <= G; ++g) work_indptr[g] = g;
   } else {
-    std::vector<std::vector<Item>> groups(G);
-    std::vector<int64_t> load(G, 0);
-    for (int32_t x = 0; x < X; ++x) {
-      for (const Item& it : chiplet[x]) {
-        int32_t best = -1;
-        for (int32_t g = x; g < G; g += X)   // workgroups of chiplet x
-          if (best < 0 || load[g] < load[best]) best = g;
-        groups[best].push_back(it);
-        load[best] += cost[it.split];
+    // Member j of lane l (chiplet x = l mod X, k = l / X) is workgroup
+    // x + X (k u + j) and runs (s, j) for the lane's splits s in order.
+    std::vector<int32_t> lane_of_wg, member_of_wg;
+    for (int64_t l = 0; l < (int64_t)lane_splits.size(); ++l) {
+      if (lane_splits[l].empty()) continue;
+      const int64_t x = l % X, k = l / X;
+      for (int64_t j = 0; j < u; ++j) {
+        const int64_t g = x + X * (k * u + j);
+        if (g >= (int64_t)lane_of_wg.size()) {
+          lane_of_wg.resize(g + 1, -1);
+          member_of_wg.resize(g + 1, -1);
+        }
+        lane_of_wg[g] = (int32_t)l;
+        member_of_wg[g] = (int32_t)j;
       }
     }
+    G = (int32_t)lane_of_wg.size();
+    work_indptr.assign(G + 1, 0);
     for (int32_t g = 0; g < G; ++g) {
-      items.insert(items.end(), groups[g].begin(), groups[g].end());
+      if (lane_of_wg[g] >= 0)
+        for (int32_t s : lane_splits[lane_of_wg[g]]) items.push_back({s, member_of_wg[g]});
       work_indptr[g + 1] = (int32_t)items.size();
     }
   }

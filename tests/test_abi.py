@@ -100,7 +100,7 @@ def test_fwd_plan_corruption(lib):
     p[0] ^= 1
     assert call_fwd(lib, fwd_args(plan=p)) == MISMATCH
     p = good_plan().copy()
-    p[1] = 2
+    p[1] += 1      # another plan spec version
     assert call_fwd(lib, fwd_args(plan=p)) == MISMATCH
     p = good_plan().copy()
     p[8] = 32      # M_UNIT the kernel was not compiled for

@@ -115,6 +115,8 @@ SMALL = [
     (128, 8, BF16, BF16, True, [2048, 100], 1, 256),
     (128, 16, BF16, BF16, True, [3, 20, 5000], 1, 16),               # q_len > L for row 0
     (7, 9, BF16, FP8, True, [1, 0, 9], 1, 2),                        # heads not a multiple of 16
+    (16, 1, BF16, BF16, True, [40000], 1, 256),                      # uniform, 157 splits in one row
+    (16, 1, BF16, FP8, False, [60000, 100], 2, 256),                 # lanes: about 250 splits in one row
 ]
 
 

@@ -8,7 +8,7 @@ import pytest
 from oracle.attention import attend_case
 from oracle.merge import merge_partials, split_attend
 from oracle.plan import (plan_ref, unpack_plan, MODE_AUTO, MODE_UNIFORM, MODE_LENGTH_AWARE,
-                         KV_BF16, KV_FP8, N_MAX, OCC, XCDS, M_UNIT)
+                         KV_BF16, KV_FP8, N_MAX, OCC, XCDS, M_UNIT, ITEM_OVERHEAD)
 from workloads import make_case, config_lengths, CONFIGS, BF16, FP8
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -101,8 +101,29 @@ def check_invariants(lens, H, q_len, kv_dtype, mode, C):
         assert G == W and len(set(nsplit)) == 1
         assert S <= R * N_MAX
     else:
-        assert G == min(OCC * C, W)
+        assert G <= max(OCC * C, u)
         assert S <= R + OCC * C
+        # lanes: u workgroups of one chiplet run the same consecutive splits,
+        # member j taking M tile j; lanes follow each other in split order
+        X = XCDS
+        while X > 1 and (OCC * C) // X < u:
+            X //= 2
+        lanes = {}
+        for g in range(G):
+            its = items[wi[g]:wi[g + 1]]
+            if not its:
+                continue
+            ms = {m for _, m in its}
+            assert len(ms) == 1
+            seq = tuple(s for s, _ in its)
+            assert list(seq) == list(range(seq[0], seq[0] + len(seq)))
+            lanes.setdefault(seq, []).append((g, ms.pop()))
+        firsts = sorted(seq[0] for seq in lanes)
+        assert firsts[0] == 0
+        for seq, members in lanes.items():
+            assert sorted(m for _, m in members) == list(range(u))
+            assert len({g % X for g, _ in members}) == 1
+        assert sum(len(seq) for seq in lanes) == S
     return d
 
 
@@ -142,3 +163,19 @@ def test_auto_mode_on_the_five_workloads():
         assert d["mode"] == mode, name
         if n is not None:
             assert d["S"] == n * len(lens), name
+
+
+@pytest.mark.parametrize("name", ["verify_causal", "draft_noncausal", "longctx_split",
+                                  "ragged_persistent_causal", "sparse_topk"])
+def test_length_aware_lanes_are_balanced(name):
+    """On the workload shapes with 256 CUs, every workgroup gets work and the
+    busiest one's cost (keys + ITEM_OVERHEAD per split) is within 6% of the
+    mean: the plan cuts the rows' concatenated keys into equal lanes."""
+    spec = CONFIGS[name]
+    lens = [int(x) for x in config_lengths(name)]
+    d = check_invariants(lens, spec["heads"], spec["q_len"], KV_FP8, MODE_LENGTH_AWARE, 256)
+    wi, its = d["work_indptr"], d["item_split"]
+    costs = [sum(d["split_end"][s] - d["split_begin"][s] + ITEM_OVERHEAD for s in its[wi[g]:wi[g + 1]])
+             for g in range(d["G"])]
+    assert d["G"] == 256 and min(costs) > 0
+    assert max(costs) <= 1.06 * (sum(costs) / len(costs))
