@@ -90,7 +90,10 @@ constexpr int kMainBytes = kNT * kMainRow;    // 32768
 constexpr int kRopeBytes = kNT * kRopeRow;    // 4096
 constexpr int kF8MainRow = 512, kF8RopeRow = 64;
 constexpr int kF8MainBytes = kNT * kF8MainRow;        // 16384
-constexpr int kF8TileBytes = kF8MainBytes + kNT * kF8RopeRow;  // 18432
+// fp8 rope: each wave's 8 rows (512 bytes) sit at the start of a 1 KB slot;
+// its load runs on all 64 lanes (lanes 32-63 repeat lanes 0-31's sources
+// into the slot's second half), so no lane mask splits the pipeline code.
+constexpr int kF8RopeBytes = (kDecodeThreads / 64) * 1024;   // 4096
 constexpr int kKSteps = kDLat / 16;           // 36 QK k-steps (32 main + 4 rope)
 constexpr int kWaves = kDecodeThreads / 64;   // 4
 constexpr int kRows = 128;                    // query rows per work item
@@ -102,10 +105,10 @@ constexpr int kPBytes = kRowBlocks * 2 * 64 * 16;     // P^T of one tile: [4 row
 // bf16 KV: main tiles t-1 (PV), t (QK), t+1, t+2 (loads in flight) and rope
 // tiles t, t+1, t+2. fp8 KV: fp8 staging tiles t, t+1, t+2, bf16 main tiles
 // t-1, t and rope tiles t-1, t.
-constexpr int kBf16MainBufs = 4, kBf16RopeBufs = 3, kF8StageBufs = 3;
+constexpr int kMainBufs = 4, kRopeBufs = 3;
 constexpr int kTilesEnd = 143360;             // end of the tile region for either KV dtype
-static_assert(kBf16MainBufs * kMainBytes + kBf16RopeBufs * kRopeBytes <= kTilesEnd, "bf16 tiles");
-static_assert(kF8StageBufs * kF8TileBytes + 2 * kMainBytes + 2 * kRopeBytes <= kTilesEnd, "fp8 tiles");
+static_assert(kMainBufs * kMainBytes + kRopeBufs * kRopeBytes <= kTilesEnd, "bf16 tiles");
+static_assert(kMainBufs * kF8MainBytes + kRopeBufs * kF8RopeBytes <= kTilesEnd, "fp8 tiles");
 constexpr int kOffP = kTilesEnd;                      // [2] P^T buffers (tiles of even / odd index)
 constexpr int kOffL = kOffP + 2 * kPBytes;            // [128] f32 row sums (epilogue)
 constexpr int kOffSlots = kOffL + kRows * 4;          // [4 waves][4][32] int32
@@ -121,19 +124,25 @@ static_assert(64 * kDV * 4 <= kTilesEnd, "epilogue staging of 64 fp32 rows");
 template <bool KV_FP8> struct Layout;
 template <> struct Layout<false> {
   static __device__ __forceinline__ int main(int t) { return (t & 3) * kMainBytes; }
-  static __device__ __forceinline__ int rope(int t) { return kBf16MainBufs * kMainBytes + (t % 3) * kRopeBytes; }
+  static __device__ __forceinline__ int rope(int t) { return kMainBufs * kMainBytes + (t % 3) * kRopeBytes; }
 };
 template <> struct Layout<true> {
-  static __device__ __forceinline__ int stage(int t) { return (t % 3) * kF8TileBytes; }
-  static __device__ __forceinline__ int main(int t) { return kF8StageBufs * kF8TileBytes + (t & 1) * kMainBytes; }
-  static __device__ __forceinline__ int rope(int t) {
-    return kF8StageBufs * kF8TileBytes + 2 * kMainBytes + (t & 1) * kRopeBytes;
-  }
+  static __device__ __forceinline__ int main(int t) { return (t & 3) * kF8MainBytes; }
+  static __device__ __forceinline__ int rope(int t) { return kMainBufs * kF8MainBytes + (t % 3) * kF8RopeBytes; }
 };
 __device__ __forceinline__ int p_buf(int t) { return kOffP + (t & 1) * kPBytes; }
 
 __device__ __forceinline__ int swz_main(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int swz_rope(int row) { return (row >> 1) & 7; }
+// fp8 tiles: main rows are 512 bytes (32 chunks), rope rows 64 bytes (4
+// chunks). swz_f8 is a bijection on 0..15 (a K read of 16 keys covers all
+// banks) whose value >> 1 differs across the 8 keys of one transposed V read
+// (4g..4g+3 and 8+4g..8+4g+3 of a 16-key half), so those 8 keys' two chunks
+// land in 16 different chunk slots.
+__device__ __forceinline__ int swz_f8(int row) {
+  return ((row & 3) << 2) | (((row >> 3) & 1) << 1) | ((row >> 2) & 1);
+}
+__device__ __forceinline__ int swz_f8_rope(int row) { return (row >> 2) & 3; }
 
 // ---------------------------------------------------------------------------
 // Tile loader (shared by the decode kernel and the gather test hook).
@@ -145,8 +154,8 @@ __device__ __forceinline__ int swz_rope(int row) { return (row >> 1) & 7; }
 //         its slot wave-uniform); op 8 loads rope rows 8w .. 8w+7, 8 lanes
 //         per row.
 //   fp8:  op i < 4 loads main rows 2k, 2k + 1 for k = 4 i + w (two 512-byte
-//         rows per instruction) into the linear staging tile; op 4 loads rope
-//         rows 8w .. 8w+7, 4 lanes per row.
+//         rows per instruction); op 4 loads rope rows 8w .. 8w+7, 4 lanes per
+//         row, into the wave's 1 KB rope slot.
 template <bool KV_FP8> struct TileDma {
   static constexpr int kMainOps = (KV_FP8 ? 16 : 32) / kWaves;
   static constexpr int n = kMainOps + 1;
@@ -169,19 +178,18 @@ template <bool KV_FP8> struct TileDma {
         dma16_vaddr(src, lds0 + rope_off + w * kRopeRows * kRopeRow);
       }
     } else {
-      const uint32_t stage = lds0 + main_off;   // staging tile: main then rope
       if (i < kMainOps) {
         const int k = kWaves * i + w;            // rows 2k (lanes 0-31) and 2k + 1
-        const int slot = __shfl(slot_lane, 2 * k + (lane >> 5), 64);
-        dma16_vaddr(kv + (int64_t)slot * kDLat + ((lane & 31) << 4), stage + k * 1024);
+        const int row = 2 * k + (lane >> 5);
+        const int slot = __shfl(slot_lane, row, 64);
+        dma16_vaddr(kv + (int64_t)slot * kDLat + (((lane & 31) ^ swz_f8(row)) << 4),
+                    lds0 + main_off + k * 2 * kF8MainRow);
       } else {
-        const int j = kRopeRows * w + (lane >> 2);
-        const int slot = __shfl(slot_lane, j & 31, 64);
-        const unsigned char* src = kv + (int64_t)slot * kDLat + kF8MainRow + ((lane & 3) << 4);
-        if (lane < 4 * kRopeRows)
-          dma16_vaddr(src, stage + kF8MainBytes + w * kRopeRows * kF8RopeRow);
+        const int j = kRopeRows * w + ((lane & 31) >> 2);
+        const int slot = __shfl(slot_lane, j, 64);
+        dma16_vaddr(kv + (int64_t)slot * kDLat + kF8MainRow + (((lane & 3) ^ swz_f8_rope(j)) << 4),
+                    lds0 + rope_off + w * 1024);
       }
-      (void)rope_off;
     }
   }
 
@@ -194,16 +202,9 @@ template <bool KV_FP8> struct TileDma {
   }
 };
 
-// LDS offsets a tile's loads target: bf16 tiles are loaded in place, fp8 tiles
-// into their staging tile.
-template <bool KV_FP8> __device__ __forceinline__ int dma_main(int t) {
-  if constexpr (KV_FP8) return Layout<true>::stage(t);
-  else return Layout<false>::main(t);
-}
-template <bool KV_FP8> __device__ __forceinline__ int dma_rope(int t) {
-  if constexpr (KV_FP8) return 0;
-  else return Layout<false>::rope(t);
-}
+// LDS offsets a tile's loads target.
+template <bool KV_FP8> __device__ __forceinline__ int dma_main(int t) { return Layout<KV_FP8>::main(t); }
+template <bool KV_FP8> __device__ __forceinline__ int dma_rope(int t) { return Layout<KV_FP8>::rope(t); }
 
 // DMA the slot list of tile `tile` (32 int32, keys clamped to the split) into
 // this wave's private ring entry (one load, lanes 0-31).
@@ -230,31 +231,6 @@ __device__ __forceinline__ int load_tile_slot(const int32_t* kv_indices, int kv0
   return kv_indices[kv0 + key];
 }
 
-// fp8 staging tile -> swizzled bf16 tile (256 threads): a 16-byte fp8 chunk
-// becomes two bf16 chunks.
-__device__ __forceinline__ void convert_tile(lds_u8* smem, int stage, int main_off, int rope_off,
-                                             int tid) {
-#pragma unroll
-  for (int i = 0; i < 1024 / kDecodeThreads; ++i) {
-    const int p = i * kDecodeThreads + tid;
-    const int row = p >> 5, c = p & 31;
-    const u32x4 w = lds_load<u32x4>(smem, stage + row * kF8MainRow + c * 16);
-    const int base = main_off + row * kMainRow;
-    lds_store(smem, base + (((2 * c) ^ swz_main(row)) << 4),
-              cat(fp8x4_to_bf16(w[0]), fp8x4_to_bf16(w[1])));
-    lds_store(smem, base + (((2 * c + 1) ^ swz_main(row)) << 4),
-              cat(fp8x4_to_bf16(w[2]), fp8x4_to_bf16(w[3])));
-  }
-  if (tid < 128) {
-    const int row = tid >> 2, c = tid & 3;
-    const u32x4 w = lds_load<u32x4>(smem, stage + kF8MainBytes + row * kF8RopeRow + c * 16);
-    const int base = rope_off + row * kRopeRow;
-    lds_store(smem, base + (((2 * c) ^ swz_rope(row)) << 4),
-              cat(fp8x4_to_bf16(w[0]), fp8x4_to_bf16(w[1])));
-    lds_store(smem, base + (((2 * c + 1) ^ swz_rope(row)) << 4),
-              cat(fp8x4_to_bf16(w[2]), fp8x4_to_bf16(w[3])));
-  }
-}
 
 // ---------------------------------------------------------------------------
 // QK MFMAs. They go through inline assembly so that their accumulators are
@@ -297,22 +273,50 @@ __device__ __forceinline__ void mfma_qk_last(f32x16& d, bf16x8 a, bf16x8 b) {
 //   16 w + 4 (ct ^ r) + (c0 ^ (2 q + g)) with r = li >> 2: the four keys of a
 //   half-wave's read sit in the four different 64-byte bank sectors, and its
 //   32 lanes cover all 64 banks once.
+//
+// fp8 tiles (the decode converts in registers, exactly):
+//   K: the QK k-steps are taken in pairs; pair j covers dims 32 j .. 32 j + 31
+//   and lane l reads 16 bytes, dims 32 j + 16 h .. +15 (h = l >> 5), of key
+//   i = l & 31: the first 8 are its elements of k-step 2 j, the last 8 of
+//   k-step 2 j + 1 (Q is loaded in the same order). Main chunk 2 j + h of
+//   row i is stored at (2 j) ^ xm, xm = h ^ swz_f8(i); rope chunk
+//   2 (j - 16) + h at (2 (j - 16)) ^ xr, xr = h ^ swz_f8_rope(i), rope row i
+//   at (i / 8) 1024 + (i % 8) 64.
+//   V^T: one transposed 8-bit read per fragment (ds_read_b64_tr_b8: in a
+//   16-lane block, source lane s gives row s / 2 and bytes 8 (s & 1) .. +7 of
+//   the block's 16 columns; result lane c gets column c of the 8 rows). Block
+//   b = (l >> 4) & 3 takes columns 16 (b & 1) .. +15 of the column tile and
+//   the lane-half-g keys (g = b >> 1), row r = s / 2 being key 4 g + r
+//   (r < 4) or 8 + 4 g + r - 4: the key order of the P^T fragments. Column
+//   chunk 8 w + 2 ct + (b & 1) of key k is stored at that ^ swz_f8(k), so
+//   va = k 512 + 256 (w >> 1) + 16 ((8 (w & 1) + (b & 1)) ^ swz_f8(k)) +
+//   8 (s & 1), and column tile ct flips bits 5-6.
 struct LaneAddr {
   int krow, xm, rrow, xr;   // K
-  int va;                   // V: kb * 1024 + 256 w + 64 r + 16 (c0 ^ g) + 8 (li & 1)
+  int va;                   // V: bf16 kb * 1024 + 256 w + 64 r + 16 (c0 ^ g) + 8 (li & 1); fp8 as above
   int pl;                   // P: lane * 16
   int w;
 };
-__device__ __forceinline__ LaneAddr lane_addr(int lane, int w) {
+template <bool KV_FP8> __device__ __forceinline__ LaneAddr lane_addr(int lane, int w) {
   LaneAddr a;
   const int i = lane & 31, h = lane >> 5;
-  a.krow = i * kMainRow;
-  a.xm = h ^ swz_main(i);
-  a.rrow = i * kRopeRow;
-  a.xr = h ^ swz_rope(i);
-  const int li = lane & 15, g16 = (lane >> 4) & 1, g = lane >> 5;
-  const int kb = 4 * g + (li >> 2), c0 = 2 * g16 + ((li & 3) >> 1);
-  a.va = kb * kMainRow + 256 * w + 64 * (li >> 2) + 16 * (c0 ^ g) + 8 * (li & 1);
+  if constexpr (!KV_FP8) {
+    a.krow = i * kMainRow;
+    a.xm = h ^ swz_main(i);
+    a.rrow = i * kRopeRow;
+    a.xr = h ^ swz_rope(i);
+    const int li = lane & 15, g16 = (lane >> 4) & 1, g = lane >> 5;
+    const int kb = 4 * g + (li >> 2), c0 = 2 * g16 + ((li & 3) >> 1);
+    a.va = kb * kMainRow + 256 * w + 64 * (li >> 2) + 16 * (c0 ^ g) + 8 * (li & 1);
+  } else {
+    a.krow = i * kF8MainRow;
+    a.xm = h ^ swz_f8(i);
+    a.rrow = (i >> 3) * 1024 + (i & 7) * kF8RopeRow;
+    a.xr = h ^ swz_f8_rope(i);
+    const int sl = lane & 15, b1 = (lane >> 4) & 1, g = lane >> 5, r = sl >> 1;
+    const int key = r < 4 ? 4 * g + r : 8 + 4 * g + (r - 4);
+    a.va = key * kF8MainRow + 256 * (w >> 1) + 16 * ((8 * (w & 1) + b1) ^ swz_f8(key)) + 8 * (sl & 1);
+  }
   a.pl = lane * 16;
   a.w = w;
   return a;
@@ -322,6 +326,23 @@ __device__ __forceinline__ bf16x8 k_frag(const lds_u8* smem, const LaneAddr& la,
   if (ks < 32)
     return lds_load<bf16x8>(smem, kmain + la.krow + (ks >> 3) * 256 + (((2 * (ks & 7)) ^ la.xm) << 4));
   return lds_load<bf16x8>(smem, krope + la.rrow + (((2 * (ks - 32)) ^ la.xr) << 4));
+}
+
+// fp8 K pair j (k-steps 2 j and 2 j + 1), 16 bytes.
+__device__ __forceinline__ u32x4 k_pair_f8(const lds_u8* smem, const LaneAddr& la, int kmain, int krope, int j) {
+  if (j < 16) return lds_load<u32x4>(smem, kmain + la.krow + (((2 * j) ^ la.xm) << 4));
+  return lds_load<u32x4>(smem, krope + la.rrow + (((2 * (j - 16)) ^ la.xr) << 4));
+}
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  return cat(fp8x4_to_bf16(lo), fp8x4_to_bf16(hi));
+}
+
+// fp8 V^T fragment (kk, ct): one transposed 8-byte read, converted.
+__device__ __forceinline__ bf16x8 v_frag_f8(const lds_u8* smem, const LaneAddr& la, int vmain, int kk, int ct) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2*)(smem + vmain + 16 * kF8MainRow * kk + (la.va ^ (ct << 5))));
+  return fp8x8_to_bf16((uint32_t)v[0], (uint32_t)v[1]);
 }
 
 // V^T fragment for PV MFMAs (kk, ct): two transposed 8-byte reads. The XOR
@@ -448,11 +469,15 @@ __device__ __forceinline__ void merge_tile(const DecodeArgs& a, int m, int M, in
 // ct = (p / 4) % 4, row block rb = p % 4. Each V^T fragment feeds four
 // products and is read four products ahead; the key-half-1 P^T fragment of a
 // row block replaces key half 0's after its last use.
+template <bool KV_FP8>
 __device__ __forceinline__ void pv_product(const lds_u8* smem, const LaneAddr& la, int vmain, int pbuf, int p,
                                            bf16x8 (&vb)[2], bf16x8 (&pb)[kRowBlocks],
                                            f32x16 (&oacc)[kRowBlocks][kColTiles]) {
   const int kk = p >> 4, ct = (p >> 2) & 3, rb = p & 3;
-  if (rb == 0 && p + 4 < 32) vb[((p >> 2) + 1) & 1] = v_frag(smem, la, vmain, (p + 4) >> 4, ((p + 4) >> 2) & 3);
+  if (rb == 0 && p + 4 < 32) {
+    if constexpr (KV_FP8) vb[((p >> 2) + 1) & 1] = v_frag_f8(smem, la, vmain, (p + 4) >> 4, ((p + 4) >> 2) & 3);
+    else vb[((p >> 2) + 1) & 1] = v_frag(smem, la, vmain, (p + 4) >> 4, ((p + 4) >> 2) & 3);
+  }
   oacc[rb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[(p >> 2) & 1], pb[rb], oacc[rb][ct], 0, 0, 0);
   if (kk == 0 && ct == 3) pb[rb] = p_frag(smem, la, pbuf, rb, 1);
 }
@@ -465,36 +490,63 @@ __device__ __forceinline__ void pv_product(const lds_u8* smem, const LaneAddr& l
 // keeps this order; K fragments are read kKDepth products ahead.
 constexpr int kKDepth = 5;
 constexpr int kPvEarly = 20;
-template <bool QK, bool PV, int NDMA, typename Dma>
+template <bool QK, bool PV, int NDMA, bool KV_FP8, typename Dma>
 __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, const bf16x8 (&qf)[kKSteps],
                                               int kmain, int krope, f32x16& s_acc, Softmax& sm, float score_c,
                                               int lim, RowState& rs, int pwrite, int vmain, int pbuf,
                                               f32x16 (&oacc)[kRowBlocks][kColTiles], Dma&& dma) {
+  // bf16 K: fragments read kKDepth products ahead. fp8 K: 16-byte pairs read
+  // kRawDepth pairs ahead and each k-step converted two products ahead of its
+  // MFMA (so the conversion's VALU writes are far from the assembly MFMA
+  // that reads them).
+  constexpr int kRawDepth = 3;
   bf16x8 kb[kKDepth];
+  u32x4 raw[kRawDepth];
   bf16x8 pb[kRowBlocks];
   bf16x8 vb[2];
   if constexpr (QK) {
+    if constexpr (!KV_FP8) {
 #pragma unroll
-    for (int d = 0; d < kKDepth; ++d) kb[d] = k_frag(smem, la, kmain, krope, d);
+      for (int d = 0; d < kKDepth; ++d) kb[d] = k_frag(smem, la, kmain, krope, d);
+    } else {
+#pragma unroll
+      for (int d = 0; d < kRawDepth; ++d) raw[d] = k_pair_f8(smem, la, kmain, krope, d);
+      kb[0] = fp8x8_to_bf16(raw[0][0], raw[0][1]);
+      kb[1] = fp8x8_to_bf16(raw[0][2], raw[0][3]);
+      raw[0] = k_pair_f8(smem, la, kmain, krope, kRawDepth);   // pair 0 is consumed
+    }
   }
   if constexpr (PV) {
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) pb[rb] = p_frag(smem, la, pbuf, rb, 0);
-    vb[0] = v_frag(smem, la, vmain, 0, 0);
+    if constexpr (KV_FP8) vb[0] = v_frag_f8(smem, la, vmain, 0, 0);
+    else vb[0] = v_frag(smem, la, vmain, 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < kKSteps; ++s) {
     if (s < NDMA) dma(s);
     if constexpr (QK) {
-      const bf16x8 a = kb[s % kKDepth];
-      if (s + kKDepth < kKSteps) kb[s % kKDepth] = k_frag(smem, la, kmain, krope, s + kKDepth);
+      bf16x8 a;
+      if constexpr (!KV_FP8) {
+        a = kb[s % kKDepth];
+        if (s + kKDepth < kKSteps) kb[s % kKDepth] = k_frag(smem, la, kmain, krope, s + kKDepth);
+      } else {
+        a = kb[s % 3];
+        const int ks = s + 2, pj = ks >> 1;
+        if (ks < kKSteps) {
+          const u32x4 r = raw[pj % kRawDepth];
+          kb[ks % 3] = (ks & 1) ? fp8x8_to_bf16(r[2], r[3]) : fp8x8_to_bf16(r[0], r[1]);
+          if ((ks & 1) && pj + kRawDepth < kKSteps / 2)
+            raw[pj % kRawDepth] = k_pair_f8(smem, la, kmain, krope, pj + kRawDepth);
+        }
+      }
       if (s == 0) mfma_qk_first(s_acc, a, qf[s]);
       else if (s + 1 < kKSteps) mfma_qk(s_acc, a, qf[s]);
       else mfma_qk_last(s_acc, a, qf[s]);
     }
     if constexpr (PV) {
-      if (s < kPvEarly) pv_product(smem, la, vmain, pbuf, s, vb, pb, oacc);
+      if (s < kPvEarly) pv_product<KV_FP8>(smem, la, vmain, pbuf, s, vb, pb, oacc);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -502,7 +554,7 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
 #pragma unroll
   for (int j = 0; j < kTail; ++j) {
     if constexpr (PV) {
-      if (kPvEarly + j < 32) pv_product(smem, la, vmain, pbuf, kPvEarly + j, vb, pb, oacc);
+      if (kPvEarly + j < 32) pv_product<KV_FP8>(smem, la, vmain, pbuf, kPvEarly + j, vb, pb, oacc);
     }
     if constexpr (QK) {
       if (j < kSoftmaxPieces) softmax_piece(j, sm, s_acc, score_c, lim, rs);
@@ -570,19 +622,25 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     const int causal_lim = qpos >= 0 ? qpos / a.dcp_world : -1;
     const int pos_limit = (a.causal && row_ok) ? causal_lim : (L - 1);
     const int key_last = min(end - 1, pos_limit);   // last visible key of this row in the split
-    // lane holds Q[row][16 ks + 8 (lane >> 5) .. +7] for ks = 0..35 (B operand of S^T = K Q^T)
+    // The B operand of S^T = K Q^T: lane holds, for k-step ks, the 8 dims
+    // that the K fragment's lane half h = lane >> 5 holds: 16 ks + 8 h .. +7
+    // for bf16 KV; for fp8 KV (k-steps in pairs) 32 (ks / 2) + 16 h +
+    // 8 (ks & 1) .. +7. In 8-element units: 2 ks + h, or 4 (ks / 2) + 2 h +
+    // (ks & 1).
     bf16x8 qf[kKSteps];
     if (row_ok) {
-      const int64_t qrow = ((int64_t)(q0 + tok) * H + head) * kDLat + 8 * (lane >> 5);
+      const int64_t qrow = ((int64_t)(q0 + tok) * H + head) * kDLat;
+      const int h = lane >> 5;
+      auto unit = [&](int ks) { return KV_FP8 ? 4 * (ks >> 1) + 2 * h + (ks & 1) : 2 * ks + h; };
       if constexpr (!Q_FP8) {
         const bf16x8* src = (const bf16x8*)((const uint16_t*)a.q + qrow);
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = src[ks * 2];
+        for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = src[unit(ks)];
       } else {
         const u32x2* src = (const u32x2*)((const unsigned char*)a.q + qrow);
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) {
-          const u32x2 v = src[ks * 2];
+          const u32x2 v = src[unit(ks)];
           qf[ks] = cat(fp8x4_to_bf16(v[0]), fp8x4_to_bf16(v[1]));
         }
       }
@@ -619,10 +677,6 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         if (ntiles > 1) wait_vm<1 + Dma::n>();
         else wait_vm<1>();
         __syncthreads();
-        if constexpr (KV_FP8) {
-          convert_tile(smem, LY::stage(0), LY::main(0), LY::rope(0), tid);
-          __syncthreads();
-        }
 
         f32x16 s_acc;
         Softmax sm;
@@ -643,19 +697,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
             Dma::op(i, kv, slot, lds_addr_of(smem), dm, dr, w, dlane);
           };
           const int lim = key_last - (begin + t * kNT + 4 * (lane >> 5));
-          const LaneAddr la_s = lane_addr(dlane, w);
-          pipeline_step<DO_QK, DO_PV, DO_DMA ? Dma::n : 0>(smem, la_s, qf, LY::main(t), LY::rope(t), s_acc, sm,
+          const LaneAddr la_s = lane_addr<KV_FP8>(dlane, w);
+          pipeline_step<DO_QK, DO_PV, DO_DMA ? Dma::n : 0, KV_FP8>(smem, la_s, qf, LY::main(t), LY::rope(t), s_acc, sm,
                                                             score_c, lim, rs, p_buf(t), LY::main(t + 11), p_buf(t + 1),
                                                             oacc, dma);
           if (have) wait_vm<1 + Dma::n>();
           else wait_vm<1>();
           __syncthreads();   // tile t+1 landed; P(t) published; tile t-1 and P(t-1) are free
-          if constexpr (KV_FP8) {
-            if (t + 1 < ntiles) {
-              convert_tile(smem, LY::stage(t + 1), LY::main(t + 1), LY::rope(t + 1), tid);
-              __syncthreads();
-            }
-          }
         };
         using T_ = std::true_type;
         using F_ = std::false_type;
@@ -773,8 +821,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
 
 // ---------------------------------------------------------------------------
 // Gather test hook: one block per split; every tile goes through the decode
-// kernel's loader (and fp8 conversion) into tile 0, then is copied out of LDS
-// with the swizzle undone.
+// kernel's loader into tile 0, then is copied out of LDS with the swizzle
+// undone (fp8 converted exactly to bf16, as the decode does in registers).
 template <bool KV_FP8>
 __global__ __launch_bounds__(kDecodeThreads) void gather_kernel(GatherArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kTilesEnd];
@@ -800,16 +848,23 @@ __global__ __launch_bounds__(kDecodeThreads) void gather_kernel(GatherArgs a) {
     TileDma<KV_FP8>::all(kv, slot, smem, dma_main<KV_FP8>(0), dma_rope<KV_FP8>(0), wave, lane);
     wait_vm_all();
     __syncthreads();
-    if constexpr (KV_FP8) {
-      convert_tile(smem, Layout<true>::stage(0), LY::main(0), LY::rope(0), tid);
-      __syncthreads();
-    }
     for (int p = tid; p < kNT * 72; p += kDecodeThreads) {
-      const int row = p / 72, chunk = p - row * 72;
+      const int row = p / 72, chunk = p - row * 72;   // chunk: 8 latent dims
       if (key0 + row < end) {
-        const int off = chunk < 64 ? LY::main(0) + row * kMainRow + ((chunk ^ swz_main(row)) << 4)
-                                   : LY::rope(0) + row * kRopeRow + (((chunk - 64) ^ swz_rope(row)) << 4);
-        const u32x4 v = lds_load<u32x4>(smem, off);
+        u32x4 v;
+        if constexpr (!KV_FP8) {
+          const int off = chunk < 64 ? LY::main(0) + row * kMainRow + ((chunk ^ swz_main(row)) << 4)
+                                     : LY::rope(0) + row * kRopeRow + (((chunk - 64) ^ swz_rope(row)) << 4);
+          v = lds_load<u32x4>(smem, off);
+        } else {   // 8 fp8 bytes, half of a 16-byte chunk, converted exactly
+          const int c = chunk < 64 ? chunk : chunk - 64;
+          const int off = chunk < 64
+                              ? LY::main(0) + row * kF8MainRow + (((c >> 1) ^ swz_f8(row)) << 4) + 8 * (c & 1)
+                              : LY::rope(0) + (row >> 3) * 1024 + (row & 7) * kF8RopeRow +
+                                    (((c >> 1) ^ swz_f8_rope(row)) << 4) + 8 * (c & 1);
+          const u32x2 x = lds_load<u32x2>(smem, off);
+          v = __builtin_bit_cast(u32x4, cat(fp8x4_to_bf16(x[0]), fp8x4_to_bf16(x[1])));
+        }
         *(u32x4*)(a.dense + (dense0 + key0 + row) * kDLat + chunk * 8) = v;
       }
     }
