@@ -116,7 +116,8 @@ MLA_API int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t nu
                         int32_t num_cus, int32_t* plan, int64_t plan_words);
 
 /* Workspace bytes mla_decode_fwd needs for this plan: 0 when no row is
- * split, else the fp32 partials, P * q_len_max * heads * (512 + 1) * 4 bytes,
+ * split, else the partials (bf16 O, fp32 LSE), P * q_len_max * heads *
+ * (512 * 2 + 4) bytes,
  * preceded for an MLA_PLAN_MERGE_IN_KERNEL plan by 256 KiB of split-arrival
  * counters. plan: host words from mla_decode_plan. Errors: INVALID_ARG,
  * PLAN_MISMATCH (bad magic or version). */

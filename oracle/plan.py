@@ -11,7 +11,7 @@ library's own choice (spec version 1); the library's C++ planner must produce
 the same int32 words.
 
 Constants: M_UNIT 128 query rows per work item, N_MAX 256 splits per row,
-MIN_SPLIT_KEYS 256, ITEM_OVERHEAD 128 (a work item's fixed cost, in keys),
+MIN_SPLIT_KEYS 256, ITEM_OVERHEAD 256 (a work item's fixed cost, in keys),
 OCC 1 resident work item per compute unit (a decode workgroup takes nearly
 all of a CU's LDS), XCDS 8 (the chiplets whose L2 a launch spreads over).
 All arithmetic is integer; cdiv(a, b) = (a + b - 1) // b.
@@ -31,7 +31,7 @@ Steps:
    n_x = (OCC*C) // X slots per chiplet; lam = max(1, n_x // u) lanes per
    chiplet; LAMBDA = X * lam lanes. Lane l (chiplet x = l mod X, k = l // X)
    has members j = 0..u-1, workgroup x + X*(k*u + j).
-   Lane capacity T = max(MIN_SPLIT_KEYS,
+   Lane capacity T = max(MIN_SPLIT_KEYS + ITEM_OVERHEAD,
    cdiv(sum L + ITEM_OVERHEAD*(R + LAMBDA), LAMBDA),
    cdiv(max L, N_MAX - 1) + ITEM_OVERHEAD). A split costs its keys plus
    ITEM_OVERHEAD. Walk the rows in order with lane l = 0 and cap = T: a row
@@ -69,7 +69,7 @@ HEADER_WORDS = 20
 M_UNIT = 128
 N_MAX = 256
 MIN_SPLIT_KEYS = 256
-ITEM_OVERHEAD = 128
+ITEM_OVERHEAD = 256
 OCC = 1
 XCDS = 8
 
@@ -126,7 +126,7 @@ def plan_ref(kv_lens, H, q_len_max, kv_dtype, mode, C):
             X //= 2
         lam = max(1, ((OCC * C) // X) // u)
         n_lanes = X * lam
-        T = max(MIN_SPLIT_KEYS, cdiv(sum(lens) + ITEM_OVERHEAD * (R + n_lanes), n_lanes),
+        T = max(MIN_SPLIT_KEYS + ITEM_OVERHEAD, cdiv(sum(lens) + ITEM_OVERHEAD * (R + n_lanes), n_lanes),
                 cdiv(max(lens), N_MAX - 1) + ITEM_OVERHEAD)
         lane_splits = [[] for _ in range(n_lanes)]
         lane, cap = 0, T

@@ -103,9 +103,9 @@ int32_t decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale, cons
   a.o = (uint16_t*)o;
   a.lse = lse;
   const int64_t ws_o_elems = (int64_t)v.P * q_len_max * num_heads * MLA_D_V;
-  float* partials = need > 0 ? (float*)((char*)workspace + workspace_counter_bytes(v)) : nullptr;
+  uint16_t* partials = need > 0 ? (uint16_t*)((char*)workspace + workspace_counter_bytes(v)) : nullptr;
   a.ws_o = partials;
-  a.ws_lse = need > 0 ? partials + ws_o_elems : nullptr;
+  a.ws_lse = need > 0 ? (float*)(partials + ws_o_elems) : nullptr;
   a.counters = need > 0 ? (int32_t*)workspace : nullptr;
   a.off_split_indptr = (int32_t)v.off_split_indptr;
   a.u = v.u;

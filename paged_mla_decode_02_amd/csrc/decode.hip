@@ -453,10 +453,10 @@ __device__ __forceinline__ void merge_tile(const DecodeArgs& a, int m, int M, in
 #pragma unroll
     for (int k = 0; k < kMaxInKernelSplits; ++k) {
       if (k < n) {
-        const f32x4* src = (const f32x4*)(a.ws_o + (base + k * stride) * kDV + c * 8);
+        const bf16x8 src = *(const bf16x8*)(a.ws_o + (base + k * stride) * kDV + c * 8);
         const float wk = lk[k] * inv;   // an empty split's partial is 0 and its weight 0
-        acc0 += wk * src[0];
-        acc1 += wk * src[1];
+        acc0 += wk * f32x4{(float)src[0], (float)src[1], (float)src[2], (float)src[3]};
+        acc1 += wk * f32x4{(float)src[4], (float)src[5], (float)src[6], (float)src[7]};
       }
     }
     *(bf16x8*)dst = bf16x8{(__bf16)acc0[0], (__bf16)acc0[1], (__bf16)acc0[2], (__bf16)acc0[3],
@@ -765,28 +765,18 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         }
         __syncthreads();
         const int nrows = min(64, M - (m * kRows + 64 * half));   // rows of this half inside the block
-        if (part < 0) {
-          // bf16: thread takes 8 columns (two chunks) of a row per store
+        uint16_t* const dst0 = part < 0 ? a.o : a.ws_o;            // bf16 O, or the split's partial O
+        // thread takes 8 columns (two staged chunks) of a row per store
 #pragma unroll 4
-          for (int i = 0; i < 64 * 64 / kDecodeThreads; ++i) {
-            const int p2 = i * kDecodeThreads + et;
-            const int r = p2 >> 6, c2 = p2 & 63;
-            if (r < nrows) {
-              const f32x4 x0 = lds_load<f32x4>(smem, r * 2048 + (((2 * c2) ^ (r & 15)) << 4));
-              const f32x4 x1 = lds_load<f32x4>(smem, r * 2048 + (((2 * c2 + 1) ^ (r & 15)) << 4));
-              *(bf16x8*)(a.o + (orow0 + 64 * half + r) * kDV + 8 * c2) =
-                  bf16x8{(__bf16)x0[0], (__bf16)x0[1], (__bf16)x0[2], (__bf16)x0[3],
-                         (__bf16)x1[0], (__bf16)x1[1], (__bf16)x1[2], (__bf16)x1[3]};
-            }
-          }
-        } else {
-#pragma unroll 4
-          for (int i = 0; i < 64 * 128 / kDecodeThreads; ++i) {
-            const int p2 = i * kDecodeThreads + et;
-            const int r = p2 >> 7, c = p2 & 127;
-            if (r < nrows)
-              *(f32x4*)(a.ws_o + (orow0 + 64 * half + r) * kDV + 4 * c) =
-                  lds_load<f32x4>(smem, r * 2048 + ((c ^ (r & 15)) << 4));
+        for (int i = 0; i < 64 * 64 / kDecodeThreads; ++i) {
+          const int p2 = i * kDecodeThreads + et;
+          const int r = p2 >> 6, c2 = p2 & 63;
+          if (r < nrows) {
+            const f32x4 x0 = lds_load<f32x4>(smem, r * 2048 + (((2 * c2) ^ (r & 15)) << 4));
+            const f32x4 x1 = lds_load<f32x4>(smem, r * 2048 + (((2 * c2 + 1) ^ (r & 15)) << 4));
+            *(bf16x8*)(dst0 + (orow0 + 64 * half + r) * kDV + 8 * c2) =
+                bf16x8{(__bf16)x0[0], (__bf16)x0[1], (__bf16)x0[2], (__bf16)x0[3],
+                       (__bf16)x1[0], (__bf16)x1[1], (__bf16)x1[2], (__bf16)x1[3]};
           }
         }
         __syncthreads();

@@ -30,7 +30,7 @@ struct DecodeArgs {
   const int32_t* kv_len_global;     // [rows] keys of each row over all shards, or null (= local)
   uint16_t* o;              // bf16 bits
   float* lse;
-  float* ws_o;              // [P, q_len_max, heads, 512] fp32 partial O
+  uint16_t* ws_o;           // [P, q_len_max, heads, 512] bf16 partial O (normalized)
   float* ws_lse;            // [P, q_len_max, heads] fp32 partial LSE
 };
 
@@ -39,7 +39,7 @@ struct MergeArgs {
   const int32_t* plan;
   int32_t off_split_indptr, off_split_part;
   int32_t heads, q_len_max;
-  const float* ws_o;
+  const uint16_t* ws_o;
   const float* ws_lse;
   uint16_t* o;
   float* lse;

@@ -61,6 +61,13 @@ __device__ __forceinline__ bool merge_weights(const MergeArgs& a, int64_t base, 
   return true;
 }
 
+// 8 columns of a bf16 partial O as fp32.
+__device__ __forceinline__ void load_partial(const uint16_t* p, f32x4 (&v)[2]) {
+  const bf16x8 x = *(const bf16x8*)p;
+  v[0] = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+  v[1] = f32x4{(float)x[4], (float)x[5], (float)x[6], (float)x[7]};
+}
+
 // Weight of split k (wave-uniform k < 256) from merge_weights' registers.
 __device__ __forceinline__ float weight_of(const float (&wk)[kMergeLanes], int k) {
   const int i = k >> 6;   // uniform
@@ -100,15 +107,11 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
     const int64_t orow = (int64_t)(q0 + i) * a.heads + h;
     float wk[kMergeLanes], lse;
     if (!merge_weights(a, base, stride, n, lane, orow, wk, lse, true)) return;
-    const float* src = a.ws_o + base * kDV + lane * 8;
+    const uint16_t* src = a.ws_o + base * kDV + lane * 8;
     f32x4 v[8][2];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      if (k < n) {
-        const f32x4* p = (const f32x4*)(src + k * stride * kDV);
-        v[k][0] = p[0];
-        v[k][1] = p[1];
-      }
+      if (k < n) load_partial(src + k * stride * kDV, v[k]);
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 8; ++k)
@@ -128,18 +131,14 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
     const int64_t orow = (int64_t)(q0 + i) * a.heads + h;
     float wk[kMergeLanes], lse;
     if (!merge_weights(a, base, stride, n, lane, orow, wk, lse, w == 0)) continue;   // uniform
-    const float* src = a.ws_o + base * kDV + lane * 8;
+    const uint16_t* src = a.ws_o + base * kDV + lane * 8;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = w; k0 < n; k0 += 8 * kW) {
       f32x4 v[8][2];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int k = k0 + u * kW;
-        if (k < n) {
-          const f32x4* p = (const f32x4*)(src + k * stride * kDV);
-          v[u][0] = p[0];
-          v[u][1] = p[1];
-        }
+        if (k < n) load_partial(src + k * stride * kDV, v[u]);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {

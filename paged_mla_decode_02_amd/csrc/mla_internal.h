@@ -17,7 +17,7 @@ constexpr int32_t kHeaderWords = 20;
 constexpr int32_t kMUnit = 128;
 constexpr int32_t kNMax = 256;
 constexpr int32_t kMinSplitKeys = 256;
-constexpr int32_t kItemOverhead = 128;
+constexpr int32_t kItemOverhead = 256;
 constexpr int32_t kOcc = 1;
 constexpr int32_t kXcds = 8;
 
@@ -52,7 +52,8 @@ int32_t view_plan(const int32_t* plan, PlanView* v);
 inline int64_t workspace_counter_bytes(const PlanView& v) { return v.merge_in_kernel ? kWsCounterBytes : 0; }
 inline int64_t workspace_bytes(const PlanView& v) {
   if (v.P == 0) return 0;
-  return workspace_counter_bytes(v) + (int64_t)v.P * v.q_len_max * v.heads * (MLA_D_V + 1) * 4;
+  // bf16 partial O, then fp32 partial LSE
+  return workspace_counter_bytes(v) + (int64_t)v.P * v.q_len_max * v.heads * (MLA_D_V * 2 + 4);
 }
 
 int32_t set_error(int32_t status, const std::string& msg);

@@ -158,7 +158,7 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
     while (X > 1 && slots / X < u) X /= 2;
     const int64_t lam = std::max<int64_t>(1, (slots / X) / u);
     const int64_t n_lanes = X * lam;
-    const int64_t T = std::max({(int64_t)kMinSplitKeys,
+    const int64_t T = std::max({(int64_t)kMinSplitKeys + kItemOverhead,
                                 cdiv(sum_len + (int64_t)kItemOverhead * (rows + n_lanes), n_lanes),
                                 cdiv(max_len, kNMax - 1) + kItemOverhead});
     lane_splits.resize(n_lanes);
