@@ -15,77 +15,83 @@ namespace {
 using namespace dev;
 
 constexpr int kDV = 512;
-constexpr int kMergeLanes = 4;   // splits per lane: n <= 256
+constexpr int kChunk = 8;   // partials whose loads a lane has in flight at once
 
 // ---------------------------------------------------------------------------
 // Split merge: one block of four waves per (request row b, query token i,
-// heads 4 j .. 4 j + 3) of a row with n > 1 splits (n <= 256). Lane l of a
-// wave reads LSE_k for k = l + 64 i and the wave reduces max and sum. With n <= 8 splits each wave
-// merges one head, all n partials' loads in flight at once; with more, the
-// four waves take every fourth split of one head at a time and add up in
-// LDS. A lane owns 8 output columns.
-// Weights of the n partials of one (token, head): lane l gets
-// exp(LSE_k - LSE) for its splits k; returns false (and writes O = 0, LSE = -inf) when every
-// split is empty.
-__device__ __forceinline__ bool merge_weights(const MergeArgs& a, int64_t base, int64_t stride, int n,
-                                              int lane, int64_t orow, float (&wk)[kMergeLanes], float& lse,
-                                              bool writer) {
-  // Lane l holds split k = l + 64 i in slot i (up to 256 splits).
-  float lk[kMergeLanes];
-  float mx = -INFINITY;
+// heads 4 j .. 4 j + 3) of a row with n > 1 splits. A lane owns 8 of the 512
+// output columns. The split partials are merged by log-sum-exp, online, in
+// chunks of kChunk splits: a chunk's partial-O loads and LSE loads are issued
+// together (the LSE addresses are wave-uniform, so those are scalar loads),
+// so a chunk costs one memory round trip; the running (max, sum, O) are
+// rescaled when a chunk raises the max. With n <= kChunk splits each wave
+// merges one head in one round trip; with more, the four waves of the block
+// take every fourth split of one head at a time and combine their running
+// states through LDS.
+struct MergeState {
+  float m, l;       // running max of LSE_k, and sum of exp(LSE_k - m)
+  f32x4 acc0, acc1; // sum of exp(LSE_k - m) O_k over this lane's 8 columns
+};
+
+// Splits k = k0 + j kstep, j < kChunk, k < n, of the partial rows at `src`
+// (this lane's 8 columns) and `lse_base` (uniform), folded into st.
+__device__ __forceinline__ void merge_chunk(const uint16_t* src, const float* lse_base, int64_t stride, int k0,
+                                            int kstep, int n, MergeState& st) {
+  bf16x8 v[kChunk];
+  float lk[kChunk];
 #pragma unroll
-  for (int i = 0; i < kMergeLanes; ++i) {
-    const int k = lane + 64 * i;
-    lk[i] = k < n ? a.ws_lse[base + k * stride] : -INFINITY;
-    mx = fmaxf(mx, lk[i]);
-  }
-  mx = wave_max(mx);
-  if (mx == -INFINITY) {
-    if (writer) {
-      *(u32x4*)(a.o + orow * kDV + lane * 8) = u32x4{0u, 0u, 0u, 0u};
-      if (lane == 0) a.lse[orow] = -INFINITY;
+  for (int j = 0; j < kChunk; ++j) {
+    const int k = k0 + j * kstep;
+    if (k < n) {
+      v[j] = *(const bf16x8*)(src + (int64_t)k * stride * kDV);
+      lk[j] = lse_base[(int64_t)k * stride];
+    } else {
+      lk[j] = -INFINITY;
     }
-    return false;
   }
-  const float kLog2e = 1.44269504088896340736f;
-  float part = 0.f;
+  float cm = lk[0];
 #pragma unroll
-  for (int i = 0; i < kMergeLanes; ++i) {
-    wk[i] = lk[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lk[i] - mx) * kLog2e);
-    part += wk[i];
+  for (int j = 1; j < kChunk; ++j) cm = fmaxf(cm, lk[j]);
+  if (cm == -INFINITY) return;   // every split of the chunk is empty (uniform)
+  const float mnew = fmaxf(st.m, cm);
+  if (mnew > st.m) {   // uniform
+    const float r = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - mnew) * kLog2e);
+    st.l *= r;
+    st.acc0 *= r;
+    st.acc1 *= r;
+    st.m = mnew;
   }
-  const float tot = wave_sum(part);
 #pragma unroll
-  for (int i = 0; i < kMergeLanes; ++i) wk[i] /= tot;
-  lse = mx + __log2f(tot) * kLn2;
-  return true;
+  for (int j = 0; j < kChunk; ++j) {
+    if (lk[j] != -INFINITY) {   // an empty split's partial O is 0 and carries no weight
+      const float c = __builtin_amdgcn_exp2f((lk[j] - mnew) * kLog2e);
+      st.l += c;
+      st.acc0 += c * f32x4{(float)v[j][0], (float)v[j][1], (float)v[j][2], (float)v[j][3]};
+      st.acc1 += c * f32x4{(float)v[j][4], (float)v[j][5], (float)v[j][6], (float)v[j][7]};
+    }
+  }
 }
 
-// 8 columns of a bf16 partial O as fp32.
-__device__ __forceinline__ void load_partial(const uint16_t* p, f32x4 (&v)[2]) {
-  const bf16x8 x = *(const bf16x8*)p;
-  v[0] = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-  v[1] = f32x4{(float)x[4], (float)x[5], (float)x[6], (float)x[7]};
-}
-
-// Weight of split k (wave-uniform k < 256) from merge_weights' registers.
-__device__ __forceinline__ float weight_of(const float (&wk)[kMergeLanes], int k) {
-  const int i = k >> 6;   // uniform
-  const float v = i == 0 ? wk[0] : i == 1 ? wk[1] : i == 2 ? wk[2] : wk[3];
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), k & 63));
-}
-
-__device__ __forceinline__ void store_row(const MergeArgs& a, int64_t orow, int lane, f32x4 acc0, f32x4 acc1,
-                                          float lse) {
-  *(bf16x8*)(a.o + orow * kDV + lane * 8) =
-      bf16x8{(__bf16)acc0[0], (__bf16)acc0[1], (__bf16)acc0[2], (__bf16)acc0[3],
-             (__bf16)acc1[0], (__bf16)acc1[1], (__bf16)acc1[2], (__bf16)acc1[3]};
-  if (lane == 0) a.lse[orow] = lse;
+// O = acc / l (bf16) and LSE = m + ln l, or O = 0 and LSE = -inf when no
+// split saw a key.
+__device__ __forceinline__ void store_merged(const MergeArgs& a, int64_t orow, int lane, const MergeState& st) {
+  uint16_t* dst = a.o + orow * kDV + lane * 8;
+  if (st.m == -INFINITY) {
+    *(u32x4*)dst = u32x4{0u, 0u, 0u, 0u};
+    if (lane == 0) a.lse[orow] = -INFINITY;
+    return;
+  }
+  const float inv = 1.0f / st.l;
+  const f32x4 x0 = st.acc0 * inv, x1 = st.acc1 * inv;
+  *(bf16x8*)dst = bf16x8{(__bf16)x0[0], (__bf16)x0[1], (__bf16)x0[2], (__bf16)x0[3],
+                         (__bf16)x1[0], (__bf16)x1[1], (__bf16)x1[2], (__bf16)x1[3]};
+  if (lane == 0) a.lse[orow] = st.m + __log2f(st.l) * kLn2;
 }
 
 __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
-  __shared__ f32x4 part[kBlockThreads / 64 - 1][64][2];
   constexpr int kW = kBlockThreads / 64;
+  __shared__ f32x4 part_acc[kW - 1][64][2];
+  __shared__ float part_ml[kW - 1][2];
   const int hgroups = (a.heads + kW - 1) / kW;
   const int hg = blockIdx.x % hgroups;
   const int bi = blockIdx.x / hgroups;
@@ -96,31 +102,18 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
   if (n <= a.skip_upto) return;   // unsplit, or merged in the decode kernel
   const int q0 = a.qo_indptr[b];
   if (i >= a.qo_indptr[b + 1] - q0) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int part0 = a.plan[a.off_split_part + s0];
   const int64_t stride = (int64_t)a.q_len_max * a.heads;   // partial slots are consecutive
 
-  if (n <= 8) {   // one wave per head (uniform over the block: n is the row's)
+  if (n <= kChunk) {   // one wave per head, one round trip (uniform over the block: n is the row's)
     const int h = hg * kW + w;
     if (h >= a.heads) return;
     const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
-    const int64_t orow = (int64_t)(q0 + i) * a.heads + h;
-    float wk[kMergeLanes], lse;
-    if (!merge_weights(a, base, stride, n, lane, orow, wk, lse, true)) return;
-    const uint16_t* src = a.ws_o + base * kDV + lane * 8;
-    f32x4 v[8][2];
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (k < n) load_partial(src + k * stride * kDV, v[k]);
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (k < n) {
-        const float c = weight_of(wk, k);
-        acc0 += c * v[k][0];   // an empty split's partial is 0 and its weight 0
-        acc1 += c * v[k][1];
-      }
-    store_row(a, orow, lane, acc0, acc1, lse);
+    MergeState st{-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    merge_chunk(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, 0, 1, n, st);
+    store_merged(a, (int64_t)(q0 + i) * a.heads + h, lane, st);
     return;
   }
 
@@ -128,42 +121,42 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
     const int h = hg * kW + hh;
     if (h >= a.heads) break;          // uniform
     const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
-    const int64_t orow = (int64_t)(q0 + i) * a.heads + h;
-    float wk[kMergeLanes], lse;
-    if (!merge_weights(a, base, stride, n, lane, orow, wk, lse, w == 0)) continue;   // uniform
-    const uint16_t* src = a.ws_o + base * kDV + lane * 8;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = w; k0 < n; k0 += 8 * kW) {
-      f32x4 v[8][2];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k0 + u * kW;
-        if (k < n) load_partial(src + k * stride * kDV, v[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k0 + u * kW;
-        if (k < n) {
-          const float c = weight_of(wk, k);
-          acc0 += c * v[u][0];
-          acc1 += c * v[u][1];
-        }
-      }
-    }
+    MergeState st{-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int k0 = w; k0 < n; k0 += kChunk * kW)
+      merge_chunk(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, k0, kW, n, st);
     if (w > 0) {
-      part[w - 1][lane][0] = acc0;
-      part[w - 1][lane][1] = acc1;
+      part_acc[w - 1][lane][0] = st.acc0;
+      part_acc[w - 1][lane][1] = st.acc1;
+      if (lane == 0) {
+        part_ml[w - 1][0] = st.m;
+        part_ml[w - 1][1] = st.l;
+      }
     }
     __syncthreads();
     if (w == 0) {
+      float M = st.m;
 #pragma unroll
-      for (int j = 0; j < kW - 1; ++j) {
-        acc0 += part[j][lane][0];
-        acc1 += part[j][lane][1];
+      for (int j = 0; j < kW - 1; ++j) M = fmaxf(M, part_ml[j][0]);
+      if (M != -INFINITY) {
+        const float r = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - M) * kLog2e);
+        st.l *= r;
+        st.acc0 *= r;
+        st.acc1 *= r;
+#pragma unroll
+        for (int j = 0; j < kW - 1; ++j) {
+          const float mj = part_ml[j][0];
+          if (mj != -INFINITY) {
+            const float c = __builtin_amdgcn_exp2f((mj - M) * kLog2e);
+            st.l += c * part_ml[j][1];
+            st.acc0 += c * part_acc[j][lane][0];
+            st.acc1 += c * part_acc[j][lane][1];
+          }
+        }
       }
-      store_row(a, orow, lane, acc0, acc1, lse);
+      st.m = M;
+      store_merged(a, (int64_t)(q0 + i) * a.heads + h, lane, st);
     }
-    __syncthreads();   // part[] is reused for the next head
+    __syncthreads();   // the LDS states are reused for the next head
   }
 }
 
