@@ -27,11 +27,15 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode effective KV GB/s + MFMA TFLOP/s (128 heads, q_len 8, fp8 KV)"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
-KERNEL_SRC = os.path.join(ROOT, "paged_mla_decode_02_amd", "csrc", "kernels.hip")
+# The sources of the kernels one mla_decode_fwd call launches (decode, merge).
+KERNEL_SRCS = [os.path.join(ROOT, "paged_mla_decode_02_amd", "csrc", f) for f in ("decode.hip", "kernels.hip")]
 
 
 def kernel_sha():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def visible_pairs(kv_lens, q_lens, causal):
@@ -137,6 +141,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=3, help="disjoint index lists cycled over steps")
     ap.add_argument("--plan", default="length_aware", choices=["auto", "uniform", "length_aware"],
                     help="split plan mode (the uniform plan is also timed beside it)")
+    ap.add_argument("--no-uniform", action="store_true",
+                    help="skip the comparison run with the uniform plan (counter passes use this)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warm-up, one plain device copy of this many MiB: the known-size "
                          "reference for scaling hardware byte counters")
@@ -248,7 +254,7 @@ def main():
     # The uniform plan (its split count depends only on the row count, the
     # longest row and the config) timed the same way, for comparison.
     uniform = None
-    if plan_info["mode"] != "uniform":
+    if plan_info["mode"] != "uniform" and not args.no_uniform:
         dec_u = mla.MlaDecoder(case.heads, case.q_len, case.q_dtype, case.kv_dtype, case.causal,
                                float(case.sm_scale), mode=mla.PLAN_UNIFORM)
         for k in range(args.warmup):

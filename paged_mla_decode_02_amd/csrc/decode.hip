@@ -378,21 +378,28 @@ struct RowState {
   bool over;
 };
 // piece 0..3: scale and mask 4 scores, running max; piece 4: row max, the
-// reference; pieces 5..12: two exponentials each.
+// reference; pieces 5..12: two exponentials each. FAST (every score of the
+// tile visible to every row of the wave, and a positive score scale) skips
+// the mask and folds the scale into the exponent: the max of the raw scores
+// times the scale is the max of the scaled scores, and exp2(s c - mu) is one
+// fma.
+template <bool FAST>
 __device__ __forceinline__ void softmax_piece(int piece, Softmax& sm, f32x16& s, float score_c, int lim,
                                               RowState& rs) {
-  // The scores are scaled and masked in place (s is dead after this tile).
   if (piece < 4) {
+    if constexpr (!FAST) {
+      // The scores are scaled and masked in place (s is dead after this tile).
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 4 * piece + e;
-      const float v = s[r] * score_c;
-      s[r] = (8 * (r >> 2) + (r & 3) <= lim) ? v : -INFINITY;
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * piece + e;
+        const float v = s[r] * score_c;
+        s[r] = (8 * (r >> 2) + (r & 3) <= lim) ? v : -INFINITY;
+      }
     }
     const float m4 = fmaxf(fmaxf(s[4 * piece], s[4 * piece + 1]), fmaxf(s[4 * piece + 2], s[4 * piece + 3]));
     sm.tmax = piece == 0 ? m4 : fmaxf(sm.tmax, m4);
   } else if (piece == 4) {
-    const float tmax = half_max(sm.tmax);
+    const float tmax = FAST ? half_max(sm.tmax) * score_c : half_max(sm.tmax);
     rs.m_seen = fmaxf(rs.m_seen, tmax);
     // Until a row has seen a visible key its O and l are exactly zero, so its
     // reference may start at this tile's max without rescaling anything.
@@ -405,7 +412,7 @@ __device__ __forceinline__ void softmax_piece(int piece, Softmax& sm, f32x16& s,
       const int r = 2 * (piece - 5) + e;
       // v_exp_f32 directly: arguments below -126 give 0 or a denormal, which
       // only drops weights under 2^-126 of the row's reference.
-      const float pr = __builtin_amdgcn_exp2f(s[r] - sm.mu);
+      const float pr = __builtin_amdgcn_exp2f(FAST ? __builtin_fmaf(s[r], score_c, -sm.mu) : s[r] - sm.mu);
       rs.l_part += pr;
       sm.pf[r >> 3][r & 7] = (__bf16)pr;
     }
@@ -490,7 +497,7 @@ __device__ __forceinline__ void pv_product(const lds_u8* smem, const LaneAddr& l
 // keeps this order; K fragments are read kKDepth products ahead.
 constexpr int kKDepth = 5;
 constexpr int kPvEarly = 20;
-template <bool QK, bool PV, int NDMA, bool KV_FP8, typename Dma>
+template <bool QK, bool PV, int NDMA, bool KV_FP8, bool FAST, typename Dma>
 __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, const bf16x8 (&qf)[kKSteps],
                                               int kmain, int krope, f32x16& s_acc, Softmax& sm, float score_c,
                                               int lim, RowState& rs, int pwrite, int vmain, int pbuf,
@@ -557,7 +564,7 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
       if (kPvEarly + j < 32) pv_product<KV_FP8>(smem, la, vmain, pbuf, kPvEarly + j, vb, pb, oacc);
     }
     if constexpr (QK) {
-      if (j < kSoftmaxPieces) softmax_piece(j, sm, s_acc, score_c, lim, rs);
+      if (j < kSoftmaxPieces) softmax_piece<FAST>(j, sm, s_acc, score_c, lim, rs);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -685,9 +692,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         // P(t) stored, this wave's loads of tile t+1 landed and one barrier.
         // DMA: this step issues tile t+2's loads (t + 2 < ntiles); it is a
         // template flag, so the hot loop carries no per-load branch.
-        auto run_step = [&](int t, auto QKc, auto PVc, auto DMAc) {
+        auto run_step = [&](int t, auto QKc, auto PVc, auto DMAc, auto FASTc) {
           constexpr bool DO_QK = decltype(QKc)::value, DO_PV = decltype(PVc)::value;
-          constexpr bool DO_DMA = decltype(DMAc)::value;
+          constexpr bool DO_DMA = decltype(DMAc)::value, FAST = decltype(FASTc)::value;
           const int dlane = opaque(lane);
           issue_slots(a.kv_indices, kv0, begin, end, t + 4, smem, w, dlane);
           constexpr bool have = DO_DMA;
@@ -698,9 +705,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
           };
           const int lim = key_last - (begin + t * kNT + 4 * (lane >> 5));
           const LaneAddr la_s = lane_addr<KV_FP8>(dlane, w);
-          pipeline_step<DO_QK, DO_PV, DO_DMA ? Dma::n : 0, KV_FP8>(smem, la_s, qf, LY::main(t), LY::rope(t), s_acc, sm,
-                                                            score_c, lim, rs, p_buf(t), LY::main(t + 11), p_buf(t + 1),
-                                                            oacc, dma);
+          pipeline_step<DO_QK, DO_PV, DO_DMA ? Dma::n : 0, KV_FP8, FAST>(smem, la_s, qf, LY::main(t), LY::rope(t),
+                                                                  s_acc, sm, score_c, lim, rs, p_buf(t),
+                                                                  LY::main(t + 11), p_buf(t + 1), oacc, dma);
           if (have) wait_vm<1 + Dma::n>();
           else wait_vm<1>();
           __syncthreads();   // tile t+1 landed; P(t) published; tile t-1 and P(t-1) are free
@@ -708,11 +715,20 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         using T_ = std::true_type;
         using F_ = std::false_type;
         // ntiles + 1 steps: 0 .. ntiles
-        if (ntiles > 2) run_step(0, T_{}, F_{}, T_{});
-        else run_step(0, T_{}, F_{}, F_{});
-        for (int t = 1; t + 2 < ntiles; ++t) run_step(t, T_{}, T_{}, T_{});
-        for (int t = ntiles > 3 ? ntiles - 2 : 1; t < ntiles; ++t) run_step(t, T_{}, T_{}, F_{});
-        run_step(ntiles, F_{}, T_{}, F_{});
+        if (ntiles > 2) run_step(0, T_{}, F_{}, T_{}, F_{});
+        else run_step(0, T_{}, F_{}, F_{}, F_{});
+        // The steady-state steps take the unmasked softmax while every key of
+        // the tile is visible to every row of this wave: tile t is, iff
+        // lim >= 27 on every lane (a lane's keys sit at most 27 past its
+        // key0), i.e. for t < nfast, a prefix of the tiles (uniform).
+        const int slack = __builtin_amdgcn_readfirstlane(
+            wave_min_i32(key_last - begin - 4 * (lane >> 5) - 27));
+        const int nfast = score_c > 0.f && slack >= 0 ? slack / kNT + 1 : 0;
+        int t = 1;
+        for (; t + 2 < ntiles && t < nfast; ++t) run_step(t, T_{}, T_{}, T_{}, T_{});
+        for (; t + 2 < ntiles; ++t) run_step(t, T_{}, T_{}, T_{}, F_{});
+        for (t = ntiles > 3 ? ntiles - 2 : 1; t < ntiles; ++t) run_step(t, T_{}, T_{}, F_{}, F_{});
+        run_step(ntiles, F_{}, T_{}, F_{}, F_{});
         wait_vm<0>();
       }
       // Did any row of the item overflow its reference? (uniform)

@@ -105,6 +105,11 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int d = 8; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
   return v;
 }
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, 64));
+  return v;
+}
 __device__ __forceinline__ float wave_sum(float v) {
   v = group_sum(v);
 #pragma unroll
