@@ -149,35 +149,59 @@ __device__ __forceinline__ int swz_f8_rope(int row) { return (row >> 2) & 3; }
 
 // One tile's direct-to-LDS loads, spread over the four waves; every wave
 // issues the same number n of load instructions, op(i) for i = 0..n-1.
-// slot_lane: lane j < 32 holds the pool slot of the tile's key j.
+// The source addresses come from a TileSrc, built once per tile from the
+// slot list (slot_lane: lane j < 32 holds the pool slot of the tile's key j),
+// so the address arithmetic of the n loads is not a chain in front of each.
 //   bf16: op i < 8 loads main row j = 4 i + w (one 1 KB row per instruction,
-//         its slot wave-uniform); op 8 loads rope rows 8w .. 8w+7, 8 lanes
-//         per row.
+//         its address wave-uniform: read from lane j of the per-lane row
+//         addresses); op 8 loads rope rows 8w .. 8w+7, 8 lanes per row.
 //   fp8:  op i < 4 loads main rows 2k, 2k + 1 for k = 4 i + w (two 512-byte
 //         rows per instruction); op 4 loads rope rows 8w .. 8w+7, 4 lanes per
 //         row, into the wave's 1 KB rope slot.
+template <bool KV_FP8> struct TileSrc;
+template <> struct TileSrc<false> {
+  uint32_t lo, hi;            // lane j < 32: byte address of key j's latent row
+  const unsigned char* rope;  // this lane's source of the rope load
+};
+template <> struct TileSrc<true> {
+  int slot_lane;
+};
+
 template <bool KV_FP8> struct TileDma {
   static constexpr int kMainOps = (KV_FP8 ? 16 : 32) / kWaves;
   static constexpr int n = kMainOps + 1;
   static constexpr int kRopeRows = kNT / kWaves;
 
-  static __device__ __forceinline__ void op(int i, const unsigned char* kv, int slot_lane,
+  static __device__ __forceinline__ TileSrc<KV_FP8> src(const unsigned char* kv, int slot_lane, int w, int lane) {
+    TileSrc<KV_FP8> t;
+    if constexpr (!KV_FP8) {
+      const uint64_t row = (uint64_t)(uintptr_t)kv + (uint64_t)(uint32_t)slot_lane * (2 * kDLat);
+      t.lo = (uint32_t)row;
+      t.hi = (uint32_t)(row >> 32);
+      const int j = kRopeRows * w + (lane >> 3);
+      const int slot = __shfl(slot_lane, j & 31, 64);
+      t.rope = kv + (int64_t)(uint32_t)slot * (2 * kDLat) + kMainRow + (((lane & 7) ^ swz_rope(j)) << 4);
+    } else {
+      t.slot_lane = slot_lane;
+    }
+    return t;
+  }
+
+  static __device__ __forceinline__ void op(int i, const unsigned char* kv, const TileSrc<KV_FP8>& src,
                                             uint32_t lds0, int main_off, int rope_off, int w,
                                             int lane) {
     if constexpr (!KV_FP8) {
       if (i < kMainOps) {
         const int j = kWaves * i + w;
-        const int slot = __builtin_amdgcn_readlane(slot_lane, j);   // wave-uniform
-        const unsigned char* row = kv + (int64_t)slot * (2 * kDLat);
+        const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)src.lo, j);   // wave-uniform
+        const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)src.hi, j);
+        const unsigned char* row = (const unsigned char*)(uintptr_t)((hi << 32) | lo);
         dma16_sbase(row, (uint32_t)((lane ^ swz_main(j)) << 4), lds0 + main_off + j * kMainRow);
       } else {
-        const int j = kRopeRows * w + (lane >> 3);
-        const int slot = __shfl(slot_lane, j & 31, 64);
-        const unsigned char* src =
-            kv + (int64_t)slot * (2 * kDLat) + kMainRow + (((lane & 7) ^ swz_rope(j)) << 4);
-        dma16_vaddr(src, lds0 + rope_off + w * kRopeRows * kRopeRow);
+        dma16_vaddr(src.rope, lds0 + rope_off + w * kRopeRows * kRopeRow);
       }
     } else {
+      const int slot_lane = src.slot_lane;
       if (i < kMainOps) {
         const int k = kWaves * i + w;            // rows 2k (lanes 0-31) and 2k + 1
         const int row = 2 * k + (lane >> 5);
@@ -197,8 +221,9 @@ template <bool KV_FP8> struct TileDma {
   static __device__ __forceinline__ void all(const unsigned char* kv, int slot_lane, lds_u8* smem,
                                              int main_off, int rope_off, int w, int lane_in) {
     const int lane = opaque(lane_in);
+    const TileSrc<KV_FP8> s = src(kv, slot_lane, w, lane);
 #pragma unroll
-    for (int i = 0; i < n; ++i) op(i, kv, slot_lane, lds_addr_of(smem), main_off, rope_off, w, lane);
+    for (int i = 0; i < n; ++i) op(i, kv, s, lds_addr_of(smem), main_off, rope_off, w, lane);
   }
 };
 
@@ -254,8 +279,12 @@ __device__ __forceinline__ void mfma_qk_first(f32x16& d, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma_qk(f32x16& d, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma_qk_last(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3" : "+v"(d) : "v"(a), "v"(b));
+// The last link writes its own output operand: the chain's accumulator is
+// then only an input, so the compiler never needs to move it between links to
+// place the result.
+__device__ __forceinline__ void mfma_qk_last(f32x16& out, const f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\ts_nop 7\n\ts_nop 3"
+               : "=&v"(out) : "v"(a), "v"(b), "v"(acc));
 }
 
 // Per-lane LDS addressing, fixed for a work item.
@@ -489,19 +518,29 @@ __device__ __forceinline__ void pv_product(const lds_u8* smem, const LaneAddr& l
   if (kk == 0 && ct == 3) pb[rb] = p_frag(smem, la, pbuf, rb, 1);
 }
 
-// One pipeline step: QK(t) with the K tile in (kmain, krope) into s, then the
-// softmax of tile t (masked by lim) published as P^T in pwrite; PV(t-1) with V
-// in vmain and P^T in pbuf. dma(i), i < NDMA, issues later tiles' loads. The first kPvEarly PV products are paired with the 36 QK products
-// (one QK product per slot); the rest run between the softmax's pieces once
-// the scores are complete. A sched_barrier ends every slot, so the compiler
-// keeps this order; K fragments are read kKDepth products ahead.
+// One pipeline step t, in two phases split by a barrier.
+//   Phase A: QK(t) (if QK) from the K tile in (kmain, krope); the softmax
+//     of tile t-1 (if PREV; scores in s_old, masked by lim_old)
+//     runs between its products, one piece every kSmStride slots, and
+//     publishes P^T(t-1) in pbuf. The matrix core works on QK(t) while the
+//     VALU works on the softmax. The last QK product writes the scores of
+//     tile t into s_old (the softmax has ended by then); the chain itself
+//     accumulates in a variable local to the step.
+//   Barrier: P^T(t-1) of every wave is visible.
+//   Phase B: PV(t-1) (if PREV) with V in vmain and P^T in pbuf; dma(i),
+//     i < NDMA, issues later tiles' loads, one every kDmaStride products.
+// A sched_barrier ends every slot, so the compiler keeps this order. K
+// fragments are read kKDepth products ahead.
 constexpr int kKDepth = 5;
-constexpr int kPvEarly = 20;
-template <bool QK, bool PV, int NDMA, bool KV_FP8, bool FAST, typename Dma>
+constexpr int kSmStride = 2;
+constexpr int kDmaStride = 3;
+template <bool QK, bool PREV, int NDMA, bool KV_FP8, bool FAST, typename Dma>
 __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, const bf16x8 (&qf)[kKSteps],
-                                              int kmain, int krope, f32x16& s_acc, Softmax& sm, float score_c,
-                                              int lim, RowState& rs, int pwrite, int vmain, int pbuf,
+                                              int kmain, int krope, f32x16& s_old, float score_c,
+                                              int lim_old, RowState& rs, int pbuf, int vmain,
                                               f32x16 (&oacc)[kRowBlocks][kColTiles], Dma&& dma) {
+  static_assert(kSmStride * kSoftmaxPieces <= kKSteps, "softmax pieces fit between the QK products");
+  static_assert(NDMA == 0 || kDmaStride * (NDMA - 1) < 32, "loads fit between the PV products");
   // bf16 K: fragments read kKDepth products ahead. fp8 K: 16-byte pairs read
   // kRawDepth pairs ahead and each k-step converted two products ahead of its
   // MFMA (so the conversion's VALU writes are far from the assembly MFMA
@@ -509,8 +548,8 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
   constexpr int kRawDepth = 3;
   bf16x8 kb[kKDepth];
   u32x4 raw[kRawDepth];
-  bf16x8 pb[kRowBlocks];
-  bf16x8 vb[2];
+  Softmax sm;
+  f32x16 s_cur;
   if constexpr (QK) {
     if constexpr (!KV_FP8) {
 #pragma unroll
@@ -523,16 +562,10 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
       raw[0] = k_pair_f8(smem, la, kmain, krope, kRawDepth);   // pair 0 is consumed
     }
   }
-  if constexpr (PV) {
-#pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) pb[rb] = p_frag(smem, la, pbuf, rb, 0);
-    if constexpr (KV_FP8) vb[0] = v_frag_f8(smem, la, vmain, 0, 0);
-    else vb[0] = v_frag(smem, la, vmain, 0, 0);
-  }
   __builtin_amdgcn_sched_barrier(0);
+  constexpr int kSlotsA = QK ? kKSteps : kSoftmaxPieces * kSmStride;
 #pragma unroll
-  for (int s = 0; s < kKSteps; ++s) {
-    if (s < NDMA) dma(s);
+  for (int s = 0; s < kSlotsA; ++s) {
     if constexpr (QK) {
       bf16x8 a;
       if constexpr (!KV_FP8) {
@@ -548,29 +581,42 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
             raw[pj % kRawDepth] = k_pair_f8(smem, la, kmain, krope, pj + kRawDepth);
         }
       }
-      if (s == 0) mfma_qk_first(s_acc, a, qf[s]);
-      else if (s + 1 < kKSteps) mfma_qk(s_acc, a, qf[s]);
-      else mfma_qk_last(s_acc, a, qf[s]);
+      if (s == 0) mfma_qk_first(s_cur, a, qf[s]);
+      else if (s + 1 < kKSteps) mfma_qk(s_cur, a, qf[s]);
+      else mfma_qk_last(s_old, s_cur, a, qf[s]);   // s_old is dead: the softmax ended
     }
-    if constexpr (PV) {
-      if (s < kPvEarly) pv_product<KV_FP8>(smem, la, vmain, pbuf, s, vb, pb, oacc);
+    if constexpr (PREV) {
+      if (s % kSmStride == 0 && s / kSmStride < kSoftmaxPieces)
+        softmax_piece<FAST>(s / kSmStride, sm, s_old, score_c, lim_old, rs);
+      if (s == kSmStride * kSoftmaxPieces) {   // publish P^T(t-1) of this wave's rows
+        lds_store(smem, pbuf + (la.w * 2 + 0) * 1024 + la.pl, sm.pf[0]);
+        lds_store(smem, pbuf + (la.w * 2 + 1) * 1024 + la.pl, sm.pf[1]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  constexpr int kTail = (32 - kPvEarly) > kSoftmaxPieces ? (32 - kPvEarly) : kSoftmaxPieces;
+  if constexpr (PREV) {
+    if constexpr (!QK) {   // the last step: the slot loop ended with the last piece
+      lds_store(smem, pbuf + (la.w * 2 + 0) * 1024 + la.pl, sm.pf[0]);
+      lds_store(smem, pbuf + (la.w * 2 + 1) * 1024 + la.pl, sm.pf[1]);
+    }
+  }
+  if constexpr (PREV) __syncthreads();   // P^T(t-1) of all rows is visible
+  // Phase B.
+  bf16x8 pb[kRowBlocks];
+  bf16x8 vb[2];
+  if constexpr (PREV) {
 #pragma unroll
-  for (int j = 0; j < kTail; ++j) {
-    if constexpr (PV) {
-      if (kPvEarly + j < 32) pv_product<KV_FP8>(smem, la, vmain, pbuf, kPvEarly + j, vb, pb, oacc);
-    }
-    if constexpr (QK) {
-      if (j < kSoftmaxPieces) softmax_piece<FAST>(j, sm, s_acc, score_c, lim, rs);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    for (int rb = 0; rb < kRowBlocks; ++rb) pb[rb] = p_frag(smem, la, pbuf, rb, 0);
+    if constexpr (KV_FP8) vb[0] = v_frag_f8(smem, la, vmain, 0, 0);
+    else vb[0] = v_frag(smem, la, vmain, 0, 0);
   }
-  if constexpr (QK) {   // publish P^T of this wave's rows (read after the step's barrier)
-    lds_store(smem, pwrite + (la.w * 2 + 0) * 1024 + la.pl, sm.pf[0]);
-    lds_store(smem, pwrite + (la.w * 2 + 1) * 1024 + la.pl, sm.pf[1]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < 32; ++p) {
+    if (p % kDmaStride == 0 && p / kDmaStride < NDMA) dma(p / kDmaStride);
+    if constexpr (PREV) pv_product<KV_FP8>(smem, la, vmain, pbuf, p, vb, pb, oacc);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -685,32 +731,32 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         else wait_vm<1>();
         __syncthreads();
 
-        f32x16 s_acc;
-        Softmax sm;
-        // Step t: QK(t) and the softmax of tile t if t < ntiles, PV(t-1) if
-        // t >= 1; the loads of tile t+2 are issued first. The step ends with
-        // P(t) stored, this wave's loads of tile t+1 landed and one barrier.
-        // DMA: this step issues tile t+2's loads (t + 2 < ntiles); it is a
-        // template flag, so the hot loop carries no per-load branch.
-        auto run_step = [&](int t, auto QKc, auto PVc, auto DMAc, auto FASTc) {
-          constexpr bool DO_QK = decltype(QKc)::value, DO_PV = decltype(PVc)::value;
+        // s_old: the previous tile's scores, consumed by its softmax in the
+        // next step.
+        f32x16 s_old;
+        // Step t: QK(t) if t < ntiles, the softmax of tile t-1 and PV(t-1) if
+        // t >= 1; tile t+2's loads are issued in phase B. The step ends with
+        // this wave's loads of tile t+1 landed and one barrier. QK, PREV and
+        // DMA are template flags, so the hot loop carries no per-slot branch;
+        // FAST selects the unmasked softmax for tile t-1.
+        auto run_step = [&](int t, auto QKc, auto PREVc, auto DMAc, auto FASTc) {
+          constexpr bool DO_QK = decltype(QKc)::value, PREV = decltype(PREVc)::value;
           constexpr bool DO_DMA = decltype(DMAc)::value, FAST = decltype(FASTc)::value;
           const int dlane = opaque(lane);
           issue_slots(a.kv_indices, kv0, begin, end, t + 4, smem, w, dlane);
-          constexpr bool have = DO_DMA;
-          const int slot = have ? read_slots(smem, t + 2, w, dlane) : 0;
+          const TileSrc<KV_FP8> src = Dma::src(kv, DO_DMA ? read_slots(smem, t + 2, w, dlane) : 0, w, dlane);
           const int dm = dma_main<KV_FP8>(t + 2), dr = dma_rope<KV_FP8>(t + 2);
           auto dma = [&](int i) {
-            Dma::op(i, kv, slot, lds_addr_of(smem), dm, dr, w, dlane);
+            Dma::op(i, kv, src, lds_addr_of(smem), dm, dr, w, dlane);
           };
-          const int lim = key_last - (begin + t * kNT + 4 * (lane >> 5));
+          const int lim_old = key_last - (begin + (t - 1) * kNT + 4 * (lane >> 5));
           const LaneAddr la_s = lane_addr<KV_FP8>(dlane, w);
-          pipeline_step<DO_QK, DO_PV, DO_DMA ? Dma::n : 0, KV_FP8, FAST>(smem, la_s, qf, LY::main(t), LY::rope(t),
-                                                                  s_acc, sm, score_c, lim, rs, p_buf(t),
-                                                                  LY::main(t + 11), p_buf(t + 1), oacc, dma);
-          if (have) wait_vm<1 + Dma::n>();
+          pipeline_step<DO_QK, PREV, DO_DMA ? Dma::n : 0, KV_FP8, FAST>(
+              smem, la_s, qf, LY::main(t), LY::rope(t), s_old, score_c, lim_old, rs, p_buf(t + 1),
+              LY::main(t + 11), oacc, dma);
+          if (DO_DMA) wait_vm<1 + Dma::n>();
           else wait_vm<1>();
-          __syncthreads();   // tile t+1 landed; P(t) published; tile t-1 and P(t-1) are free
+          __syncthreads();   // tile t+1 landed; tile t-1 and P(t-1) are free
         };
         using T_ = std::true_type;
         using F_ = std::false_type;
@@ -725,7 +771,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
             wave_min_i32(key_last - begin - 4 * (lane >> 5) - 27));
         const int nfast = score_c > 0.f && slack >= 0 ? slack / kNT + 1 : 0;
         int t = 1;
-        for (; t + 2 < ntiles && t < nfast; ++t) run_step(t, T_{}, T_{}, T_{}, T_{});
+        for (; t + 2 < ntiles && t - 1 < nfast; ++t) run_step(t, T_{}, T_{}, T_{}, T_{});
         for (; t + 2 < ntiles; ++t) run_step(t, T_{}, T_{}, T_{}, F_{});
         for (t = ntiles > 3 ? ntiles - 2 : 1; t < ntiles; ++t) run_step(t, T_{}, T_{}, F_{}, F_{});
         run_step(ntiles, F_{}, T_{}, F_{}, F_{});
