@@ -7,7 +7,7 @@ the row count and config, so graph capture and replay agree (same section);
 the persistent kernel instead plans from the real per-row KV lengths on every
 call (same page, "Summary", part 2), and its gate is fp8 KV, 128 local heads
 and 15 <= rows <= 32768. The constants and tie-breaks below are this
-library's own choice (spec version 1); the library's C++ planner must produce
+library's own choice (spec version 2); the library's C++ planner must produce
 the same int32 words.
 
 Constants: M_UNIT 128 query rows per work item, N_MAX 256 splits per row,
