@@ -35,22 +35,22 @@
 // {4g..4g+3, 8+4g..8+4g+3} for lane half g, so P never needs a register
 // shuffle; the V^T reads use the same key order.
 //
-// The three stages form a software pipeline with one barrier per tile: step t
-// runs QK(t), the softmax of tile t-1 and PV(t-2), slot by slot -- each of the
-// 36 QK MFMAs is paired with one of the 32 PV MFMAs, and the softmax's VALU
-// work, the LDS reads for later slots and the next tile's loads are spread
-// between them -- so the matrix core, the VALU and the LDS work at the same
-// time inside one wave.
+// The stages form a software pipeline of one step per tile, in two phases
+// split by a barrier: phase A of step t runs the 36 QK products of tile t
+// with the softmax of tile t-1 spread between them (VALU work beside the
+// matrix core) and publishes P^T(t-1); phase B runs the 32 PV products of
+// tile t-1 with the loads of tile t+2 spread between them.
 //
-// fp8 KV is fetched as fp8 (half the HBM bytes) into a staging tile and
-// converted once per tile to a bf16 tile (exact: every e4m3fn value is a bf16
-// value), so the compute core is the same for all dtypes. Scales are applied
-// to the fp32 scores and to O.
+// fp8 KV stays fp8 in LDS (half the HBM and LDS bytes) and is converted to
+// bf16 in registers when a K or V^T fragment is read (exact: every e4m3fn
+// value is a bf16 value), so the matrix core always computes in bf16. Scales
+// are applied to the fp32 scores and to O.
 //
 // The epilogue writes bf16 O and the natural-log LSE when the row has one
-// split, or the split's fp32 partial (O_k, LSE_k) to the workspace; the merge
-// kernel then combines a row's partials by log-sum-exp ([DSV4] Tuned ASM FP8
-// decode with split plans, ATOM pull request 2462, Dependencies).
+// split, or the split's normalized bf16 partial O and fp32 LSE_k to the
+// workspace; the merge kernel then combines a row's partials by log-sum-exp
+// ([DSV4] Tuned ASM FP8 decode with split plans, ATOM pull request 2462,
+// Dependencies).
 //
 // LDS tile layout (bf16): a "main" array of 32 rows x 1024 bytes (latent dims
 // 0..511, which are also V) and a "rope" array of 32 rows x 128 bytes (dims
@@ -65,10 +65,10 @@
 // different sectors. The swizzle is applied on the global side of each load
 // (the LDS side of a direct load is fixed to consecutive 16-byte chunks).
 //
-// Loads run one tile ahead: step t issues tile t+1's loads first, and every
-// wave waits for its own before the barrier that ends the step. The loads are
-// inline assembly, so the compiler neither waits for them early nor tracks
-// them.
+// Loads run two tiles ahead: step t issues tile t+2's loads, and every wave
+// waits for its own loads of tile t+1 before the barrier that ends the step.
+// The loads are inline assembly, so the compiler neither waits for them early
+// nor tracks them.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <type_traits>
@@ -102,9 +102,8 @@ constexpr int kWaveCols = kDV / kWaves;       // 128 output columns per wave
 constexpr int kColTiles = kWaveCols / 32;     // 4
 constexpr int kSlotRing = 4;                  // per-wave ring of tile slot lists
 constexpr int kPBytes = kRowBlocks * 2 * 64 * 16;     // P^T of one tile: [4 row blocks][2 key halves][64 lanes] bf16x8
-// bf16 KV: main tiles t-1 (PV), t (QK), t+1, t+2 (loads in flight) and rope
-// tiles t, t+1, t+2. fp8 KV: fp8 staging tiles t, t+1, t+2, bf16 main tiles
-// t-1, t and rope tiles t-1, t.
+// Main tiles t-1 (PV), t (QK), t+1, t+2 (loads in flight) and rope tiles t,
+// t+1, t+2, in the KV dtype (fp8 tiles are half the size).
 constexpr int kMainBufs = 4, kRopeBufs = 3;
 constexpr int kTilesEnd = 143360;             // end of the tile region for either KV dtype
 static_assert(kMainBufs * kMainBytes + kRopeBufs * kRopeBytes <= kTilesEnd, "bf16 tiles");
@@ -451,7 +450,7 @@ constexpr int kSoftmaxPieces = 13;
 
 // ---------------------------------------------------------------------------
 // In-kernel merge of one (row b, M tile m): rows m 128 .. m 128 + 127 of the
-// row's block, n <= kMaxInKernelSplits fp32 partials each (consecutive
+// row's block, n <= kMaxInKernelSplits bf16 partials each (consecutive
 // partial slots from part0). Thread tid takes 32 (row, 8-column chunk) pairs.
 __device__ __forceinline__ void merge_tile(const DecodeArgs& a, int m, int M, int n, int part0,
                                            int q0, int tid) {

@@ -21,7 +21,7 @@ constexpr int32_t kItemOverhead = 256;
 constexpr int32_t kOcc = 1;
 constexpr int32_t kXcds = 8;
 
-// Workspace layout: the fp32 partial O and LSE of the split rows; with an
+// Workspace layout: the bf16 partial O and fp32 LSE of the split rows; with an
 // in-kernel-merge plan, a fixed region of split-arrival counters (one per
 // request row and M tile, zero between calls) comes first. With such a plan,
 // rows with at most kMaxInKernelSplits splits are merged inside the decode
