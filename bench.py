@@ -32,9 +32,14 @@ KERNEL_SRCS = [os.path.join(ROOT, "paged_mla_decode_02_amd", "csrc", f) for f in
 
 
 def kernel_sha():
+    """Hash of the kernel code: the sources with // comments and blank lines
+    dropped, so a comment edit does not invalidate a traffic record."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        h.update(open(path, "rb").read())
+        for line in open(path, encoding="utf-8"):
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
