@@ -15,33 +15,34 @@ namespace {
 using namespace dev;
 
 constexpr int kDV = 512;
-constexpr int kChunk = 8;   // partials whose loads a lane has in flight at once
+constexpr int kChunk = 8;        // splits whose loads a lane has in flight at once (n <= 8)
+constexpr int kChunkWide = 16;   // the same for rows with more splits
 
 // ---------------------------------------------------------------------------
 // Split merge: one block of four waves per (request row b, query token i,
-// heads 4 j .. 4 j + 3) of a row with n > 1 splits. A lane owns 8 of the 512
-// output columns. The split partials are merged by log-sum-exp, online, in
-// chunks of kChunk splits: a chunk's partial-O loads and LSE loads are issued
-// together (the LSE addresses are wave-uniform, so those are scalar loads),
-// so a chunk costs one memory round trip; the running (max, sum, O) are
-// rescaled when a chunk raises the max. With n <= kChunk splits each wave
-// merges one head in one round trip; with more, the four waves of the block
-// take every fourth split of one head at a time and combine their running
-// states through LDS.
+// heads 4 j .. 4 j + 3) of a row with n > 1 splits; each wave merges one
+// head, a lane owning 8 of the 512 output columns. The split partials are
+// merged by log-sum-exp, online, in chunks: a chunk's partial-O loads and LSE
+// loads are issued together (the LSE addresses are wave-uniform), so a chunk
+// costs one memory round trip, and the running (max, sum, O) are rescaled
+// when a chunk raises the max. A row with n <= 8 splits takes one round trip;
+// more splits go in chunks of 16, so the four heads of a block proceed in
+// parallel with ceil(n / 16) round trips each.
 struct MergeState {
   float m, l;       // running max of LSE_k, and sum of exp(LSE_k - m)
   f32x4 acc0, acc1; // sum of exp(LSE_k - m) O_k over this lane's 8 columns
 };
 
-// Splits k = k0 + j kstep, j < kChunk, k < n, of the partial rows at `src`
-// (this lane's 8 columns) and `lse_base` (uniform), folded into st.
+// Splits k = k0 + j, j < C, k < n, of the partial rows at `src` (this lane's
+// 8 columns) and `lse_base` (uniform), folded into st.
+template <int C>
 __device__ __forceinline__ void merge_chunk(const uint16_t* src, const float* lse_base, int64_t stride, int k0,
-                                            int kstep, int n, MergeState& st) {
-  bf16x8 v[kChunk];
-  float lk[kChunk];
+                                            int n, MergeState& st) {
+  bf16x8 v[C];
+  float lk[C];
 #pragma unroll
-  for (int j = 0; j < kChunk; ++j) {
-    const int k = k0 + j * kstep;
+  for (int j = 0; j < C; ++j) {
+    const int k = k0 + j;
     if (k < n) {
       v[j] = *(const bf16x8*)(src + (int64_t)k * stride * kDV);
       lk[j] = lse_base[(int64_t)k * stride];
@@ -51,7 +52,7 @@ __device__ __forceinline__ void merge_chunk(const uint16_t* src, const float* ls
   }
   float cm = lk[0];
 #pragma unroll
-  for (int j = 1; j < kChunk; ++j) cm = fmaxf(cm, lk[j]);
+  for (int j = 1; j < C; ++j) cm = fmaxf(cm, lk[j]);
   if (cm == -INFINITY) return;   // every split of the chunk is empty (uniform)
   const float mnew = fmaxf(st.m, cm);
   if (mnew > st.m) {   // uniform
@@ -62,7 +63,7 @@ __device__ __forceinline__ void merge_chunk(const uint16_t* src, const float* ls
     st.m = mnew;
   }
 #pragma unroll
-  for (int j = 0; j < kChunk; ++j) {
+  for (int j = 0; j < C; ++j) {
     if (lk[j] != -INFINITY) {   // an empty split's partial O is 0 and carries no weight
       const float c = __builtin_amdgcn_exp2f((lk[j] - mnew) * kLog2e);
       st.l += c;
@@ -90,8 +91,6 @@ __device__ __forceinline__ void store_merged(const MergeArgs& a, int64_t orow, i
 
 __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
   constexpr int kW = kBlockThreads / 64;
-  __shared__ f32x4 part_acc[kW - 1][64][2];
-  __shared__ float part_ml[kW - 1][2];
   const int hgroups = (a.heads + kW - 1) / kW;
   const int hg = blockIdx.x % hgroups;
   const int bi = blockIdx.x / hgroups;
@@ -104,60 +103,19 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
   if (i >= a.qo_indptr[b + 1] - q0) return;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = hg * kW + w;
+  if (h >= a.heads) return;
   const int part0 = a.plan[a.off_split_part + s0];
   const int64_t stride = (int64_t)a.q_len_max * a.heads;   // partial slots are consecutive
-
-  if (n <= kChunk) {   // one wave per head, one round trip (uniform over the block: n is the row's)
-    const int h = hg * kW + w;
-    if (h >= a.heads) return;
-    const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
-    MergeState st{-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    merge_chunk(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, 0, 1, n, st);
-    store_merged(a, (int64_t)(q0 + i) * a.heads + h, lane, st);
-    return;
+  const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
+  MergeState st{-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  if (n <= kChunk) {   // uniform over the block: n is the row's
+    merge_chunk<kChunk>(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, 0, n, st);
+  } else {
+    for (int k0 = 0; k0 < n; k0 += kChunkWide)
+      merge_chunk<kChunkWide>(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, k0, n, st);
   }
-
-  for (int hh = 0; hh < kW; ++hh) {   // four waves per head, one head at a time
-    const int h = hg * kW + hh;
-    if (h >= a.heads) break;          // uniform
-    const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
-    MergeState st{-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    for (int k0 = w; k0 < n; k0 += kChunk * kW)
-      merge_chunk(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, k0, kW, n, st);
-    if (w > 0) {
-      part_acc[w - 1][lane][0] = st.acc0;
-      part_acc[w - 1][lane][1] = st.acc1;
-      if (lane == 0) {
-        part_ml[w - 1][0] = st.m;
-        part_ml[w - 1][1] = st.l;
-      }
-    }
-    __syncthreads();
-    if (w == 0) {
-      float M = st.m;
-#pragma unroll
-      for (int j = 0; j < kW - 1; ++j) M = fmaxf(M, part_ml[j][0]);
-      if (M != -INFINITY) {
-        const float r = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - M) * kLog2e);
-        st.l *= r;
-        st.acc0 *= r;
-        st.acc1 *= r;
-#pragma unroll
-        for (int j = 0; j < kW - 1; ++j) {
-          const float mj = part_ml[j][0];
-          if (mj != -INFINITY) {
-            const float c = __builtin_amdgcn_exp2f((mj - M) * kLog2e);
-            st.l += c * part_ml[j][1];
-            st.acc0 += c * part_acc[j][lane][0];
-            st.acc1 += c * part_acc[j][lane][1];
-          }
-        }
-      }
-      st.m = M;
-      store_merged(a, (int64_t)(q0 + i) * a.heads + h, lane, st);
-    }
-    __syncthreads();   // the LDS states are reused for the next head
-  }
+  store_merged(a, (int64_t)(q0 + i) * a.heads + h, lane, st);
 }
 
 // ---------------------------------------------------------------------------
