@@ -365,12 +365,18 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return cat(fp8x4_to_bf16(lo), fp8x4_to_bf16(hi));
 }
 
-// fp8 V^T fragment (kk, ct): one transposed 8-byte read, converted.
-__device__ __forceinline__ bf16x8 v_frag_f8(const lds_u8* smem, const LaneAddr& la, int vmain, int kk, int ct) {
+// fp8 V^T fragment (kk, ct): one transposed 8-byte read (v_raw_f8), converted
+// (v_frag_f8). The PV loop reads a fragment four products ahead and converts
+// it two products ahead, so the conversion never waits on the read.
+__device__ __forceinline__ u32x2 v_raw_f8(const lds_u8* smem, const LaneAddr& la, int vmain, int kk, int ct) {
   typedef int i32x2 __attribute__((ext_vector_type(2)));
   const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
       (__attribute__((address_space(3))) i32x2*)(smem + vmain + 16 * kF8MainRow * kk + (la.va ^ (ct << 5))));
-  return fp8x8_to_bf16((uint32_t)v[0], (uint32_t)v[1]);
+  return u32x2{(uint32_t)v[0], (uint32_t)v[1]};
+}
+__device__ __forceinline__ bf16x8 v_frag_f8(const lds_u8* smem, const LaneAddr& la, int vmain, int kk, int ct) {
+  const u32x2 v = v_raw_f8(smem, la, vmain, kk, ct);
+  return fp8x8_to_bf16(v[0], v[1]);
 }
 
 // V^T fragment for PV MFMAs (kk, ct): two transposed 8-byte reads. The XOR
@@ -506,12 +512,15 @@ __device__ __forceinline__ void merge_tile(const DecodeArgs& a, int m, int M, in
 // row block replaces key half 0's after its last use.
 template <bool KV_FP8>
 __device__ __forceinline__ void pv_product(const lds_u8* smem, const LaneAddr& la, int vmain, int pbuf, int p,
-                                           bf16x8 (&vb)[2], bf16x8 (&pb)[kRowBlocks],
+                                           bf16x8 (&vb)[2], u32x2& vraw, bf16x8 (&pb)[kRowBlocks],
                                            f32x16 (&oacc)[kRowBlocks][kColTiles]) {
   const int kk = p >> 4, ct = (p >> 2) & 3, rb = p & 3;
   if (rb == 0 && p + 4 < 32) {
-    if constexpr (KV_FP8) vb[((p >> 2) + 1) & 1] = v_frag_f8(smem, la, vmain, (p + 4) >> 4, ((p + 4) >> 2) & 3);
+    if constexpr (KV_FP8) vraw = v_raw_f8(smem, la, vmain, (p + 4) >> 4, ((p + 4) >> 2) & 3);
     else vb[((p >> 2) + 1) & 1] = v_frag(smem, la, vmain, (p + 4) >> 4, ((p + 4) >> 2) & 3);
+  }
+  if constexpr (KV_FP8) {
+    if (rb == 2 && p + 2 < 32) vb[((p >> 2) + 1) & 1] = fp8x8_to_bf16(vraw[0], vraw[1]);
   }
   oacc[rb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[(p >> 2) & 1], pb[rb], oacc[rb][ct], 0, 0, 0);
   if (kk == 0 && ct == 3) pb[rb] = p_frag(smem, la, pbuf, rb, 1);
@@ -604,6 +613,7 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
   // Phase B.
   bf16x8 pb[kRowBlocks];
   bf16x8 vb[2];
+  u32x2 vraw;
   if constexpr (PREV) {
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) pb[rb] = p_frag(smem, la, pbuf, rb, 0);
@@ -614,7 +624,7 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
 #pragma unroll
   for (int p = 0; p < 32; ++p) {
     if (p % kDmaStride == 0 && p / kDmaStride < NDMA) dma(p / kDmaStride);
-    if constexpr (PREV) pv_product<KV_FP8>(smem, la, vmain, pbuf, p, vb, pb, oacc);
+    if constexpr (PREV) pv_product<KV_FP8>(smem, la, vmain, pbuf, p, vb, vraw, pb, oacc);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
