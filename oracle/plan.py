@@ -7,7 +7,7 @@ the row count and config, so graph capture and replay agree (same section);
 the persistent kernel instead plans from the real per-row KV lengths on every
 call (same page, "Summary", part 2), and its gate is fp8 KV, 128 local heads
 and 15 <= rows <= 32768. The constants and tie-breaks below are this
-library's own choice (spec version 2); the library's C++ planner must produce
+library's own choice (spec version 3); the library's C++ planner must produce
 the same int32 words.
 
 Constants: M_UNIT 128 query rows per work item, N_MAX 256 splits per row,
@@ -24,22 +24,29 @@ Steps:
 3. UNIFORM: n = clamp(min(cdiv(OCC*C, R*u), cdiv(max L, MIN_SPLIT_KEYS)), 1,
    N_MAX); every row gets n splits; split k of row b covers keys
    [k*L_b // n, (k+1)*L_b // n) (empty ranges are legal).
-4. LENGTH_AWARE cuts the concatenated key ranges of all rows into lanes of
-   equal cost. A lane is u workgroups on one chiplet that run the same splits,
-   one M tile each, so the u tiles of a split read its keys from one L2 at
-   about the same time. X starts at XCDS and halves while (OCC*C) // X < u;
+4. LENGTH_AWARE packs the rows' key ranges into lanes of equal capacity. A
+   lane is u workgroups on one chiplet that run the same splits, one M tile
+   each, so the u tiles of a split read its keys from one L2 at about the
+   same time. X starts at XCDS and halves while (OCC*C) // X < u;
    n_x = (OCC*C) // X slots per chiplet; lam = max(1, n_x // u) lanes per
    chiplet; LAMBDA = X * lam lanes. Lane l (chiplet x = l mod X, k = l // X)
    has members j = 0..u-1, workgroup x + X*(k*u + j).
    Lane capacity T = max(MIN_SPLIT_KEYS + ITEM_OVERHEAD,
    cdiv(sum L + ITEM_OVERHEAD*(R + LAMBDA), LAMBDA),
-   cdiv(max L, N_MAX - 1) + ITEM_OVERHEAD). A split costs its keys plus
-   ITEM_OVERHEAD. Walk the rows in order with lane l = 0 and cap = T: a row
-   with L_b = 0 gets one empty split [0, 0) in lane l; otherwise, while keys
-   s < L_b remain: if cap <= ITEM_OVERHEAD and l < LAMBDA - 1, move to the
-   next lane (cap = T); the split takes n = L_b - s keys in the last lane,
-   else n = min(L_b - s, cap - ITEM_OVERHEAD); cap -= n + ITEM_OVERHEAD.
-   Split ids follow creation order (rows in order, keys ascending).
+   cdiv(max L, N_MAX - 1) + ITEM_OVERHEAD); every lane starts with room T.
+   A split costs its keys plus ITEM_OVERHEAD. Rows are taken longest first
+   (ties by row index); "the roomiest lane" is the lane with the most room,
+   the lowest index among equals.
+   - A row with L_b = 0 gets one empty split [0, 0) in the roomiest lane;
+     its room is unchanged.
+   - Otherwise, while keys s < L_b remain, with l the roomiest lane and
+     r = room[l] - ITEM_OVERHEAD: if r >= L_b - s, or r < MIN_SPLIT_KEYS, or
+     the row already has N_MAX - 1 splits, the split takes the rest
+     (n = L_b - s); else it takes n = r. room[l] -= n + ITEM_OVERHEAD.
+   So a row is cut only where a lane is full, a lane ends at most one row
+   that continues elsewhere, and most rows stay whole.
+   Split ids are then assigned in (row, first key) order, so each row's
+   splits are consecutive; a lane's splits are listed in id order.
 5. split_indptr is the running count of splits per row. Splits of rows with
    more than one split get partial-buffer slots 0, 1, 2, ... in split order;
    the others get -1.
@@ -64,7 +71,7 @@ Steps:
 import numpy as np
 
 MAGIC = 0x4D4C4150
-VERSION = 2
+VERSION = 3
 HEADER_WORDS = 20
 M_UNIT = 128
 N_MAX = 256
@@ -128,26 +135,42 @@ def plan_ref(kv_lens, H, q_len_max, kv_dtype, mode, C):
         n_lanes = X * lam
         T = max(MIN_SPLIT_KEYS + ITEM_OVERHEAD, cdiv(sum(lens) + ITEM_OVERHEAD * (R + n_lanes), n_lanes),
                 cdiv(max(lens), N_MAX - 1) + ITEM_OVERHEAD)
-        lane_splits = [[] for _ in range(n_lanes)]
-        lane, cap = 0, T
-        for b, L in enumerate(lens):
+        room = [T] * n_lanes
+        pieces = []   # (row, begin, end, lane) in creation order
+
+        def roomiest():
+            best = 0
+            for l in range(1, n_lanes):
+                if room[l] > room[best]:
+                    best = l
+            return best
+
+        order = sorted(range(R), key=lambda b: (-lens[b], b))
+        for b in order:
+            L = lens[b]
             if L == 0:
-                lane_splits[lane].append(len(split_row))
-                split_row.append(b)
-                split_begin.append(0)
-                split_end.append(0)
+                pieces.append((b, 0, 0, roomiest()))
                 continue
-            pos = 0
+            pos, count = 0, 0
             while pos < L:
-                if cap <= ITEM_OVERHEAD and lane < n_lanes - 1:
-                    lane, cap = lane + 1, T
-                take = L - pos if lane == n_lanes - 1 else min(L - pos, cap - ITEM_OVERHEAD)
-                lane_splits[lane].append(len(split_row))
-                split_row.append(b)
-                split_begin.append(pos)
-                split_end.append(pos + take)
+                lane = roomiest()
+                r = room[lane] - ITEM_OVERHEAD
+                if r >= L - pos or r < MIN_SPLIT_KEYS or count == N_MAX - 1:
+                    take = L - pos
+                else:
+                    take = r
+                pieces.append((b, pos, pos + take, lane))
+                room[lane] -= take + ITEM_OVERHEAD
                 pos += take
-                cap -= take + ITEM_OVERHEAD
+                count += 1
+        # split ids in (row, first key) order; lanes list their splits by id
+        pieces.sort(key=lambda p: (p[0], p[1]))
+        lane_splits = [[] for _ in range(n_lanes)]
+        for s_id, (b, lo, hi, lane) in enumerate(pieces):
+            split_row.append(b)
+            split_begin.append(lo)
+            split_end.append(hi)
+            lane_splits[lane].append(s_id)
     S = len(split_row)
     nsplit = [0] * R
     for b in split_row:

@@ -1,4 +1,4 @@
-// Host split planner (plan spec version 2).
+// Host split planner (plan spec version 3).
 //
 // A plan is a split count and split_indptr per request row, built on the host
 // next to the decode CSR ([DSV4] Tuned ASM FP8 decode with split plans, ATOM
@@ -13,10 +13,11 @@
 // they run on one chiplet (XCD) and share its L2. UNIFORM ranks splits
 // longest first, deals them to the eight chiplets and launches one workgroup
 // per item, ordering workgroup ids so that the hardware's round-robin
-// dispatch over chiplets lands each chiplet's items on it. LENGTH_AWARE cuts
-// the concatenated key ranges of all rows into lanes of equal cost -- a lane
-// being u workgroups of one chiplet that run the same splits, one M tile
-// each -- and launches those workgroups persistently.
+// dispatch over chiplets lands each chiplet's items on it. LENGTH_AWARE packs
+// the rows, longest first, into lanes of equal capacity -- a lane being u
+// workgroups of one chiplet that run the same splits, one M tile each --
+// cutting a row only where a lane is full, and launches those workgroups
+// persistently.
 #include <algorithm>
 #include <cstring>
 #include <numeric>
@@ -152,8 +153,9 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
       }
   } else {
     // Lanes: u workgroups of one chiplet that run the same splits, one M
-    // tile each; the concatenated key ranges of all rows are cut into lanes
-    // of equal cost (keys + kItemOverhead per split).
+    // tile each, all with room T (keys + kItemOverhead per split). Rows go
+    // longest first (ties by index) to the roomiest lane (lowest index among
+    // equals); a row is cut only where that lane is full.
     const int64_t slots = (int64_t)kOcc * num_cus;
     while (X > 1 && slots / X < u) X /= 2;
     const int64_t lam = std::max<int64_t>(1, (slots / X) / u);
@@ -161,30 +163,46 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
     const int64_t T = std::max({(int64_t)kMinSplitKeys + kItemOverhead,
                                 cdiv(sum_len + (int64_t)kItemOverhead * (rows + n_lanes), n_lanes),
                                 cdiv(max_len, kNMax - 1) + kItemOverhead});
-    lane_splits.resize(n_lanes);
-    int64_t lane = 0, cap = T;
-    for (int32_t b = 0; b < rows; ++b) {
+    std::vector<int64_t> room(n_lanes, T);
+    auto roomiest = [&]() {
+      int64_t best = 0;
+      for (int64_t l = 1; l < n_lanes; ++l)
+        if (room[l] > room[best]) best = l;
+      return best;
+    };
+    std::vector<int32_t> order(rows);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return kv_lens[a] > kv_lens[b]; });
+    struct Piece {
+      int32_t row, begin, end, lane;
+    };
+    std::vector<Piece> pieces;
+    pieces.reserve(rows + n_lanes);
+    for (int32_t b : order) {
       const int64_t L = kv_lens[b];
       if (L == 0) {
-        lane_splits[lane].push_back((int32_t)srow.size());
-        srow.push_back(b);
-        sbeg.push_back(0);
-        send.push_back(0);
+        pieces.push_back({b, 0, 0, (int32_t)roomiest()});
         continue;
       }
-      for (int64_t pos = 0; pos < L;) {
-        if (cap <= kItemOverhead && lane < n_lanes - 1) {
-          ++lane;
-          cap = T;
-        }
-        const int64_t take = lane == n_lanes - 1 ? L - pos : std::min(L - pos, cap - kItemOverhead);
-        lane_splits[lane].push_back((int32_t)srow.size());
-        srow.push_back(b);
-        sbeg.push_back((int32_t)pos);
-        send.push_back((int32_t)(pos + take));
+      int32_t count = 0;
+      for (int64_t pos = 0; pos < L; ++count) {
+        const int64_t lane = roomiest();
+        const int64_t r = room[lane] - kItemOverhead;
+        const int64_t take = (r >= L - pos || r < kMinSplitKeys || count == kNMax - 1) ? L - pos : r;
+        pieces.push_back({b, (int32_t)pos, (int32_t)(pos + take), (int32_t)lane});
+        room[lane] -= take + kItemOverhead;
         pos += take;
-        cap -= take + kItemOverhead;
       }
+    }
+    // Split ids in (row, first key) order; lanes list their splits by id.
+    std::sort(pieces.begin(), pieces.end(),
+              [](const Piece& a, const Piece& b) { return a.row != b.row ? a.row < b.row : a.begin < b.begin; });
+    lane_splits.resize(n_lanes);
+    for (const Piece& p : pieces) {
+      lane_splits[p.lane].push_back((int32_t)srow.size());
+      srow.push_back(p.row);
+      sbeg.push_back(p.begin);
+      send.push_back(p.end);
     }
   }
   const int32_t S = (int32_t)srow.size();

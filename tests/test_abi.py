@@ -134,10 +134,10 @@ def test_plan_argument_errors(lib):
 
 def test_workspace_size_formula(lib):
     w = lib_mod.plan([1000, 300, 5000, 0], 128, 1, 1, lib_mod.PLAN_LENGTH_AWARE, 4)
-    assert lib_mod.workspace_size(w) == 4 * 1 * 128 * (512 * 2 + 4)      # P = 4 partial slots
+    assert lib_mod.workspace_size(w) == 3 * 1 * 128 * (512 * 2 + 4)      # P = 3 partial slots (golden plan)
     w = lib_mod.plan([1000, 300, 5000, 0], 128, 1, 1,
                      lib_mod.PLAN_LENGTH_AWARE | lib_mod.PLAN_MERGE_IN_KERNEL, 4)
-    assert lib_mod.workspace_size(w) == 256 * 1024 + 4 * 1 * 128 * (512 * 2 + 4)   # + split counters
+    assert lib_mod.workspace_size(w) == 256 * 1024 + 3 * 1 * 128 * (512 * 2 + 4)   # + split counters
     w = lib_mod.plan([100, 200], 16, 1, 0, lib_mod.PLAN_UNIFORM, 1)  # one split per row
     assert lib_mod.workspace_size(w) == 0
 

@@ -8,7 +8,7 @@ import pytest
 from oracle.attention import attend_case
 from oracle.merge import merge_partials, split_attend
 from oracle.plan import (plan_ref, unpack_plan, MODE_AUTO, MODE_UNIFORM, MODE_LENGTH_AWARE,
-                         KV_BF16, KV_FP8, N_MAX, OCC, XCDS, M_UNIT, ITEM_OVERHEAD)
+                         KV_BF16, KV_FP8, N_MAX, OCC, XCDS, M_UNIT, ITEM_OVERHEAD, MIN_SPLIT_KEYS)
 from workloads import make_case, config_lengths, CONFIGS, BF16, FP8
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -103,8 +103,10 @@ def check_invariants(lens, H, q_len, kv_dtype, mode, C):
     else:
         assert G <= max(OCC * C, u)
         assert S <= R + OCC * C
-        # lanes: u workgroups of one chiplet run the same consecutive splits,
-        # member j taking M tile j; lanes follow each other in split order
+        # lanes: u workgroups of one chiplet run the same splits (in id order),
+        # member j taking M tile j; every split is in exactly one lane, and a
+        # row is cut only into pieces of at least MIN_SPLIT_KEYS keys (except
+        # its last piece)
         X = XCDS
         while X > 1 and (OCC * C) // X < u:
             X //= 2
@@ -116,14 +118,15 @@ def check_invariants(lens, H, q_len, kv_dtype, mode, C):
             ms = {m for _, m in its}
             assert len(ms) == 1
             seq = tuple(s for s, _ in its)
-            assert list(seq) == list(range(seq[0], seq[0] + len(seq)))
+            assert all(seq[i] < seq[i + 1] for i in range(len(seq) - 1))
             lanes.setdefault(seq, []).append((g, ms.pop()))
-        firsts = sorted(seq[0] for seq in lanes)
-        assert firsts[0] == 0
         for seq, members in lanes.items():
             assert sorted(m for _, m in members) == list(range(u))
             assert len({g % X for g, _ in members}) == 1
-        assert sum(len(seq) for seq in lanes) == S
+        assert sorted(s for seq in lanes for s in seq) == list(range(S))
+        for b in range(R):
+            for s in range(sp[b], sp[b + 1] - 1):
+                assert d["split_end"][s] - d["split_begin"][s] >= MIN_SPLIT_KEYS
     return d
 
 
