@@ -26,9 +26,12 @@ def _regs(text):
 
 def check_qk_chains(asm: str):
     """Return (chains, violations): the number of VGPR-accumulator MFMA chains
-    found and a list of offending instruction lines."""
+    found and a list of offending instruction lines. Several chains may be
+    interleaved (one per query row block); each link's srcC must be exactly
+    its chain's accumulator, and no other instruction may touch an open
+    chain's registers before its last link (the one followed by s_nop 7)."""
     lines = [l.split(";", 1)[0].strip() for l in asm.splitlines()]
-    chains, bad, active = 0, [], None
+    chains, bad, active = 0, [], []   # active: register sets of open chains
     for i, l in enumerate(lines):
         if not l or l.startswith(".") or l.endswith(":"):
             continue
@@ -36,15 +39,61 @@ def check_qk_chains(asm: str):
         if mnem == _MFMA and ops.strip().startswith("v["):
             dst = _regs(ops.split(",")[0])
             src_c = ops.split(",")[-1].strip()
-            if active is None or src_c == "0":
-                chains += 1
-            elif _regs(src_c) != active:
-                bad.append(f"{i}: {l} (accumulator changed inside a chain)")
+            srcs = _regs(",".join(ops.split(",")[1:-1]))
             nxt = next((x for x in lines[i + 1:] if x and not x.startswith(".")), "")
-            active = None if nxt.startswith("s_nop 7") else dst
+            ends = nxt.startswith("s_nop 7")
+            if src_c == "0":
+                chains += 1
+                if any(srcs & a or dst & a for a in active):
+                    bad.append(f"{i}: {l} (a new chain touches an open chain)")
+                if not ends:
+                    active.append(dst)
+                continue
+            acc = _regs(src_c)
+            if acc not in active:
+                if any(acc & a for a in active) or any(dst & a for a in active):
+                    bad.append(f"{i}: {l} (accumulator changed inside a chain)")
+                continue
+            active.remove(acc)
+            if any(srcs & a or dst & a for a in active):
+                bad.append(f"{i}: {l} (touches another open chain)")
+            if not ends:
+                active.append(dst)
             continue
-        if active is None or mnem.startswith("s_"):
+        if not active or mnem.startswith("s_"):
             continue
-        if _regs(ops) & active:
+        regs = _regs(ops)
+        if any(regs & a for a in active):
             bad.append(f"{i}: {l}")
     return chains, bad
+
+
+_WAIT_STATES = 2   # VALU write of a VGPR -> MFMA read of it as an operand
+
+
+def check_valu_to_mfma(asm: str):
+    """Return the assembly MFMA links (VGPR accumulators) that read an
+    operand a VALU instruction wrote fewer than _WAIT_STATES wait states
+    earlier: the compiler inserts no hazard wait states for inline assembly."""
+    lines = [l.split(";", 1)[0].strip() for l in asm.splitlines()]
+    bad = []
+    for i, l in enumerate(lines):
+        mnem, _, ops = l.partition(" ")
+        if mnem != _MFMA or not ops.strip().startswith("v["):
+            continue
+        srcs = _regs(",".join(ops.split(",")[1:]))
+        waits, k = 0, i - 1
+        while k >= 0 and waits < _WAIT_STATES:
+            t = lines[k]
+            k -= 1
+            if not t or t.startswith(".") or t.endswith(":"):
+                continue
+            tm, _, tops = t.partition(" ")
+            if tm == "s_nop":
+                waits += int(tops.strip().split()[0], 0) + 1
+                continue
+            if tm.startswith("v_") and not tm.startswith("v_mfma") and _regs(tops.split(",")[0]) & srcs:
+                bad.append(f"{i}: {l} (VALU write {k + 1}: {t})")
+                break
+            waits += 1
+    return bad

@@ -78,14 +78,19 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
 def _check_decode_asm(path):
     sys.path.insert(0, PKG)
     try:
-        from asm_check import check_qk_chains
+        from asm_check import check_qk_chains, check_valu_to_mfma
     finally:
         sys.path.pop(0)
     with open(path) as f:
-        chains, bad = check_qk_chains(f.read())
+        text = f.read()
+    chains, bad = check_qk_chains(text)
     if chains == 0 or bad:
         raise RuntimeError(f"decode.hip: the generated code breaks the QK accumulator chains "
                            f"({chains} chains; offending lines of {path}):\n" + "\n".join(bad[:20]))
+    hazards = check_valu_to_mfma(text)
+    if hazards:
+        raise RuntimeError(f"decode.hip: an assembly MFMA reads a VALU result without the required "
+                           f"wait states (offending lines of {path}):\n" + "\n".join(hazards[:20]))
 
 
 def _wait(item, verbose):
