@@ -284,16 +284,24 @@ def main():
     # rows, since one mla_decode_fwd call launches both).
     q_elem = 2 if case.q_dtype == "bf16" else 1
     alg_bytes = (kv_bytes + keys * 4 + T * case.heads * 576 * q_elem + T * case.heads * (512 * 2 + 4))
-    compute_dtype = "bf16"
+    # With fp8 Q and KV the QK products (576 of every 1088 flops) run on the
+    # fp8 matrix core and PV on bf16: the peak is the rate at which both
+    # parts would finish at their own dtype's peak.
+    if case.q_dtype == "fp8" and case.kv_dtype == "fp8":
+        compute_dtype = "fp8+bf16"
+        peak_tflops = (576 + 512) / (576 / MFMA_PEAK_TFLOPS["fp8"] + 512 / MFMA_PEAK_TFLOPS["bf16"])
+    else:
+        compute_dtype = "bf16"
+        peak_tflops = MFMA_PEAK_TFLOPS["bf16"]
     achieved_tflops = flops / (fwd_avg * 1e-3) / 1e12
     achieved_gbs = alg_bytes / (fwd_avg * 1e-3) / 1e9
-    ridge = MFMA_PEAK_TFLOPS[compute_dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ridge = peak_tflops * 1e12 / (HBM_PEAK_GBS * 1e9)
     bound = "mfma" if flops / alg_bytes > ridge else "hbm"
     traffic = measured_traffic(args.workload)
     if bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(achieved_tflops, 2),
-                "peak": MFMA_PEAK_TFLOPS[compute_dtype], "unit": "TFLOP/s",
-                "frac": round(achieved_tflops / MFMA_PEAK_TFLOPS[compute_dtype], 4)}
+                "peak": round(peak_tflops, 1), "unit": "TFLOP/s",
+                "frac": round(achieved_tflops / peak_tflops, 4)}
     else:
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
@@ -319,7 +327,7 @@ def main():
     }
     if uniform is not None:
         ach = flops / (uniform["launch_ms"] * 1e-3) / 1e12
-        uniform["mfma_frac"] = round(ach / MFMA_PEAK_TFLOPS[compute_dtype], 4)
+        uniform["mfma_frac"] = round(ach / peak_tflops, 4)
         out["uniform_plan"] = uniform
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)

@@ -1,6 +1,6 @@
 """Build-time check of the decode kernel's generated code.
 
-The QK products of a tile are inline-assembly MFMAs chained through one VGPR
+The QK products of a tile (bf16, or fp8 with fp8 queries) are inline-assembly MFMAs chained through one VGPR
 accumulator, and only the last link of a chain waits (inside its own
 statement, with s_nop) until its result can be read. The compiler does not
 know when an assembly MFMA's result arrives, so the kernel is only correct if
@@ -10,7 +10,7 @@ the gfx950 assembly of decode.hip; build() fails if it does not hold.
 """
 import re
 
-_MFMA = "v_mfma_f32_32x32x16_bf16"
+_MFMAS = ("v_mfma_f32_32x32x16_bf16", "v_mfma_f32_32x32x64_f8f6f4")
 _REG = re.compile(r"([vas])\[(\d+):(\d+)\]|([vas])(\d+)\b")
 
 
@@ -36,7 +36,7 @@ def check_qk_chains(asm: str):
         if not l or l.startswith(".") or l.endswith(":"):
             continue
         mnem, _, ops = l.partition(" ")
-        if mnem == _MFMA and ops.strip().startswith("v["):
+        if mnem in _MFMAS and ops.strip().startswith("v["):
             dst = _regs(ops.split(",")[0])
             src_c = ops.split(",")[-1].strip()
             srcs = _regs(",".join(ops.split(",")[1:-1]))
@@ -79,7 +79,7 @@ def check_valu_to_mfma(asm: str):
     bad = []
     for i, l in enumerate(lines):
         mnem, _, ops = l.partition(" ")
-        if mnem != _MFMA or not ops.strip().startswith("v["):
+        if mnem not in _MFMAS or not ops.strip().startswith("v["):
             continue
         srcs = _regs(",".join(ops.split(",")[1:]))
         waits, k = 0, i - 1

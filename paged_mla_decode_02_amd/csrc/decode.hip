@@ -95,6 +95,7 @@ constexpr int kF8MainBytes = kNT * kF8MainRow;        // 16384
 // into the slot's second half), so no lane mask splits the pipeline code.
 constexpr int kF8RopeBytes = (kDecodeThreads / 64) * 1024;   // 4096
 constexpr int kKSteps = kDLat / 16;           // 36 QK k-steps (32 main + 4 rope)
+constexpr int kKSteps8 = kDLat / 64;          // 9 fp8 QK products (8 main + 1 rope) for fp8 Q and KV
 constexpr int kWaves = kDecodeThreads / 64;   // 4
 constexpr int kRows = 128;                    // query rows per work item
 constexpr int kRowBlocks = kRows / 32;        // 4 blocks of 32 rows (one per wave)
@@ -286,6 +287,30 @@ __device__ __forceinline__ void mfma_qk_last(f32x16& out, const f32x16& acc, bf1
                : "=&v"(out) : "v"(a), "v"(b), "v"(acc));
 }
 
+// fp8 Q with fp8 KV: the QK products take both operands in fp8
+// (v_mfma_f32_32x32x64_f8f6f4, OCP e4m3 by default), so K is never converted.
+// A product is 16 passes: the last link waits 22 wait states before its
+// result is read. Each operand register of lane l holds 32 bytes of its row
+// (key l & 31 in A, query row l & 31 in B): product p takes dims
+// 64 p + 16 h .. +15 and 64 p + 32 + 16 h .. +15 (h = l >> 5) for both. The
+// products sum over every dim exactly once whatever order the matrix core
+// gives the 64 k positions, since A and B put the same dim in the same
+// (lane half, byte) position; the exact fp8 products are accumulated in fp32
+// as in the bf16 path.
+__device__ __forceinline__ void mfma8_qk_first(f32x16& d, u32x8 a, u32x8 b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma8_qk(f32x16& d, u32x8 a, u32x8 b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma8_qk_last(f32x16& out, const f32x16& acc, u32x8 a, u32x8 b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %3\n\ts_nop 7\n\ts_nop 7\n\ts_nop 5"
+               : "=&v"(out) : "v"(a), "v"(b), "v"(acc));
+}
+__device__ __forceinline__ u32x8 cat8(u32x4 a, u32x4 b) {
+  return u32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 // Per-lane LDS addressing, fixed for a work item.
 //   K fragment (A operand of S^T = K Q^T), k-step ks: lane l holds key
 //   i = l & 31, dims 16 ks + 8 (l >> 5) .. +7 -- main chunk 2 ks + h of row i,
@@ -360,6 +385,11 @@ __device__ __forceinline__ bf16x8 k_frag(const lds_u8* smem, const LaneAddr& la,
 __device__ __forceinline__ u32x4 k_pair_f8(const lds_u8* smem, const LaneAddr& la, int kmain, int krope, int j) {
   if (j < 16) return lds_load<u32x4>(smem, kmain + la.krow + (((2 * j) ^ la.xm) << 4));
   return lds_load<u32x4>(smem, krope + la.rrow + (((2 * (j - 16)) ^ la.xr) << 4));
+}
+// fp8 A operand of QK product p: pairs 2 p and 2 p + 1 (dims 64 p + 16 h and
+// 64 p + 32 + 16 h, 16 bytes each).
+__device__ __forceinline__ u32x8 k_prod_f8(const lds_u8* smem, const LaneAddr& la, int kmain, int krope, int p) {
+  return cat8(k_pair_f8(smem, la, kmain, krope, 2 * p), k_pair_f8(smem, la, kmain, krope, 2 * p + 1));
 }
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return cat(fp8x4_to_bf16(lo), fp8x4_to_bf16(hi));
@@ -542,8 +572,10 @@ __device__ __forceinline__ void pv_product(const lds_u8* smem, const LaneAddr& l
 constexpr int kKDepth = 5;
 constexpr int kSmStride = 2;
 constexpr int kDmaStride = 3;
-template <bool QK, bool PREV, int NDMA, bool KV_FP8, bool FAST, typename Dma>
-__device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, const bf16x8 (&qf)[kKSteps],
+// QF8 (fp8 Q and KV): the 9 fp8 QK products take every fourth slot, read
+// kK8Depth products ahead; the softmax pieces keep their slots.
+template <bool QK, bool PREV, int NDMA, bool KV_FP8, bool FAST, bool QF8, typename QF, int NQ, typename Dma>
+__device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, const QF (&qf)[NQ],
                                               int kmain, int krope, f32x16& s_old, float score_c,
                                               int lim_old, RowState& rs, int pbuf, int vmain,
                                               f32x16 (&oacc)[kRowBlocks][kColTiles], Dma&& dma) {
@@ -554,12 +586,18 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
   // MFMA (so the conversion's VALU writes are far from the assembly MFMA
   // that reads them).
   constexpr int kRawDepth = 3;
+  constexpr int kK8Depth = 3;
+  static_assert(!QF8 || (KV_FP8 && NQ == kKSteps8), "fp8 QK products need fp8 K and fp8 Q fragments");
   bf16x8 kb[kKDepth];
   u32x4 raw[kRawDepth];
+  u32x8 k8[kK8Depth];
   Softmax sm;
   f32x16 s_cur;
   if constexpr (QK) {
-    if constexpr (!KV_FP8) {
+    if constexpr (QF8) {
+#pragma unroll
+      for (int d = 0; d < kK8Depth; ++d) k8[d] = k_prod_f8(smem, la, kmain, krope, d);
+    } else if constexpr (!KV_FP8) {
 #pragma unroll
       for (int d = 0; d < kKDepth; ++d) kb[d] = k_frag(smem, la, kmain, krope, d);
     } else {
@@ -574,7 +612,16 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
   constexpr int kSlotsA = QK ? kKSteps : kSoftmaxPieces * kSmStride;
 #pragma unroll
   for (int s = 0; s < kSlotsA; ++s) {
-    if constexpr (QK) {
+    if constexpr (QK && QF8) {
+      if (s % 4 == 0) {
+        const int p = s / 4;
+        const u32x8 a = k8[p % kK8Depth];
+        if (p + kK8Depth < kKSteps8) k8[p % kK8Depth] = k_prod_f8(smem, la, kmain, krope, p + kK8Depth);
+        if (p == 0) mfma8_qk_first(s_cur, a, qf[p]);
+        else if (p + 1 < kKSteps8) mfma8_qk(s_cur, a, qf[p]);
+        else mfma8_qk_last(s_old, s_cur, a, qf[p]);   // s_old is dead: the softmax ended
+      }
+    } else if constexpr (QK) {
       bf16x8 a;
       if constexpr (!KV_FP8) {
         a = kb[s % kKDepth];
@@ -637,6 +684,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
   lds_u8* smem = (lds_u8*)smem_raw;
   using LY = Layout<KV_FP8>;
   using Dma = TileDma<KV_FP8>;
+  constexpr bool QF8 = Q_FP8 && KV_FP8;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -689,12 +737,18 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     // for bf16 KV; for fp8 KV (k-steps in pairs) 32 (ks / 2) + 16 h +
     // 8 (ks & 1) .. +7. In 8-element units: 2 ks + h, or 4 (ks / 2) + 2 h +
     // (ks & 1).
-    bf16x8 qf[kKSteps];
+    // With fp8 Q and KV the raw fp8 bytes of product p: 16-byte units
+    // 4 p + h and 4 p + 2 + h.
+    std::conditional_t<QF8, u32x8, bf16x8> qf[QF8 ? kKSteps8 : kKSteps];
     if (row_ok) {
       const int64_t qrow = ((int64_t)(q0 + tok) * H + head) * kDLat;
       const int h = lane >> 5;
       auto unit = [&](int ks) { return KV_FP8 ? 4 * (ks >> 1) + 2 * h + (ks & 1) : 2 * ks + h; };
-      if constexpr (!Q_FP8) {
+      if constexpr (QF8) {
+        const u32x4* src = (const u32x4*)((const unsigned char*)a.q + qrow);
+#pragma unroll
+        for (int p = 0; p < kKSteps8; ++p) qf[p] = cat8(src[4 * p + h], src[4 * p + 2 + h]);
+      } else if constexpr (!Q_FP8) {
         const bf16x8* src = (const bf16x8*)((const uint16_t*)a.q + qrow);
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = src[unit(ks)];
@@ -708,7 +762,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       }
     } else {
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = bf16x8{};
+      for (auto& f : qf) f = {};
     }
 
     // Pass 0 fixes each row's reference at its first visible tile's max. In
@@ -760,7 +814,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
           };
           const int lim_old = key_last - (begin + (t - 1) * kNT + 4 * (lane >> 5));
           const LaneAddr la_s = lane_addr<KV_FP8>(dlane, w);
-          pipeline_step<DO_QK, PREV, DO_DMA ? Dma::n : 0, KV_FP8, FAST>(
+          pipeline_step<DO_QK, PREV, DO_DMA ? Dma::n : 0, KV_FP8, FAST, QF8>(
               smem, la_s, qf, LY::main(t), LY::rope(t), s_old, score_c, lim_old, rs, p_buf(t + 1),
               LY::main(t + 11), oacc, dma);
           if (DO_DMA) wait_vm<1 + Dma::n>();
