@@ -311,6 +311,62 @@ __device__ __forceinline__ u32x8 cat8(u32x4 a, u32x4 b) {
   return u32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// bf16 Q with fp8 KV takes the same fp8 products twice: every query row is
+// split as x 2^A = hi + lo with hi = fp8(x 2^A) and lo = fp8(x 2^A - hi),
+// A per row so that its largest |x| 2^A lies in [128, 256). hi keeps the top
+// 4 significant bits of an element, lo the next 4, so the pair is exact for
+// every bf16 element above 2^-2 after scaling (lo is then at least the
+// smallest subnormal step 2^-9); a smaller element loses at most 2^-10, i.e.
+// 2^-17 of the row's largest. The scores come out times 2^A, which the
+// softmax takes out with its score scale.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
+}
+// 8 bf16 elements (times `scale`) -> 2 dwords of hi and 2 of lo.
+__device__ __forceinline__ void split_fp8x8(bf16x8 x, float scale, uint32_t* hi, uint32_t* lo) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const float y0 = (float)x[4 * q] * scale, y1 = (float)x[4 * q + 1] * scale;
+    const float y2 = (float)x[4 * q + 2] * scale, y3 = (float)x[4 * q + 3] * scale;
+    const uint32_t h = pack_fp8x4(y0, y1, y2, y3);
+    const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, false);
+    const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, true);
+    hi[q] = h;
+    lo[q] = pack_fp8x4(y0 - f01[0], y1 - f01[1], y2 - f23[0], y3 - f23[1]);
+  }
+}
+// In place: q[2 p] and q[2 p + 1] hold the 32 bf16 elements of product p
+// (dims 64 p + 16 h .. +15, then 64 p + 32 + 16 h .. +15) and become its hi
+// and lo fp8 operands. The row's largest |x| is taken over both lane halves
+// (lanes l and l ^ 32 hold one row). Returns 2^-A.
+__device__ __forceinline__ float split_q_rows(u32x8 (&q)[2 * kKSteps8]) {
+  uint32_t m = 0;   // largest |x| as bf16 bits: the order of non-negative floats
+#pragma unroll
+  for (int n = 0; n < 2 * kKSteps8; ++n)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) m = max(m, max(q[n][d] & 0x7FFFu, (q[n][d] >> 16) & 0x7FFFu));
+  const float amax = half_max(__uint_as_float(m << 16));
+  int ex = 0;
+  if (amax > 0.f && __builtin_isfinite(amax)) frexpf(amax, &ex);   // amax in [2^(ex-1), 2^ex)
+  ex = max(ex, -100);   // keeps 2^(8 - ex) and the score scale normal floats
+  const float scale = ldexpf(1.0f, 8 - ex);
+#pragma unroll
+  for (int p = 0; p < kKSteps8; ++p) {
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x8& v = q[2 * p + (u >> 1)];
+      const int d0 = 4 * (u & 1);
+      split_fp8x8(__builtin_bit_cast(bf16x8, u32x4{v[d0], v[d0 + 1], v[d0 + 2], v[d0 + 3]}), scale,
+                  hi + 2 * u, lo + 2 * u);
+    }
+    q[2 * p] = u32x8{hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]};
+    q[2 * p + 1] = u32x8{lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]};
+  }
+  return ldexpf(1.0f, ex - 8);
+}
+
 // Per-lane LDS addressing, fixed for a work item.
 //   K fragment (A operand of S^T = K Q^T), k-step ks: lane l holds key
 //   i = l & 31, dims 16 ks + 8 (l >> 5) .. +7 -- main chunk 2 ks + h of row i,
@@ -572,9 +628,12 @@ __device__ __forceinline__ void pv_product(const lds_u8* smem, const LaneAddr& l
 constexpr int kKDepth = 5;
 constexpr int kSmStride = 2;
 constexpr int kDmaStride = 3;
-// QF8 (fp8 Q and KV): the 9 fp8 QK products take every fourth slot, read
-// kK8Depth products ahead; the softmax pieces keep their slots.
-template <bool QK, bool PREV, int NDMA, bool KV_FP8, bool FAST, bool QF8, typename QF, int NQ, typename Dma>
+// QKM selects the QK products: 0 bf16 (36 k-steps, one per slot); 1 fp8 Q
+// and KV (9 fp8 products, every fourth slot); 2 bf16 Q split in two fp8
+// operands with fp8 KV (18 products, every second slot: hi then lo of each
+// 64 dims). fp8 K is read kK8Depth products ahead; the softmax pieces keep
+// their slots.
+template <bool QK, bool PREV, int NDMA, bool KV_FP8, bool FAST, int QKM, typename QF, int NQ, typename Dma>
 __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, const QF (&qf)[NQ],
                                               int kmain, int krope, f32x16& s_old, float score_c,
                                               int lim_old, RowState& rs, int pbuf, int vmain,
@@ -587,7 +646,8 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
   // that reads them).
   constexpr int kRawDepth = 3;
   constexpr int kK8Depth = 3;
-  static_assert(!QF8 || (KV_FP8 && NQ == kKSteps8), "fp8 QK products need fp8 K and fp8 Q fragments");
+  constexpr bool QF8 = QKM != 0;
+  static_assert(QKM == 0 ? NQ == kKSteps : (KV_FP8 && NQ == QKM * kKSteps8), "Q fragments of the QK mode");
   bf16x8 kb[kKDepth];
   u32x4 raw[kRawDepth];
   u32x8 k8[kK8Depth];
@@ -613,13 +673,15 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
 #pragma unroll
   for (int s = 0; s < kSlotsA; ++s) {
     if constexpr (QK && QF8) {
-      if (s % 4 == 0) {
-        const int p = s / 4;
+      constexpr int kStride = 4 / QKM;   // slots per link
+      if (s % kStride == 0) {
+        const int n = s / kStride, p = n / QKM;   // link n of NQ, on K product p
         const u32x8 a = k8[p % kK8Depth];
-        if (p + kK8Depth < kKSteps8) k8[p % kK8Depth] = k_prod_f8(smem, la, kmain, krope, p + kK8Depth);
-        if (p == 0) mfma8_qk_first(s_cur, a, qf[p]);
-        else if (p + 1 < kKSteps8) mfma8_qk(s_cur, a, qf[p]);
-        else mfma8_qk_last(s_old, s_cur, a, qf[p]);   // s_old is dead: the softmax ended
+        if (n % QKM == QKM - 1 && p + kK8Depth < kKSteps8)
+          k8[p % kK8Depth] = k_prod_f8(smem, la, kmain, krope, p + kK8Depth);
+        if (n == 0) mfma8_qk_first(s_cur, a, qf[n]);
+        else if (n + 1 < NQ) mfma8_qk(s_cur, a, qf[n]);
+        else mfma8_qk_last(s_old, s_cur, a, qf[n]);   // s_old is dead: the softmax ended
       }
     } else if constexpr (QK) {
       bf16x8 a;
@@ -684,7 +746,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
   lds_u8* smem = (lds_u8*)smem_raw;
   using LY = Layout<KV_FP8>;
   using Dma = TileDma<KV_FP8>;
-  constexpr bool QF8 = Q_FP8 && KV_FP8;
+  constexpr int QKM = !KV_FP8 ? 0 : Q_FP8 ? 1 : 2;   // QK products: bf16, fp8, split bf16 Q
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -738,16 +800,26 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     // 8 (ks & 1) .. +7. In 8-element units: 2 ks + h, or 4 (ks / 2) + 2 h +
     // (ks & 1).
     // With fp8 Q and KV the raw fp8 bytes of product p: 16-byte units
-    // 4 p + h and 4 p + 2 + h.
-    std::conditional_t<QF8, u32x8, bf16x8> qf[QF8 ? kKSteps8 : kKSteps];
+    // 4 p + h and 4 p + 2 + h. With bf16 Q and fp8 KV the same 32 elements
+    // (bf16 units 8 p + 2 h, +1, 8 p + 4 + 2 h, +1) split into hi (qf[2 p])
+    // and lo (qf[2 p + 1]); score_row then carries the row's 2^-A.
+    std::conditional_t<(QKM > 0), u32x8, bf16x8> qf[QKM == 0 ? kKSteps : QKM * kKSteps8];
+    float score_row = score_c;
     if (row_ok) {
       const int64_t qrow = ((int64_t)(q0 + tok) * H + head) * kDLat;
       const int h = lane >> 5;
       auto unit = [&](int ks) { return KV_FP8 ? 4 * (ks >> 1) + 2 * h + (ks & 1) : 2 * ks + h; };
-      if constexpr (QF8) {
+      if constexpr (QKM == 1) {
         const u32x4* src = (const u32x4*)((const unsigned char*)a.q + qrow);
 #pragma unroll
         for (int p = 0; p < kKSteps8; ++p) qf[p] = cat8(src[4 * p + h], src[4 * p + 2 + h]);
+      } else if constexpr (QKM == 2) {   // raw bf16 here; split once the item's first loads are out
+        const bf16x8* src = (const bf16x8*)((const uint16_t*)a.q + qrow);
+#pragma unroll
+        for (int n = 0; n < 2 * kKSteps8; ++n) {
+          const int u0 = 4 * n + 2 * h;   // bf16 units 8 p + 2 h (+1) for n = 2 p, 8 p + 4 + 2 h (+1) for 2 p + 1
+          qf[n] = cat8(__builtin_bit_cast(u32x4, src[u0]), __builtin_bit_cast(u32x4, src[u0 + 1]));
+        }
       } else if constexpr (!Q_FP8) {
         const bf16x8* src = (const bf16x8*)((const uint16_t*)a.q + qrow);
 #pragma unroll
@@ -784,11 +856,21 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
 #pragma unroll
         for (int t = 0; t < 4; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, w, lane);
         wait_vm<0>();
+        if constexpr (QKM == 2) {
+          // The raw queries have landed with the slot lists; the empty
+          // statements tell the compiler so, and the split below then runs
+          // while the first tiles load.
+#pragma unroll
+          for (auto& f : qf) asm volatile("" : "+v"(f));
+        }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           issue_slots(a.kv_indices, kv0, begin, end, t + 2, smem, w, lane);
           if (t < ntiles)
             Dma::all(kv, read_slots(smem, t, w, lane), smem, dma_main<KV_FP8>(t), dma_rope<KV_FP8>(t), w, lane);
+        }
+        if constexpr (QKM == 2) {
+          if (pass == 0) score_row = score_c * split_q_rows(qf);
         }
         if (ntiles > 1) wait_vm<1 + Dma::n>();
         else wait_vm<1>();
@@ -814,8 +896,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
           };
           const int lim_old = key_last - (begin + (t - 1) * kNT + 4 * (lane >> 5));
           const LaneAddr la_s = lane_addr<KV_FP8>(dlane, w);
-          pipeline_step<DO_QK, PREV, DO_DMA ? Dma::n : 0, KV_FP8, FAST, QF8>(
-              smem, la_s, qf, LY::main(t), LY::rope(t), s_old, score_c, lim_old, rs, p_buf(t + 1),
+          pipeline_step<DO_QK, PREV, DO_DMA ? Dma::n : 0, KV_FP8, FAST, QKM>(
+              smem, la_s, qf, LY::main(t), LY::rope(t), s_old, score_row, lim_old, rs, p_buf(t + 1),
               LY::main(t + 11), oacc, dma);
           if (DO_DMA) wait_vm<1 + Dma::n>();
           else wait_vm<1>();
