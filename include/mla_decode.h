@@ -43,7 +43,9 @@
  *     qo_indptr non-decreasing, qo_indptr[0] = 0, per-row q_b <= q_len_max, and
  *     kv_indptr[b+1] - kv_indptr[b] equal to the kv_lens the plan was built
  *     from. kv_indptr[0] may be non-zero (an offset list; indices are used as
- *     absolute positions in kv_indices).
+ *     absolute positions in kv_indices). An index outside [0, num_slots)
+ *     gives a wrong result but never a read outside the pool: the decode
+ *     reads row num_slots - 1 in its place.
  */
 #ifndef MLA_DECODE_H
 #define MLA_DECODE_H

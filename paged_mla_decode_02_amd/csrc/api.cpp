@@ -82,6 +82,7 @@ int32_t decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale, cons
   a.q_scale = q_scale;
   a.kv = kv_pool;
   a.kv_scale = kv_scale;
+  a.max_slot = (uint32_t)(num_slots - 1);
   a.qo_indptr = qo_indptr;
   a.kv_indptr = kv_indptr;
   a.kv_indices = kv_indices;
@@ -220,6 +221,7 @@ extern "C" int32_t mla_debug_gather(const void* kv_pool, mla_dtype kv_dtype, int
   g.kv = kv_pool;
   g.kv_indptr = kv_indptr;
   g.kv_indices = kv_indices;
+  g.max_slot = (uint32_t)(num_slots - 1);
   g.plan = plan_dev;
   g.off_split_row = (int32_t)v.off_split_row;
   g.off_split_begin = (int32_t)v.off_split_begin;

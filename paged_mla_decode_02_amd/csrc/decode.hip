@@ -172,7 +172,11 @@ template <bool KV_FP8> struct TileDma {
   static constexpr int n = kMainOps + 1;
   static constexpr int kRopeRows = kNT / kWaves;
 
-  static __device__ __forceinline__ TileSrc<KV_FP8> src(const unsigned char* kv, int slot_lane, int w, int lane) {
+  // Slots beyond the pool are clamped to its last row, so that no load
+  // leaves the pool whatever the slot lists hold.
+  static __device__ __forceinline__ TileSrc<KV_FP8> src(const unsigned char* kv, int slot_in, uint32_t max_slot,
+                                                        int w, int lane) {
+    const int slot_lane = (int)min((uint32_t)slot_in, max_slot);
     TileSrc<KV_FP8> t;
     if constexpr (!KV_FP8) {
       const uint64_t row = (uint64_t)(uintptr_t)kv + (uint64_t)(uint32_t)slot_lane * (2 * kDLat);
@@ -218,10 +222,10 @@ template <bool KV_FP8> struct TileDma {
   }
 
   // All n loads of a tile at once.
-  static __device__ __forceinline__ void all(const unsigned char* kv, int slot_lane, lds_u8* smem,
-                                             int main_off, int rope_off, int w, int lane_in) {
+  static __device__ __forceinline__ void all(const unsigned char* kv, int slot_lane, uint32_t max_slot,
+                                             lds_u8* smem, int main_off, int rope_off, int w, int lane_in) {
     const int lane = opaque(lane_in);
-    const TileSrc<KV_FP8> s = src(kv, slot_lane, w, lane);
+    const TileSrc<KV_FP8> s = src(kv, slot_lane, max_slot, w, lane);
 #pragma unroll
     for (int i = 0; i < n; ++i) op(i, kv, s, lds_addr_of(smem), main_off, rope_off, w, lane);
   }
@@ -867,7 +871,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         for (int t = 0; t < 2; ++t) {
           issue_slots(a.kv_indices, kv0, begin, end, t + 2, smem, w, lane);
           if (t < ntiles)
-            Dma::all(kv, read_slots(smem, t, w, lane), smem, dma_main<KV_FP8>(t), dma_rope<KV_FP8>(t), w, lane);
+            Dma::all(kv, read_slots(smem, t, w, lane), a.max_slot, smem, dma_main<KV_FP8>(t), dma_rope<KV_FP8>(t), w, lane);
         }
         if constexpr (QKM == 2) {
           if (pass == 0) score_row = score_c * split_q_rows(qf);
@@ -889,7 +893,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
           constexpr bool DO_DMA = decltype(DMAc)::value, FAST = decltype(FASTc)::value;
           const int dlane = opaque(lane);
           issue_slots(a.kv_indices, kv0, begin, end, t + 4, smem, w, dlane);
-          const TileSrc<KV_FP8> src = Dma::src(kv, DO_DMA ? read_slots(smem, t + 2, w, dlane) : 0, w, dlane);
+          const TileSrc<KV_FP8> src = Dma::src(kv, DO_DMA ? read_slots(smem, t + 2, w, dlane) : 0, a.max_slot, w, dlane);
           const int dm = dma_main<KV_FP8>(t + 2), dr = dma_rope<KV_FP8>(t + 2);
           auto dma = [&](int i) {
             Dma::op(i, kv, src, lds_addr_of(smem), dm, dr, w, dlane);
@@ -1042,7 +1046,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gather_kernel(GatherArgs a) {
   const unsigned char* kv = (const unsigned char*)a.kv;
   for (int key0 = begin; key0 < end; key0 += kNT) {
     const int slot = load_tile_slot(a.kv_indices, kv0, key0, end, lane);
-    TileDma<KV_FP8>::all(kv, slot, smem, dma_main<KV_FP8>(0), dma_rope<KV_FP8>(0), wave, lane);
+    TileDma<KV_FP8>::all(kv, slot, a.max_slot, smem, dma_main<KV_FP8>(0), dma_rope<KV_FP8>(0), wave, lane);
     wait_vm_all();
     __syncthreads();
     for (int p = tid; p < kNT * 72; p += kDecodeThreads) {

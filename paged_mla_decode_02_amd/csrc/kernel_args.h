@@ -21,6 +21,7 @@ struct DecodeArgs {
   int32_t off_split_row, off_split_begin, off_split_end, off_split_part;
   int32_t off_work_indptr, off_item_split, off_item_m;
   int32_t heads, q_len_max, causal;
+  uint32_t max_slot;         // num_slots - 1: slot lists are clamped to the pool
   float score_scale_log2;   // softmax_scale * log2(e)
   int32_t dcp_world, dcp_rank;      // round-robin KV shard: local key j at position j * world + rank
   int32_t* counters;        // [rows * u] split arrivals per (row, M tile); zero between calls
@@ -53,6 +54,7 @@ struct GatherArgs {
   const int32_t* plan;
   int32_t off_split_row, off_split_begin, off_split_end, off_split_indptr;
   int32_t uniform_ranges;
+  uint32_t max_slot;         // num_slots - 1
   uint16_t* dense;          // bf16 [nnz, 576]
 };
 

@@ -147,6 +147,39 @@ def test_block_length_sweep(lib, q_len, kv_dtype):
     assert_parity(case, O, LSE)
 
 
+def test_query_row_magnitudes_fp8_kv(lib):
+    """bf16 queries against fp8 KV: the decode splits each query row into two
+    fp8 operands (a high and a low part) under a power-of-two scale taken from
+    the row's largest element. Rows far from unit size, rows whose elements
+    span 24 binades, all-zero rows, rows of bf16 subnormals and rows with one
+    nonzero element must still match the oracle."""
+    case = make_case(95, [300, 77, 40], heads=16, q_len=3, q_dtype=BF16, kv_dtype=FP8, causal=True,
+                     pool_slots=4096)
+    rng = np.random.default_rng(95)
+    q = (case.q_codes.astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(-1, 576)
+    for i in range(q.shape[0]):
+        kind = i % 8
+        if kind == 0:
+            q[i] *= 2.0 ** -30
+        elif kind == 1:
+            q[i] *= 2.0 ** -12
+        elif kind == 2:
+            q[i] *= 8.0
+        elif kind == 3:
+            q[i] *= 2.0 ** rng.integers(-24, 1, 576)
+        elif kind == 4:
+            q[i] = 0.0
+        elif kind == 5:
+            q[i] = rng.integers(-127, 128, 576) * 2.0 ** -133     # bf16 subnormals
+        elif kind == 6:
+            q[i] = 0.0
+            q[i, rng.integers(0, 576)] = 1.5
+    case.q_codes = bf16_bits_of(q).reshape(case.q_codes.shape)
+    O, LSE, _ = run_gpu(case)
+    ratio, lse_err = assert_parity(case, O, LSE)
+    print(f"max|err|/max|O_ref| {ratio:.2e}, max|dLSE| {lse_err:.2e}")
+
+
 def test_ragged_blocks_and_offset_indptr(lib):
     case = make_case(91, [40, 0, 300, 17, 5], heads=16, q_len=6, q_dtype=BF16, kv_dtype=FP8,
                      causal=True, pool_slots=4096, q_lens=[6, 2, 0, 6, 1], kv_indptr_offset=13)
