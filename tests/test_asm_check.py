@@ -1,0 +1,77 @@
+"""The build-time checks of the decode kernel's generated code, on small
+hand-written instruction sequences: the inline-assembly QK accumulator chains
+(nothing may touch an open chain's registers between its links) and the
+VALU -> assembly-MFMA operand hazard (the compiler inserts no wait states for
+inline assembly)."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, os.path.join(ROOT, "paged_mla_decode_02_amd"))
+from asm_check import check_qk_chains, check_valu_to_mfma  # noqa: E402
+
+BF = "v_mfma_f32_32x32x16_bf16"
+F8 = "v_mfma_f32_32x32x64_f8f6f4"
+
+
+def chain(mnem, acc, out, a, b, links):
+    """A chain of `links` products through v[acc], the last writing v[out]."""
+    lines = [f"\t{mnem} v[{acc}:{acc + 15}], {a}, {b}, 0"]
+    for _ in range(links - 2):
+        lines.append(f"\t{mnem} v[{acc}:{acc + 15}], {a}, {b}, v[{acc}:{acc + 15}]")
+    lines.append(f"\t{mnem} v[{out}:{out + 15}], {a}, {b}, v[{acc}:{acc + 15}]")
+    lines += ["\ts_nop 7", "\ts_nop 5"]
+    return lines
+
+
+def test_clean_chains_of_both_kinds():
+    asm = chain(BF, 100, 120, "v[0:3]", "v[4:7]", 36) + chain(F8, 140, 160, "v[0:7]", "v[8:15]", 9)
+    chains, bad = check_qk_chains("\n".join(asm))
+    assert chains == 2 and bad == []
+
+
+def test_touching_an_open_accumulator_is_flagged():
+    asm = chain(BF, 100, 120, "v[0:3]", "v[4:7]", 4)
+    asm.insert(2, "\tv_mov_b32 v105, 0")          # between two links
+    _, bad = check_qk_chains("\n".join(asm))
+    assert len(bad) == 1 and "v_mov_b32 v105" in bad[0]
+
+
+def test_moving_the_accumulator_mid_chain_is_flagged():
+    asm = chain(F8, 100, 120, "v[0:7]", "v[8:15]", 4)
+    asm[2] = f"\t{F8} v[100:115], v[0:7], v[8:15], v[40:55]"   # a link that reads another accumulator
+    asm.insert(2, "\tv_mov_b32 v40, v100")
+    _, bad = check_qk_chains("\n".join(asm))
+    assert bad
+
+
+def test_interleaved_chains():
+    a = chain(BF, 100, 120, "v[0:3]", "v[4:7]", 3)
+    b = chain(BF, 140, 160, "v[0:3]", "v[4:7]", 3)
+    asm = [a[0], b[0], a[1], b[1], a[2], b[2]] + a[3:]
+    chains, bad = check_qk_chains("\n".join(asm))
+    assert chains == 2 and bad == []
+
+
+@pytest.mark.parametrize("mnem,ops", [(BF, "v[0:3], v[4:7]"), (F8, "v[0:7], v[8:15]")])
+def test_valu_write_right_before_an_operand_read(mnem, ops):
+    asm = ["\tv_cvt_pk_bf16_f32 v5, v30, v31", f"\t{mnem} v[100:115], {ops}, 0"]
+    assert len(check_valu_to_mfma("\n".join(asm))) == 1
+    asm.insert(1, "\ts_nop 1")                    # two wait states
+    assert check_valu_to_mfma("\n".join(asm)) == []
+    asm = ["\tv_cvt_pk_bf16_f32 v5, v30, v31", "\tv_add_u32 v40, v41, v42", f"\t{mnem} v[100:115], {ops}, 0"]
+    assert len(check_valu_to_mfma("\n".join(asm))) == 1   # one wait state is not enough
+    asm = ["\tv_cvt_pk_bf16_f32 v50, v30, v31", f"\t{mnem} v[100:115], {ops}, 0"]
+    assert check_valu_to_mfma("\n".join(asm)) == []       # an unrelated register
+
+
+def test_built_kernel_passes_both_checks():
+    path = os.path.join(ROOT, "paged_mla_decode_02_amd", "_build", "decode.gfx950.s")
+    if not os.path.exists(path):
+        pytest.skip("the library has not been built here")
+    text = open(path).read()
+    chains, bad = check_qk_chains(text)
+    assert chains > 0 and bad == []
+    assert check_valu_to_mfma(text) == []
