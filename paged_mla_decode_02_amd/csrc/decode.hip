@@ -12,9 +12,11 @@
 //
 // Every wave does all three stages of the attention:
 //   QK        wave w owns query rows 32w..32w+31 and keeps their queries (576
-//             dims, bf16; fp8 Q is converted at load) in registers. For tile t
-//             it computes S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys are
-//             the MFMA M side, the 576-dim latent the contraction).
+//             dims) in registers. For tile t it computes S^T = K Q^T (keys
+//             are the MFMA M side, the 576-dim latent the contraction): on
+//             v_mfma_f32_32x32x16_bf16 for bf16 KV, on the fp8
+//             v_mfma_f32_32x32x64_f8f6f4 for fp8 KV (fp8 Q as is; bf16 Q
+//             split exactly into two fp8 operands per row).
 //   softmax   the mask -- causal on positions: token i of a q_b-token block
 //             sits at L - q_b + i and sees keys j <= L - q_b + i (ATOM pull
 //             request 2760, Problem); non-causal: only the split's range (vLLM
@@ -41,10 +43,10 @@
 // matrix core) and publishes P^T(t-1); phase B runs the 32 PV products of
 // tile t-1 with the loads of tile t+2 spread between them.
 //
-// fp8 KV stays fp8 in LDS (half the HBM and LDS bytes) and is converted to
-// bf16 in registers when a K or V^T fragment is read (exact: every e4m3fn
-// value is a bf16 value), so the matrix core always computes in bf16. Scales
-// are applied to the fp32 scores and to O.
+// fp8 KV stays fp8 in LDS (half the HBM and LDS bytes). K fragments feed the
+// fp8 QK products as they are; V^T fragments are converted to bf16 in
+// registers for the bf16 PV products (exact: every e4m3fn value is a bf16
+// value). Scales are applied to the fp32 scores and to O.
 //
 // The epilogue writes bf16 O and the natural-log LSE when the row has one
 // split, or the split's normalized bf16 partial O and fp32 LSE_k to the
@@ -387,11 +389,10 @@ __device__ __forceinline__ float split_q_rows(u32x8 (&q)[2 * kKSteps8]) {
 //   half-wave's read sit in the four different 64-byte bank sectors, and its
 //   32 lanes cover all 64 banks once.
 //
-// fp8 tiles (the decode converts in registers, exactly):
-//   K: the QK k-steps are taken in pairs; pair j covers dims 32 j .. 32 j + 31
-//   and lane l reads 16 bytes, dims 32 j + 16 h .. +15 (h = l >> 5), of key
-//   i = l & 31: the first 8 are its elements of k-step 2 j, the last 8 of
-//   k-step 2 j + 1 (Q is loaded in the same order). Main chunk 2 j + h of
+// fp8 tiles (K read as fp8 QK operands; V^T converted in registers, exactly):
+//   K: pair j covers dims 32 j .. 32 j + 31 and lane l reads 16 bytes, dims
+//   32 j + 16 h .. +15 (h = l >> 5), of key i = l & 31; pairs 2 p and 2 p + 1
+//   form the A operand of fp8 product p (Q is loaded in the same order). Main chunk 2 j + h of
 //   row i is stored at (2 j) ^ xm, xm = h ^ swz_f8(i); rope chunk
 //   2 (j - 16) + h at (2 (j - 16)) ^ xr, xr = h ^ swz_f8_rope(i), rope row i
 //   at (i / 8) 1024 + (i % 8) 64.
@@ -644,16 +645,12 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
                                               f32x16 (&oacc)[kRowBlocks][kColTiles], Dma&& dma) {
   static_assert(kSmStride * kSoftmaxPieces <= kKSteps, "softmax pieces fit between the QK products");
   static_assert(NDMA == 0 || kDmaStride * (NDMA - 1) < 32, "loads fit between the PV products");
-  // bf16 K: fragments read kKDepth products ahead. fp8 K: 16-byte pairs read
-  // kRawDepth pairs ahead and each k-step converted two products ahead of its
-  // MFMA (so the conversion's VALU writes are far from the assembly MFMA
-  // that reads them).
-  constexpr int kRawDepth = 3;
+  // bf16 K: fragments read kKDepth products ahead; fp8 K: kK8Depth.
   constexpr int kK8Depth = 3;
   constexpr bool QF8 = QKM != 0;
-  static_assert(QKM == 0 ? NQ == kKSteps : (KV_FP8 && NQ == QKM * kKSteps8), "Q fragments of the QK mode");
+  static_assert(QKM == 0 ? (!KV_FP8 && NQ == kKSteps) : (KV_FP8 && NQ == QKM * kKSteps8),
+                "Q fragments of the QK mode");
   bf16x8 kb[kKDepth];
-  u32x4 raw[kRawDepth];
   u32x8 k8[kK8Depth];
   Softmax sm;
   f32x16 s_cur;
@@ -661,15 +658,9 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
     if constexpr (QF8) {
 #pragma unroll
       for (int d = 0; d < kK8Depth; ++d) k8[d] = k_prod_f8(smem, la, kmain, krope, d);
-    } else if constexpr (!KV_FP8) {
-#pragma unroll
-      for (int d = 0; d < kKDepth; ++d) kb[d] = k_frag(smem, la, kmain, krope, d);
     } else {
 #pragma unroll
-      for (int d = 0; d < kRawDepth; ++d) raw[d] = k_pair_f8(smem, la, kmain, krope, d);
-      kb[0] = fp8x8_to_bf16(raw[0][0], raw[0][1]);
-      kb[1] = fp8x8_to_bf16(raw[0][2], raw[0][3]);
-      raw[0] = k_pair_f8(smem, la, kmain, krope, kRawDepth);   // pair 0 is consumed
+      for (int d = 0; d < kKDepth; ++d) kb[d] = k_frag(smem, la, kmain, krope, d);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -688,20 +679,8 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
         else mfma8_qk_last(s_old, s_cur, a, qf[n]);   // s_old is dead: the softmax ended
       }
     } else if constexpr (QK) {
-      bf16x8 a;
-      if constexpr (!KV_FP8) {
-        a = kb[s % kKDepth];
-        if (s + kKDepth < kKSteps) kb[s % kKDepth] = k_frag(smem, la, kmain, krope, s + kKDepth);
-      } else {
-        a = kb[s % 3];
-        const int ks = s + 2, pj = ks >> 1;
-        if (ks < kKSteps) {
-          const u32x4 r = raw[pj % kRawDepth];
-          kb[ks % 3] = (ks & 1) ? fp8x8_to_bf16(r[2], r[3]) : fp8x8_to_bf16(r[0], r[1]);
-          if ((ks & 1) && pj + kRawDepth < kKSteps / 2)
-            raw[pj % kRawDepth] = k_pair_f8(smem, la, kmain, krope, pj + kRawDepth);
-        }
-      }
+      const bf16x8 a = kb[s % kKDepth];
+      if (s + kKDepth < kKSteps) kb[s % kKDepth] = k_frag(smem, la, kmain, krope, s + kKDepth);
       if (s == 0) mfma_qk_first(s_cur, a, qf[s]);
       else if (s + 1 < kKSteps) mfma_qk(s_cur, a, qf[s]);
       else mfma_qk_last(s_old, s_cur, a, qf[s]);   // s_old is dead: the softmax ended
@@ -798,11 +777,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     const int causal_lim = qpos >= 0 ? qpos / a.dcp_world : -1;
     const int pos_limit = (a.causal && row_ok) ? causal_lim : (L - 1);
     const int key_last = min(end - 1, pos_limit);   // last visible key of this row in the split
-    // The B operand of S^T = K Q^T: lane holds, for k-step ks, the 8 dims
-    // that the K fragment's lane half h = lane >> 5 holds: 16 ks + 8 h .. +7
-    // for bf16 KV; for fp8 KV (k-steps in pairs) 32 (ks / 2) + 16 h +
-    // 8 (ks & 1) .. +7. In 8-element units: 2 ks + h, or 4 (ks / 2) + 2 h +
-    // (ks & 1).
+    // The B operand of S^T = K Q^T. bf16 KV: lane holds, for k-step ks, the
+    // 8 dims that the K fragment's lane half h = lane >> 5 holds,
+    // 16 ks + 8 h .. +7, i.e. 8-element unit 2 ks + h.
     // With fp8 Q and KV the raw fp8 bytes of product p: 16-byte units
     // 4 p + h and 4 p + 2 + h. With bf16 Q and fp8 KV the same 32 elements
     // (bf16 units 8 p + 2 h, +1, 8 p + 4 + 2 h, +1) split into hi (qf[2 p])
@@ -812,7 +789,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     if (row_ok) {
       const int64_t qrow = ((int64_t)(q0 + tok) * H + head) * kDLat;
       const int h = lane >> 5;
-      auto unit = [&](int ks) { return KV_FP8 ? 4 * (ks >> 1) + 2 * h + (ks & 1) : 2 * ks + h; };
+      auto unit = [&](int ks) { return 2 * ks + h; };
       if constexpr (QKM == 1) {
         const u32x4* src = (const u32x4*)((const unsigned char*)a.q + qrow);
 #pragma unroll
