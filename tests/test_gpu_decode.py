@@ -63,38 +63,40 @@ def test_gather_bit_exact(lib, kv_dtype, offset):
 
 
 # --------------------------------------------------------------------------
-# The five workloads (full size; the oracle checks a sample of rows)
+# Every workload at full size, every row compared with the oracle, under
+# every plan the library offers: AUTO (the default), UNIFORM, LENGTH_AWARE,
+# and LENGTH_AWARE / UNIFORM with the split merge inside the decode kernel.
+# The benchmark times AUTO, so its path is among these.
 
-CONFIG_SAMPLES = {
-    "tiny_causal": None,
-    "verify_causal": "extremes",
-    "draft_noncausal": [0, 7],
-    "longctx_split": [0, 3],
-    "ragged_persistent_causal": "extremes",
-    "ragged_persistent_noncausal": "extremes",
-    "sparse_topk": [0, 17, 63],
-}
+WORKLOADS = ["tiny_causal", "verify_causal", "draft_noncausal", "longctx_split",
+             "ragged_persistent_causal", "ragged_persistent_noncausal", "sparse_topk"]
+PLAN_MODES = {"auto": 0, "uniform": 1, "length_aware": 2, "uniform_merge": 1 | 0x100,
+              "length_aware_merge": 2 | 0x100}
 
-
-def sample_rows(case, how):
-    if how is None:
-        return None
-    if how == "extremes":
-        lens = case.kv_lens
-        order = np.argsort(lens, kind="stable")
-        pick = {int(order[0]), int(order[-1]), int(order[len(order) // 2]), 1, case.rows - 1}
-        return sorted(pick)
-    return how
+_WORKLOAD_CACHE = {}
 
 
-@pytest.mark.parametrize("name", list(CONFIG_SAMPLES))
-def test_workload_parity(lib, name):
-    case = make_config(name)
-    O, LSE, words = run_gpu(case)
-    rows = sample_rows(case, CONFIG_SAMPLES[name])
-    ratio, lse_err = assert_parity(case, O, LSE, rows)
-    print(f"{name}: err/max={ratio:.2e} lse_err={lse_err:.2e} plan S={unpack_plan(words)['S']}")
-    assert not np.isnan(O).any() and not np.isnan(LSE).any()
+def workload_and_reference(name):
+    """The full-size case and the oracle's O / LSE of every row, computed once
+    per workload (the parametrization keeps one workload's tests together)."""
+    if name not in _WORKLOAD_CACHE:
+        _WORKLOAD_CACHE.clear()
+        case = make_config(name)
+        _WORKLOAD_CACHE[name] = (case, attend_case(case))
+    return _WORKLOAD_CACHE[name]
+
+
+@pytest.mark.parametrize("plan", list(PLAN_MODES))
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_workload_parity(lib, name, plan):
+    print(f"workload {name} plan {plan}", flush=True)
+    case, ref = workload_and_reference(name)
+    O, LSE, words = run_gpu(case, mode=PLAN_MODES[plan])
+    info = unpack_plan(words)
+    ratio, lse_err = assert_parity(case, O, LSE, ref=ref)
+    assert len(ref) == case.rows                      # every row was compared
+    print(f"{name} [{plan}]: err/max={ratio:.2e} lse_err={lse_err:.2e} S={info['S']} G={info['G']} "
+          f"P={info['P']}")
 
 
 # --------------------------------------------------------------------------

@@ -277,3 +277,51 @@ def index_set_capacity(name: str) -> int:
     if "sparse" in spec:
         return 3
     return max(1, int(spec["pool_slots"] // max(int(config_lengths(name).sum()), 1)))
+
+
+def make_logit_jump_case(seed: int, kv_lens: Sequence[int], heads: int, q_len: int, q_dtype: str,
+                         kv_dtype: str, causal: bool, pool_slots: int, period: int = 40,
+                         step: float = 3.0, q_level: float = 4.0, name: str = "logit_jump") -> Case:
+    """Inputs whose attention logits climb in large jumps along each row.
+
+    Every query (token, head) has q[0:64] = q_level plus N(0, 0.05) noise and
+    q[64:] = N(0, 0.05). Keys are N(0, 1), except that key j of a row with
+    j % period == period // 2 (a "hot" key) has k[0:64] = step * (j // period + 1),
+    and the key after it the same minus 0.05 (so the softmax mixes two keys).
+    The n-th hot key of a row thus scores about 64 * q_level * step * n above
+    an ordinary one: with the defaults and the softmax scale 1/sqrt(192),
+    about 80 * n in base 2, so any later tile holding a hot key beats the
+    first tile of its split by far more than its first-tile maximum.
+
+    Draw order: a slot permutation (rows take consecutive runs of it), pool
+    values, Q values; then the hot keys are written over their slots and
+    everything is stored (bf16 by RNE, fp8 with a per-tensor scale)."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(kv_lens, dtype=np.int64)
+    rows = int(lens.shape[0])
+    total = int(lens.sum())
+    if total > pool_slots:
+        raise ValueError("pool too small")
+    perm = rng.permutation(pool_slots).astype(np.int64)
+    pool = rng.standard_normal((pool_slots, D_LATENT), dtype=np.float32)
+    T = rows * q_len
+    q = (0.05 * rng.standard_normal((T, heads, D_LATENT))).astype(np.float32)
+    q[:, :, :64] += np.float32(q_level)
+    kv_indptr = np.zeros(rows + 1, dtype=np.int32)
+    kv_indptr[1:] = np.cumsum(lens)
+    kv_indices = perm[:total].astype(np.int32)
+    for b in range(rows):
+        base = int(kv_indptr[b])
+        for j in range(int(lens[b])):
+            if j % period == period // 2:
+                level = np.float32(step * (j // period + 1))
+                pool[kv_indices[base + j], :64] = level
+                if j + 1 < int(lens[b]):
+                    pool[kv_indices[base + j + 1], :64] = level - np.float32(0.05)
+    pool_codes, kv_scale = _store(pool, kv_dtype)
+    q_codes, q_scale = _store(q, q_dtype)
+    qo_indptr = (np.arange(rows + 1) * q_len).astype(np.int32)
+    return Case(name=name, rows=rows, q_len=q_len, heads=heads, causal=causal, q_dtype=q_dtype,
+                kv_dtype=kv_dtype, q_codes=q_codes, q_scale=q_scale, pool_codes=pool_codes,
+                kv_scale=kv_scale, qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=kv_indices,
+                sm_scale=SM_SCALE)
