@@ -86,7 +86,7 @@ typedef enum { MLA_BF16 = 0, MLA_FP8_E4M3 = 1 } mla_dtype;
 typedef enum { MLA_PLAN_AUTO = 0, MLA_PLAN_UNIFORM = 1, MLA_PLAN_LENGTH_AWARE = 2 } mla_plan_mode;
 
 /* OR into the plan mode to have split rows (at most 16 splits) merged inside
- * the decode kernel by the last of their splits to finish each 64-row tile,
+ * the decode kernel by the last of their splits to finish each 128-row tile,
  * instead of by a second kernel: one launch instead of two. It costs an L2
  * write-back per work item and an L2 invalidation per merged tile (the L2s
  * of the MI355X's eight XCDs are not coherent with each other), and on the
@@ -94,35 +94,47 @@ typedef enum { MLA_PLAN_AUTO = 0, MLA_PLAN_UNIFORM = 1, MLA_PLAN_LENGTH_AWARE = 
  * the request in its header mode word. */
 #define MLA_PLAN_MERGE_IN_KERNEL 0x100
 
-/* Upper bound on the int32 words mla_decode_plan can write for these sizes.
+/* Upper bound on the int32 words mla_decode_plan can write for these sizes,
+ * so that a caller can size the host plan buffer once (the plan sits next to
+ * the decode CSR on the host: ATOM pull request 2462, Summary part 1).
  * Host only; never fails for rows >= 1, heads in [1,128], q_len_max in [1,16],
- * num_cus >= 1. */
+ * num_cus >= 1. Errors: INVALID_ARG (null words_out, rows or num_cus < 1),
+ * UNSUPPORTED (heads or q_len_max out of range). */
 MLA_API int32_t mla_decode_plan_capacity(int32_t rows, int32_t num_cus, int32_t num_heads,
                                  int32_t q_len_max, int64_t* words_out);
 
-/* Build the split plan on the host (pure: the same inputs give the same
- * words). kv_lens: host [rows], each >= 0. num_cus: the device's compute-unit
- * count (256 on MI355X). plan: host buffer of plan_words int32, caller-owned;
- * on success word 19 holds the number of words written.
+/* Build the split plan on the host: per request row a split count and
+ * split_indptr, built next to the decode CSR, either uniform (the count
+ * depends only on the row count, the longest row and the config, so a graph
+ * captured with it replays with changing lengths) or planned per call from
+ * the real lengths (ATOM pull request 2462, Summary parts 1 and 2). Pure:
+ * the same inputs give the same words. kv_lens: host [rows], each >= 0.
+ * num_cus: the device's compute-unit count (256 on MI355X). plan: host buffer
+ * of plan_words int32, caller-owned; on success word 19 holds the number of
+ * words written.
  *
- * Plan words: a 20-word header [magic 0x4D4C4150, version 1, rows, heads,
- * q_len_max, kv_dtype, num_cus, mode_used, M_UNIT, u, N_MAX, MIN_SPLIT_KEYS,
- * ITEM_OVERHEAD, OCC, S, W, G, P, 20, total_words], then split_indptr[rows+1],
- * split_row[S], split_begin[S], split_end[S], split_part[S], work_indptr[G+1],
- * item_split[W], item_m[W]. S splits, W work items (split, M tile of 64 query
- * rows), G workgroups, P partial-buffer slots. Errors: INVALID_ARG (null,
- * negative length, too few words), UNSUPPORTED (heads, q_len_max or rows out
- * of range). */
+ * Plan words (spec version 3): a 20-word header [magic 0x4D4C4150, version 3,
+ * rows, heads, q_len_max, kv_dtype, num_cus, mode_used, M_UNIT (128), u,
+ * N_MAX (256), MIN_SPLIT_KEYS, ITEM_OVERHEAD, OCC, S, W, G, P, 20,
+ * total_words], then split_indptr[rows+1], split_row[S], split_begin[S],
+ * split_end[S], split_part[S], work_indptr[G+1], item_split[W], item_m[W].
+ * S splits, W work items (split, M tile of 128 query rows: row r of a request
+ * row's block is token r / heads, head r % heads), G workgroups, P
+ * partial-buffer slots. mode_used is UNIFORM or LENGTH_AWARE (AUTO resolved;
+ * | MLA_PLAN_MERGE_IN_KERNEL when asked). Errors: INVALID_ARG (null, negative
+ * length, too few words, unknown dtype or mode, num_cus < 1), UNSUPPORTED
+ * (heads, q_len_max or rows out of range, total length above 2^31 - 1). */
 MLA_API int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t num_heads,
                         int32_t q_len_max, mla_dtype kv_dtype, mla_plan_mode mode,
                         int32_t num_cus, int32_t* plan, int64_t plan_words);
 
-/* Workspace bytes mla_decode_fwd needs for this plan: 0 when no row is
- * split, else the partials (bf16 O, fp32 LSE), P * q_len_max * heads *
- * (512 * 2 + 4) bytes,
- * preceded for an MLA_PLAN_MERGE_IN_KERNEL plan by 256 KiB of split-arrival
- * counters. plan: host words from mla_decode_plan. Errors: INVALID_ARG,
- * PLAN_MISMATCH (bad magic or version). */
+/* Workspace bytes mla_decode_fwd needs for this plan (the per-device
+ * workspace that holds split partials until they are merged: ATOM pull
+ * request 2462, Summary part 1 and Dependencies): 0 when no row is split,
+ * else the partials (bf16 O, fp32 LSE), P * q_len_max * heads * (512 * 2 + 4)
+ * bytes, preceded for an MLA_PLAN_MERGE_IN_KERNEL plan by 256 KiB of
+ * split-arrival counters. plan: host words from mla_decode_plan. Errors:
+ * INVALID_ARG (null), PLAN_MISMATCH (bad magic, version or header). */
 MLA_API int32_t mla_decode_workspace_size(const int32_t* plan, int64_t* bytes_out);
 
 /* For an MLA_PLAN_MERGE_IN_KERNEL plan: zero the workspace's counter region

@@ -153,12 +153,77 @@ def _stream_handle(stream) -> Optional[int]:
     return int(s.cuda_stream)
 
 
+_CODE_DTYPES = None
+
+
+def _code_dtypes():
+    """torch dtypes accepted as the stored codes of each format: bf16 bits
+    (bfloat16 or int16), fp8 OCP e4m3fn codes (float8_e4m3fn or uint8)."""
+    global _CODE_DTYPES
+    if _CODE_DTYPES is None:
+        import torch
+        _CODE_DTYPES = {MLA_BF16: (torch.bfloat16, torch.int16),
+                        MLA_FP8_E4M3: (torch.float8_e4m3fn, torch.uint8)}
+    return _CODE_DTYPES
+
+
+def _need(cond, msg, exc=ValueError):
+    if not cond:
+        raise exc(msg)
+
+
+def _check_device_tensor(name, t, device, dtypes, dim=None):
+    import torch
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor", TypeError)
+    _need(t.is_cuda and t.device == device, f"{name} must be on {device}, got {t.device}")
+    _need(t.dtype in dtypes, f"{name} has dtype {t.dtype}; expected one of {list(dtypes)}", TypeError)
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dim is not None:
+        _need(t.dim() == dim, f"{name} must have {dim} dimensions, got shape {tuple(t.shape)}")
+
+
+def _check_decode_tensors(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, kv_indptr,
+                          kv_indices, rows, heads, q_len_max, o, lse, workspace=None):
+    """Host-side checks of everything the C ABI cannot see: tensor dtypes,
+    shapes, contiguity and device. The ABI then checks sizes, alignment and
+    the plan. Raises TypeError / ValueError; nothing is launched."""
+    import torch
+    codes = _code_dtypes()
+    dev = q.device if isinstance(q, torch.Tensor) else None
+    _check_device_tensor("q", q, dev, codes[q_dtype], 3)
+    _need(q.shape[1] == heads and q.shape[2] == D_LATENT,
+          f"q must be [tokens, {heads}, {D_LATENT}], got {tuple(q.shape)}")
+    _check_device_tensor("kv_pool", kv_pool, dev, codes[kv_dtype], 2)
+    _need(kv_pool.shape[1] == D_LATENT and kv_pool.shape[0] >= 1,
+          f"kv_pool must be [num_slots >= 1, {D_LATENT}], got {tuple(kv_pool.shape)}")
+    for name, t in (("q_scale", q_scale), ("kv_scale", kv_scale)):
+        if t is not None:
+            _check_device_tensor(name, t, dev, (torch.float32,))
+            _need(t.numel() >= 1, f"{name} must hold one float32")
+    for name, t, n in (("qo_indptr", qo_indptr, rows + 1), ("kv_indptr", kv_indptr, rows + 1),
+                       ("kv_indices", kv_indices, None)):
+        _check_device_tensor(name, t, dev, (torch.int32,), 1)
+        _need(n is None or t.numel() == n, f"{name} must have {n} entries, got {t.numel()}")
+    tokens = min(int(q.shape[0]), rows * q_len_max)    # at most q_len_max tokens per row
+    _check_device_tensor("o", o, dev, codes[MLA_BF16], 3)
+    _need(o.shape[1] == heads and o.shape[2] == D_V and o.shape[0] >= tokens,
+          f"o must be [>= {tokens}, {heads}, {D_V}] bf16, got {tuple(o.shape)}")
+    _check_device_tensor("lse", lse, dev, (torch.float32,), 2)
+    _need(lse.shape[1] == heads and lse.shape[0] >= tokens,
+          f"lse must be [>= {tokens}, {heads}] float32, got {tuple(lse.shape)}")
+    if workspace is not None:
+        _check_device_tensor("workspace", workspace, dev, (torch.uint8, torch.int8))
+
+
 def decode_fwd(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, kv_indptr, kv_indices,
                plan_host: np.ndarray, plan_dev, rows: int, heads: int, q_len_max: int, causal: bool,
                softmax_scale: float, o, lse, workspace=None, stream=None):
     """Enqueue mla_decode_fwd. Tensors are device tensors; q/kv_pool hold the
     stored codes (bf16 as int16/bfloat16, fp8 as uint8/float8_e4m3fn);
     q_scale/kv_scale are 1-element float32 device tensors or None."""
+    q_dtype, kv_dtype = _dtype_code(q_dtype), _dtype_code(kv_dtype)
+    _check_decode_tensors(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, kv_indptr,
+                          kv_indices, rows, heads, q_len_max, o, lse, workspace)
     ph = _host_i32(plan_host)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().mla_decode_fwd(
@@ -176,6 +241,12 @@ def decode_fwd_dcp(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, 
                    workspace=None, stream=None):
     """Enqueue mla_decode_fwd_dcp for shard dcp_rank of dcp_world (its own
     index lists and plan); kv_len_global is an int32 device tensor [rows]."""
+    import torch
+    q_dtype, kv_dtype = _dtype_code(q_dtype), _dtype_code(kv_dtype)
+    _check_decode_tensors(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, kv_indptr,
+                          kv_indices, rows, heads, q_len_max, o, lse, workspace)
+    _check_device_tensor("kv_len_global", kv_len_global, q.device, (torch.int32,), 1)
+    _need(kv_len_global.numel() == rows, f"kv_len_global must have {rows} entries")
     ph = _host_i32(plan_host)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().mla_decode_fwd_dcp(
@@ -202,6 +273,18 @@ def merge_shards(o_parts, lse_parts, o, lse, stream=None):
 
 def debug_gather(kv_pool, kv_dtype, kv_indptr, kv_indices, plan_host: np.ndarray, plan_dev,
                  rows: int, dense_out, stream=None):
+    """Enqueue mla_debug_gather: the decode kernel's gather of every split,
+    written as bf16 bits to dense_out [kv_indptr[rows] - kv_indptr[0], 576]."""
+    import torch
+    kv_dtype = _dtype_code(kv_dtype)
+    dev = kv_pool.device
+    _check_device_tensor("kv_pool", kv_pool, dev, _code_dtypes()[kv_dtype], 2)
+    _need(kv_pool.shape[1] == D_LATENT, f"kv_pool must be [num_slots, {D_LATENT}]")
+    for name, t in (("kv_indptr", kv_indptr), ("kv_indices", kv_indices)):
+        _check_device_tensor(name, t, dev, (torch.int32,), 1)
+    _need(kv_indptr.numel() == rows + 1, f"kv_indptr must have {rows + 1} entries")
+    _check_device_tensor("dense_out", dense_out, dev, _code_dtypes()[MLA_BF16], 2)
+    _need(dense_out.shape[1] == D_LATENT, f"dense_out must be [keys, {D_LATENT}]")
     ph = _host_i32(plan_host)
     st = load_library().mla_debug_gather(
         _ptr(kv_pool), _dtype_code(kv_dtype), int(kv_pool.shape[0]), _ptr(kv_indptr),

@@ -218,3 +218,17 @@ def test_workspace_init_errors(lib):
     assert lib.mla_decode_workspace_init(split.ctypes.data_as(P), FAKE + 4, need, None) == INVALID
     bad = split.copy(); bad[0] ^= 1
     assert lib.mla_decode_workspace_init(bad.ctypes.data_as(P), FAKE, need, None) == MISMATCH
+
+
+def test_binding_refuses_host_tensors():
+    """The binding's tensor checks run before any pointer reaches the ABI:
+    host tensors are refused."""
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((2, 16, 576), dtype=torch.bfloat16)
+    pool = torch.zeros((8, 576), dtype=torch.bfloat16)
+    i32 = torch.zeros(3, dtype=torch.int32)
+    o = torch.zeros((2, 16, 512), dtype=torch.bfloat16)
+    lse = torch.zeros((2, 16), dtype=torch.float32)
+    with pytest.raises(ValueError, match="must be on"):
+        lib_mod.decode_fwd(q, 0, None, pool, 0, None, i32, i32, i32, good_plan(), None, 2, 16, 1,
+                           True, 0.1, o, lse)

@@ -230,3 +230,49 @@ def test_deterministic_and_identical_rows(lib):
         assert np.array_equal(O1[4 * r:4 * r + 4], O1[0:4])
         assert np.array_equal(L1[4 * r:4 * r + 4], L1[0:4])
     assert_parity(case, O1, L1)
+
+
+def test_binding_refuses_bad_tensors(lib):
+    """The Python binding checks every tensor before the C ABI sees a pointer:
+    a uint8 pool declared bf16, a flattened pool, int64 index lists, short or
+    mistyped outputs and a tensor on the CPU are refused; nothing runs."""
+    import torch
+    case = make_case(96, [40, 70], heads=16, q_len=2, q_dtype=BF16, kv_dtype=BF16, causal=True,
+                     pool_slots=1024)
+    dev = lib.device_inputs(case.q_codes, None, case.pool_codes, None, case.qo_indptr, case.kv_indptr,
+                            case.kv_indices)
+    words = lib.plan(case.kv_lens, 16, 2, BF16)
+    plan_dev = torch.from_numpy(words).cuda()
+    T = case.num_tokens
+    good = dict(q=dev["q"], kv_pool=dev["kv_pool"], qo_indptr=dev["qo_indptr"], kv_indptr=dev["kv_indptr"],
+                kv_indices=dev["kv_indices"],
+                o=torch.full((T, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda"),
+                lse=torch.full((T, 16), float("nan"), dtype=torch.float32, device="cuda"))
+
+    def call(**over):
+        a = dict(good, **over)
+        lib.decode_fwd(a["q"], BF16, None, a["kv_pool"], BF16, None, a["qo_indptr"], a["kv_indptr"],
+                       a["kv_indices"], words, plan_dev, case.rows, 16, 2, True, float(case.sm_scale),
+                       a["o"], a["lse"])
+
+    bad = [
+        (TypeError, dict(kv_pool=dev["kv_pool"].view(torch.uint8))),          # bf16 pool as bytes
+        (ValueError, dict(kv_pool=dev["kv_pool"].view(-1))),                  # flattened pool
+        (TypeError, dict(kv_indptr=dev["kv_indptr"].long())),                 # int64 indptr
+        (TypeError, dict(kv_indices=dev["kv_indices"].long())),
+        (ValueError, dict(qo_indptr=dev["qo_indptr"][:-1])),                  # wrong length
+        (ValueError, dict(o=good["o"][:T - 1])),                              # too few tokens
+        (TypeError, dict(o=good["o"].float())),                               # not bf16
+        (TypeError, dict(lse=good["lse"].double())),
+        (ValueError, dict(q=dev["q"].view(T, 16 * 576))),                     # wrong shape
+        (ValueError, dict(q=dev["q"].cpu())),                                 # not on the GPU
+        (ValueError, dict(kv_pool=dev["kv_pool"][:, :288])),                  # not contiguous
+    ]
+    for exc, over in bad:
+        with pytest.raises(exc):
+            call(**over)
+    torch.cuda.synchronize()
+    assert torch.isnan(good["o"].float()).all()                               # nothing was written
+    call()
+    torch.cuda.synchronize()
+    assert_parity(case, good["o"].float().cpu().numpy(), good["lse"].cpu().numpy())
