@@ -187,6 +187,38 @@ MLA_API int32_t mla_decode_fwd(const void* q, mla_dtype q_dtype, const float* q_
                        int32_t q_len_max, int32_t causal, float softmax_scale, void* o,
                        float* lse, void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Bytes of the library-owned scratch that mla_decode_fwd_noalloc uses per GPU. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64LL << 20)
+
+/*
+ * mla_decode_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under graph capture, serving loops that may
+ * not call the allocator, harnesses that forbid hipMalloc. The split partials
+ * (and an in-kernel-merge plan's split counters) go to a static device array
+ * of MLA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library owns; each GPU the
+ * library runs on holds its own copy until the process ends. The call never
+ * allocates or frees memory. The caller still owns and passes the inputs and
+ * outputs; arguments and results are those of mla_decode_fwd (the same
+ * kernels run, so the outputs are bit-identical for the same plan).
+ * Every call on one GPU shares that GPU's array and the array keeps the last
+ * call's contents: calls that overlap on one GPU (two streams, two threads)
+ * race and must be ordered by the caller. For an in-kernel-merge plan the
+ * call first clears the counters it uses with a fill kernel (no memset), so
+ * the call may be captured in a graph.
+ * Errors: those of mla_decode_fwd, and WORKSPACE when the plan needs more
+ * than MLA_NOALLOC_SCRATCH_BYTES of scratch (mla_decode_workspace_size
+ * gives the need; use mla_decode_fwd with a caller workspace then), HIP when
+ * the scratch's device address cannot be looked up.
+ */
+MLA_API int32_t mla_decode_fwd_noalloc(const void* q, mla_dtype q_dtype, const float* q_scale,
+                                       const void* kv_pool, mla_dtype kv_dtype,
+                                       const float* kv_scale, int64_t num_slots,
+                                       const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                       const int32_t* kv_indices, const int32_t* plan_host,
+                                       const int32_t* plan_dev, int32_t rows, int32_t num_heads,
+                                       int32_t q_len_max, int32_t causal, float softmax_scale,
+                                       void* o, float* lse, void* stream);
+
 /*
  * Decode of one decode-context-parallel (DCP) shard. With dcp_world ranks the
  * KV of a row is dealt round-robin: rank dcp_rank holds the keys whose global

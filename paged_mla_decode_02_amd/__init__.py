@@ -61,6 +61,9 @@ def load_library(path: str = LIB_PATH):
     lib.mla_decode_fwd.argtypes = [vp, i32, vp, vp, i32, vp, i64, vp, vp, vp, p32, vp, i32, i32,
                                    i32, i32, ctypes.c_float, vp, vp, vp, i64, vp]
     lib.mla_decode_fwd.restype = i32
+    lib.mla_decode_fwd_noalloc.argtypes = [vp, i32, vp, vp, i32, vp, i64, vp, vp, vp, p32, vp, i32, i32,
+                                           i32, i32, ctypes.c_float, vp, vp, vp]
+    lib.mla_decode_fwd_noalloc.restype = i32
     lib.mla_debug_gather.argtypes = [vp, i32, i64, vp, vp, p32, vp, i32, vp, vp]
     lib.mla_debug_gather.restype = i32
     lib.mla_decode_fwd_dcp.argtypes = [vp, i32, vp, vp, i32, vp, i64, vp, vp, vp, p32, vp, i32, i32,
@@ -232,6 +235,27 @@ def decode_fwd(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, kv_i
         ph.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(plan_dev), rows, heads, q_len_max,
         1 if causal else 0, float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
         _stream_handle(stream))
+    _check(st)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_fwd_noalloc(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, kv_indptr,
+                       kv_indices, plan_host: np.ndarray, plan_dev, rows: int, heads: int,
+                       q_len_max: int, causal: bool, softmax_scale: float, o, lse, stream=None):
+    """Enqueue mla_decode_fwd_noalloc: decode_fwd with the split partials in
+    the library's static per-GPU scratch (no workspace, nothing allocated).
+    Calls that overlap on one GPU race."""
+    q_dtype, kv_dtype = _dtype_code(q_dtype), _dtype_code(kv_dtype)
+    _check_decode_tensors(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, kv_indptr,
+                          kv_indices, rows, heads, q_len_max, o, lse)
+    ph = _host_i32(plan_host)
+    st = load_library().mla_decode_fwd_noalloc(
+        _ptr(q), _dtype_code(q_dtype), _ptr(q_scale), _ptr(kv_pool), _dtype_code(kv_dtype),
+        _ptr(kv_scale), int(kv_pool.shape[0]), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices),
+        ph.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(plan_dev), rows, heads, q_len_max,
+        1 if causal else 0, float(softmax_scale), _ptr(o), _ptr(lse), _stream_handle(stream))
     _check(st)
 
 

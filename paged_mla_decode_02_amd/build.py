@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
-SOURCES = ["plan.cpp", "error.cpp", "api.cpp", "decode.hip", "kernels.hip", "cache_write.hip"]
+SOURCES = ["plan.cpp", "error.cpp", "api.cpp", "noalloc.hip", "decode.hip", "kernels.hip", "cache_write.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are turned off for all device code (the compiler would

@@ -37,16 +37,16 @@ int32_t check_plan_for_call(const int32_t* plan_host, const int32_t* plan_dev, i
 
 }  // namespace
 
-namespace {
-
-// Shared by mla_decode_fwd (world 1) and mla_decode_fwd_dcp.
-int32_t decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale, const void* kv_pool,
+// Shared by mla_decode_fwd (world 1), mla_decode_fwd_dcp and
+// mla_decode_fwd_noalloc.
+int32_t mla::decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale, const void* kv_pool,
                     mla_dtype kv_dtype, const float* kv_scale, int64_t num_slots,
                     const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                     const int32_t* plan_host, const int32_t* plan_dev, int32_t rows,
                     int32_t num_heads, int32_t q_len_max, int32_t causal, float softmax_scale,
                     void* o, float* lse, void* workspace, int64_t workspace_bytes, void* stream,
-                    int32_t dcp_world, int32_t dcp_rank, const int32_t* kv_len_global) {
+                    int32_t dcp_world, int32_t dcp_rank, const int32_t* kv_len_global,
+                    bool clear_counters) {
   if (!q || !kv_pool || !qo_indptr || !kv_indptr || !kv_indices || !plan_host || !o || !lse)
     return set_error(MLA_ERR_INVALID_ARG, "a required pointer is null");
   if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype))
@@ -119,7 +119,12 @@ int32_t decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale, cons
   a.uniform_ranges = v.mode == MLA_PLAN_UNIFORM;
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_decode(a, q_dtype == MLA_FP8_E4M3, kv_dtype == MLA_FP8_E4M3, v.G, s);
+  hipError_t e = hipSuccess;
+  if (clear_counters && a.inkernel_max_splits > 1) {
+    e = launch_zero((uint32_t*)a.counters, rows * v.u, s);
+    if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("counter clear launch: ") + hipGetErrorString(e));
+  }
+  e = launch_decode(a, q_dtype == MLA_FP8_E4M3, kv_dtype == MLA_FP8_E4M3, v.G, s);
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
   if (v.P > 0 && v.max_splits > a.inkernel_max_splits) {
     MergeArgs mg;
@@ -139,8 +144,6 @@ int32_t decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale, cons
   }
   return MLA_OK;
 }
-
-}  // namespace
 
 extern "C" int32_t mla_decode_fwd(const void* q, mla_dtype q_dtype, const float* q_scale,
                                   const void* kv_pool, mla_dtype kv_dtype, const float* kv_scale,

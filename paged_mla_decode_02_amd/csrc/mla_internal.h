@@ -59,4 +59,17 @@ inline int64_t workspace_bytes(const PlanView& v) {
 int32_t set_error(int32_t status, const std::string& msg);
 void clear_error();
 
+// The checks and launches behind mla_decode_fwd (dcp_world 1, dcp_rank 0,
+// kv_len_global null), mla_decode_fwd_dcp and mla_decode_fwd_noalloc. With
+// clear_counters, an in-kernel-merge plan's split-arrival counters are zeroed
+// by a fill kernel right before the decode (after every check has passed).
+int32_t decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale, const void* kv_pool,
+                    mla_dtype kv_dtype, const float* kv_scale, int64_t num_slots,
+                    const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                    const int32_t* plan_host, const int32_t* plan_dev, int32_t rows,
+                    int32_t num_heads, int32_t q_len_max, int32_t causal, float softmax_scale,
+                    void* o, float* lse, void* workspace, int64_t workspace_bytes, void* stream,
+                    int32_t dcp_world, int32_t dcp_rank, const int32_t* kv_len_global,
+                    bool clear_counters = false);
+
 }  // namespace mla

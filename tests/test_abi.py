@@ -30,7 +30,7 @@ def declared_symbols():
 
 def test_header_symbols_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 11
+    assert len(syms) == 12
     handle = ctypes.CDLL(lib_mod.LIB_PATH)
     for s in syms:
         assert hasattr(handle, s), s
@@ -218,6 +218,32 @@ def test_workspace_init_errors(lib):
     assert lib.mla_decode_workspace_init(split.ctypes.data_as(P), FAKE + 4, need, None) == INVALID
     bad = split.copy(); bad[0] ^= 1
     assert lib.mla_decode_workspace_init(bad.ctypes.data_as(P), FAKE, need, None) == MISMATCH
+
+
+def test_noalloc_argument_errors(lib):
+    """mla_decode_fwd_noalloc refuses, before touching any device, a plan whose
+    partials exceed the static scratch, a corrupted plan, and (with a plan that
+    needs no scratch) the argument errors of mla_decode_fwd."""
+    P = ctypes.POINTER(ctypes.c_int32)
+
+    def n(plan, q=FAKE, rows=ROWS, heads=H, qlen=QLEN):
+        p = np.ascontiguousarray(plan, np.int32)
+        return lib.mla_decode_fwd_noalloc(q, 0, None, FAKE, 0, None, 4096, FAKE, FAKE, FAKE,
+                                          p.ctypes.data_as(P), FAKE, rows, heads, qlen, 1, 0.1, FAKE,
+                                          FAKE, None)
+
+    big = lib_mod.plan([100000], 128, 16, 0, lib_mod.PLAN_UNIFORM, 4096)   # 256 splits of 16 x 128 rows
+    assert lib_mod.workspace_size(big) > lib_mod.NOALLOC_SCRATCH_BYTES
+    assert n(big, rows=1, heads=128, qlen=16) == WORKSPACE
+    assert "static scratch" in lib.mla_last_error().decode()
+    bad = good_plan().copy()
+    bad[0] ^= 1
+    assert n(bad) == MISMATCH
+    unsplit = lib_mod.plan([100, 0, 700], H, QLEN, 0, lib_mod.PLAN_UNIFORM, 1)
+    assert lib_mod.workspace_size(unsplit) == 0
+    assert n(unsplit, q=None) == INVALID
+    assert n(unsplit, heads=129) == UNSUPPORTED
+    assert n(unsplit, qlen=3) == MISMATCH
 
 
 def test_binding_refuses_host_tensors():
