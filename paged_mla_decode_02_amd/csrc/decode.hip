@@ -120,7 +120,7 @@ constexpr int kMaxInKernelSplits = 16;
 constexpr float kRefSlack = 64.0f;       // base-2 headroom above a row's reference max
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
 static_assert(kRows == 128, "the plan's M unit");
-static_assert(64 * kDV * 4 <= kTilesEnd, "epilogue staging of 64 fp32 rows");
+static_assert(kRows * kDV * 2 <= kTilesEnd, "epilogue staging of the item's 128 bf16 rows");
 
 // LDS offsets of tile t's buffers.
 template <bool KV_FP8> struct Layout;
@@ -145,6 +145,16 @@ __device__ __forceinline__ int swz_f8(int row) {
   return ((row & 3) << 2) | (((row >> 3) & 1) << 1) | ((row >> 2) & 1);
 }
 __device__ __forceinline__ int swz_f8_rope(int row) { return (row >> 2) & 3; }
+
+// Read-only launch metadata (plan words, indptrs, per-row lengths): nothing
+// writes it during a launch, so it is read through the constant address
+// space, which lets the compiler use scalar loads for uniform indices. Vector
+// loads would be ordered behind the previous work item's O stores (stores
+// count in the vector-memory counter), so each item's dependent chain of
+// metadata reads would first wait for those stores to be acknowledged.
+__device__ __forceinline__ int32_t ldc(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
 
 // ---------------------------------------------------------------------------
 // Tile loader (shared by the decode kernel and the gather test hook).
@@ -740,41 +750,48 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
   const float score_c = a.score_scale_log2 * q_scale * kv_scale;
 
   const int g = blockIdx.x;
-  const int it0 = a.plan[a.off_work_indptr + g], it1 = a.plan[a.off_work_indptr + g + 1];
+  const int it0 = ldc(a.plan, a.off_work_indptr + g), it1 = ldc(a.plan, a.off_work_indptr + g + 1);
   for (int it = it0; it < it1; ++it) {
-    const int s = a.plan[a.off_item_split + it];
-    const int m = a.plan[a.off_item_m + it];
-    const int b = a.plan[a.off_split_row + s];
-    const int part = a.plan[a.off_split_part + s];
-    const int q0 = a.qo_indptr[b], q_b = a.qo_indptr[b + 1] - q0;
-    const int kv0 = a.kv_indptr[b], L = a.kv_indptr[b + 1] - kv0;
-    const int s0 = a.plan[a.off_split_indptr + b];
-    const int nsplit = a.plan[a.off_split_indptr + b + 1] - s0;
+    const int s = ldc(a.plan, a.off_item_split + it);
+    const int m = ldc(a.plan, a.off_item_m + it);
+    const int b = ldc(a.plan, a.off_split_row + s);
+    const int part = ldc(a.plan, a.off_split_part + s);
+    const int q0 = ldc(a.qo_indptr, b), q_b = ldc(a.qo_indptr, b + 1) - q0;
+    const int kv0 = ldc(a.kv_indptr, b), L = ldc(a.kv_indptr, b + 1) - kv0;
+    const int s0 = ldc(a.plan, a.off_split_indptr + b);
+    const int nsplit = ldc(a.plan, a.off_split_indptr + b + 1) - s0;
     int begin, end;
     if (a.uniform_ranges) {   // split k of n covers [k L / n, (k + 1) L / n) of the live length
       begin = (int)((int64_t)(s - s0) * L / nsplit);
       end = (int)((int64_t)(s - s0 + 1) * L / nsplit);
     } else {
-      begin = a.plan[a.off_split_begin + s];
-      end = a.plan[a.off_split_end + s];
+      begin = ldc(a.plan, a.off_split_begin + s);
+      end = ldc(a.plan, a.off_split_end + s);
     }
     const int M = q_b * H;
     if (m * kRows >= M) continue;   // no query row in this tile (ragged block); uniform
     const int ntiles = (end - begin + kNT - 1) / kNT;
 
     // ---- this wave's query rows: m 128 + 32 w + (lane & 31)
-    const int mr = m * kRows + 32 * w + (lane & 31);
+    // Lane-derived values of the item head are recomputed from an opaque
+    // copy of the lane id: hoisted out of the item loop they would be spilled,
+    // and each reload from scratch is a vector-memory access whose wait also
+    // waits for the previous item's O stores.
+    const int ilane = opaque(lane);
+    const int mr = m * kRows + 32 * w + (ilane & 31);
     const bool row_ok = mr < M;
-    const int tok = row_ok ? mr / H : 0;
-    const int head = row_ok ? mr - tok * H : 0;
+    // (rows past the block's end get a token index past q_b; nothing of
+    // theirs is loaded or written)
+    const int tok = div_small(mr, opaque_s(H));
+    const int head = mr - tok * H;
     // Causal mask on global positions: local key j sits at j * world + rank
     // of the row's P keys over all shards, token tok at P - q_b + tok; the
     // visible local keys are j <= (P - q_b + tok - rank) / world (one shard:
     // j <= L - q_b + tok). Rows past the end of the block are computed but
     // never written; they take the non-causal limit.
-    const int Pk = a.kv_len_global ? a.kv_len_global[b] : L;
+    const int Pk = a.kv_len_global ? ldc(a.kv_len_global, b) : L;
     const int qpos = Pk - q_b + tok - a.dcp_rank;
-    const int causal_lim = qpos >= 0 ? qpos / a.dcp_world : -1;
+    const int causal_lim = qpos < 0 ? -1 : a.dcp_world == 1 ? qpos : qpos / opaque_s(a.dcp_world);
     const int pos_limit = (a.causal && row_ok) ? causal_lim : (L - 1);
     const int key_last = min(end - 1, pos_limit);   // last visible key of this row in the split
     // The B operand of S^T = K Q^T. bf16 KV: lane holds, for k-step ks, the
@@ -786,27 +803,37 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     // and lo (qf[2 p + 1]); score_row then carries the row's 2^-A.
     std::conditional_t<(QKM > 0), u32x8, bf16x8> qf[QKM == 0 ? kKSteps : QKM * kKSteps8];
     float score_row = score_c;
-    if (row_ok) {
-      const int64_t qrow = ((int64_t)(q0 + tok) * H + head) * kDLat;
-      const int h = lane >> 5;
+    // The split of bf16 queries for fp8 KV keeps its rows past the block's
+    // end at zero (loaded under a branch); the other modes load those rows as
+    // a copy of the block's last row (computed, never written), with no
+    // branch around the loads.
+    if (QKM != 2 || row_ok) {
+      // Query row (tok, head) of the block is row mr of the request row's
+      // [q_b * H, 576] block: a uniform row base plus a 32-bit lane offset.
+      constexpr int kQElem = Q_FP8 ? 1 : 2;
+      const unsigned char* qblock = (const unsigned char*)a.q + (int64_t)q0 * H * (kDLat * kQElem);
+      // (opaque: computed here, inside the branch, rather than hoisted above it
+      // and spilled)
+      const unsigned char* qsrc = qblock + (uint32_t)opaque(min(mr, M - 1)) * (uint32_t)(kDLat * kQElem);
+      const int h = ilane >> 5;
       auto unit = [&](int ks) { return 2 * ks + h; };
       if constexpr (QKM == 1) {
-        const u32x4* src = (const u32x4*)((const unsigned char*)a.q + qrow);
+        const u32x4* src = (const u32x4*)qsrc;
 #pragma unroll
         for (int p = 0; p < kKSteps8; ++p) qf[p] = cat8(src[4 * p + h], src[4 * p + 2 + h]);
       } else if constexpr (QKM == 2) {   // raw bf16 here; split once the item's first loads are out
-        const bf16x8* src = (const bf16x8*)((const uint16_t*)a.q + qrow);
+        const bf16x8* src = (const bf16x8*)qsrc;
 #pragma unroll
         for (int n = 0; n < 2 * kKSteps8; ++n) {
           const int u0 = 4 * n + 2 * h;   // bf16 units 8 p + 2 h (+1) for n = 2 p, 8 p + 4 + 2 h (+1) for 2 p + 1
           qf[n] = cat8(__builtin_bit_cast(u32x4, src[u0]), __builtin_bit_cast(u32x4, src[u0 + 1]));
         }
       } else if constexpr (!Q_FP8) {
-        const bf16x8* src = (const bf16x8*)((const uint16_t*)a.q + qrow);
+        const bf16x8* src = (const bf16x8*)qsrc;
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = src[unit(ks)];
       } else {
-        const u32x2* src = (const u32x2*)((const unsigned char*)a.q + qrow);
+        const u32x2* src = (const u32x2*)qsrc;
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) {
           const u32x2 v = src[unit(ks)];
@@ -835,7 +862,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         // 1, each preceded by one slot-list load so that every later wait
         // count has the same form; tile 0 lands.
 #pragma unroll
-        for (int t = 0; t < 4; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, w, lane);
+        for (int t = 0; t < 4; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, w, ilane);
         wait_vm<0>();
         if constexpr (QKM == 2) {
           // The raw queries have landed with the slot lists; the empty
@@ -846,9 +873,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          issue_slots(a.kv_indices, kv0, begin, end, t + 2, smem, w, lane);
+          issue_slots(a.kv_indices, kv0, begin, end, t + 2, smem, w, ilane);
           if (t < ntiles)
-            Dma::all(kv, read_slots(smem, t, w, lane), a.max_slot, smem, dma_main<KV_FP8>(t), dma_rope<KV_FP8>(t), w, lane);
+            Dma::all(kv, read_slots(smem, t, w, ilane), a.max_slot, smem, dma_main<KV_FP8>(t), dma_rope<KV_FP8>(t), w, ilane);
         }
         if constexpr (QKM == 2) {
           if (pass == 0) score_row = score_c * split_q_rows(qf);
@@ -875,7 +902,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
           auto dma = [&](int i) {
             Dma::op(i, kv, src, lds_addr_of(smem), dm, dr, w, dlane);
           };
-          const int lim_old = key_last - (begin + (t - 1) * kNT + 4 * (lane >> 5));
+          const int lim_old = key_last - (begin + (t - 1) * kNT + 4 * (dlane >> 5));
           const LaneAddr la_s = lane_addr<KV_FP8>(dlane, w);
           pipeline_step<DO_QK, PREV, DO_DMA ? Dma::n : 0, KV_FP8, FAST, QKM>(
               smem, la_s, qf, LY::main(t), LY::rope(t), s_old, score_row, lim_old, rs, p_buf(t + 1),
@@ -894,7 +921,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         // lim >= 27 on every lane (a lane's keys sit at most 27 past its
         // key0), i.e. for t < nfast, a prefix of the tiles (uniform).
         const int slack = __builtin_amdgcn_readfirstlane(
-            wave_min_i32(key_last - begin - 4 * (lane >> 5) - 27));
+            wave_min_i32(key_last - begin - 4 * (ilane >> 5) - 27));
         const int nfast = score_c > 0.f && slack >= 0 ? slack / kNT + 1 : 0;
         int t = 1;
         for (; t + 2 < ntiles && t - 1 < nfast; ++t) run_step(t, T_{}, T_{}, T_{}, T_{});
@@ -917,15 +944,16 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     if (lane < 32) lds_store(smem, kOffL + (w * 32 + lane) * 4, l_row);
     if (row_ok && lane < 32) {
       const float lse = l_row > 0.f ? (rs.m_ref + __log2f(l_row)) * kLn2 : -INFINITY;
-      if (part < 0) a.lse[(int64_t)(q0 + tok) * H + head] = lse;
-      else a.ws_lse[((int64_t)part * a.q_len_max + tok) * H + head] = lse;
+      // row mr of the block is (token tok, head): index (q0 + tok) H + head
+      if (part < 0) a.lse[(int64_t)q0 * H + mr] = lse;
+      else a.ws_lse[(int64_t)part * a.q_len_max * H + mr] = lse;
     }
     __syncthreads();
     // O leaves through LDS so that the stores are whole rows: the item's
     // query rows r = m 128 .. m 128 + 127 are consecutive rows of O (index
-    // q0 H + r) and of its partial slot (index (part q_len_max) H + r). Two
-    // halves of 64 rows; a half is staged as fp32 [64][512] in the tile region,
-    // 16-byte chunk c of row r at c ^ (r & 15).
+    // q0 H + r) and of its partial slot (index (part q_len_max) H + r). All
+    // 128 rows are staged at once in bf16 (1 KB per row, 128 KB of the tile
+    // region), 16-byte chunk c of row r at c ^ (r & 15).
     {
       // Opaque copies: the addresses below are recomputed here rather than
       // hoisted out of the item loop and kept live across it.
@@ -934,41 +962,36 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       const int64_t orow0 = part < 0 ? (int64_t)q0 * H + (int64_t)m * kRows
                                      : (int64_t)part * a.q_len_max * H + (int64_t)m * kRows;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      for (int rb = 0; rb < kRowBlocks; ++rb) {
+        const int r = 32 * rb + (el & 31);
+        const float l = lds_load<float>(smem, kOffL + r * 4);
+        const float inv = l > 0.f ? kv_scale / l : 0.f;
 #pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2) {
-          const int rb = 2 * half + r2;
-          const int r = 32 * r2 + (el & 31);   // row within the half
-          const float l = lds_load<float>(smem, kOffL + (rb * 32 + (el & 31)) * 4);
-          const float inv = l > 0.f ? kv_scale / l : 0.f;
+        for (int ct = 0; ct < kColTiles; ++ct)
 #pragma unroll
-          for (int ct = 0; ct < kColTiles; ++ct)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const f32x16& v = oacc[rb][ct];
-              const int c = 32 * w + 8 * ct + 2 * gq + hh;   // columns 4c .. 4c+3
-              lds_store(smem, r * 2048 + ((c ^ (r & 15)) << 4),
-                        f32x4{v[4 * gq] * inv, v[4 * gq + 1] * inv, v[4 * gq + 2] * inv, v[4 * gq + 3] * inv});
-            }
-        }
-        __syncthreads();
-        const int nrows = min(64, M - (m * kRows + 64 * half));   // rows of this half inside the block
-        uint16_t* const dst0 = part < 0 ? a.o : a.ws_o;            // bf16 O, or the split's partial O
-        // thread takes 8 columns (two staged chunks) of a row per store
-#pragma unroll 4
-        for (int i = 0; i < 64 * 64 / kDecodeThreads; ++i) {
-          const int p2 = i * kDecodeThreads + et;
-          const int r = p2 >> 6, c2 = p2 & 63;
-          if (r < nrows) {
-            const f32x4 x0 = lds_load<f32x4>(smem, r * 2048 + (((2 * c2) ^ (r & 15)) << 4));
-            const f32x4 x1 = lds_load<f32x4>(smem, r * 2048 + (((2 * c2 + 1) ^ (r & 15)) << 4));
-            *(bf16x8*)(dst0 + (orow0 + 64 * half + r) * kDV + 8 * c2) =
-                bf16x8{(__bf16)x0[0], (__bf16)x0[1], (__bf16)x0[2], (__bf16)x0[3],
-                       (__bf16)x1[0], (__bf16)x1[1], (__bf16)x1[2], (__bf16)x1[3]};
+          for (int gq = 0; gq < 4; ++gq) {
+            const f32x16& v = oacc[rb][ct];
+            // columns 4 c' .. 4 c' + 3 with c' = 32 w + 8 ct + 2 gq + hh: half hh
+            // of 16-byte chunk 16 w + 4 ct + gq
+            const int c = 16 * w + 4 * ct + gq;
+            const bf16x4 x{(__bf16)(v[4 * gq] * inv), (__bf16)(v[4 * gq + 1] * inv),
+                           (__bf16)(v[4 * gq + 2] * inv), (__bf16)(v[4 * gq + 3] * inv)};
+            lds_store(smem, r * (kDV * 2) + ((c ^ (r & 15)) << 4) + 8 * hh, x);
           }
-        }
-        __syncthreads();
       }
+      __syncthreads();
+      const int nrows = min(kRows, M - m * kRows);   // rows of the item inside the block
+      uint16_t* const dst0 = part < 0 ? a.o : a.ws_o;   // bf16 O, or the split's partial O
+      // a thread takes one staged chunk (8 columns) of a row per store
+#pragma unroll 4
+      for (int i = 0; i < kRows * 64 / kDecodeThreads; ++i) {
+        const int p2 = i * kDecodeThreads + et;
+        const int r = p2 >> 6, c2 = p2 & 63;
+        if (r < nrows)
+          *(bf16x8*)(dst0 + (orow0 + r) * kDV + 8 * c2) =
+              lds_load<bf16x8>(smem, r * (kDV * 2) + ((c2 ^ (r & 15)) << 4));
+      }
+      __syncthreads();
     }
 
     // A split row with few splits is merged here by the last of its splits
@@ -989,7 +1012,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       if (lds_load<uint32_t>(smem, kOffMisc) != 0u) {   // uniform
         if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // invalidates for the block
         __syncthreads();
-        merge_tile(a, m, M, nsplit, a.plan[a.off_split_part + s0], q0, tid);
+        merge_tile(a, m, M, nsplit, ldc(a.plan, a.off_split_part + s0), q0, tid);
         if (tid == 0) a.counters[b * a.u + m] = 0;
       }
       __syncthreads();

@@ -58,6 +58,24 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
+// The same for a wave-uniform value kept in a scalar register.
+__device__ __forceinline__ int opaque_s(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// n / d for 0 <= n < 2^20 and 1 <= d <= 2^16: a float estimate from the
+// hardware reciprocal (relative error below 2^-22, so the estimate is within
+// one of the quotient) corrected by one remainder test each way. Nothing of
+// it is hoisted out of a loop, unlike the compiler's division sequence.
+__device__ __forceinline__ int div_small(int n, int d) {
+  int q = (int)((float)n * __builtin_amdgcn_rcpf((float)d));
+  const int r = n - q * d;
+  q += r >= d ? 1 : 0;
+  q -= r < 0 ? 1 : 0;
+  return q;
+}
+
 template <typename T> __device__ __forceinline__ T lds_load(const lds_u8* base, int off) {
   return *(const __attribute__((address_space(3))) T*)(base + off);
 }
