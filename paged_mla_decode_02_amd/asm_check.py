@@ -97,3 +97,68 @@ def check_valu_to_mfma(asm: str):
                 break
             waits += 1
     return bad
+
+
+_M0 = re.compile(r"\bm0\b")
+
+
+def check_m0(asm: str):
+    """Return the instructions that touch M0 other than the direct-to-LDS load
+    sequences (s_mov_b32 m0, <sgpr>; s_nop 0; global_load_lds_*). Those
+    sequences are inline assembly that sets M0 without declaring it, which is
+    only safe while the compiler itself never keeps a value in M0."""
+    lines = [l.split(";", 1)[0].strip() for l in asm.splitlines()]
+    bad = []
+    for i, l in enumerate(lines):
+        if not l or l.startswith(".") or l.endswith(":") or not _M0.search(l):
+            continue
+        mnem, _, ops = l.partition(" ")
+        if mnem == "s_mov_b32" and ops.strip().startswith("m0,"):
+            nxt = [x for x in lines[i + 1:i + 4] if x and not x.startswith(".")]
+            if len(nxt) >= 2 and nxt[0].startswith("s_nop 0") and nxt[1].startswith("global_load_lds_"):
+                continue
+        bad.append(f"{i}: {l}")
+    return bad
+
+
+def _kernel_bodies(asm: str):
+    """(name, lines) of each kernel function in the assembly."""
+    lines = asm.splitlines()
+    out, cur, start = [], None, 0
+    for i, l in enumerate(lines):
+        m = re.match(r"^(_Z\w+):\s*(;.*)?$", l)
+        if m:
+            cur, start = m.group(1), i
+        elif cur and l.strip().startswith("s_endpgm"):
+            out.append((cur, lines[start:i + 1]))
+            cur = None
+    return out
+
+
+def check_scratch_in_step_loops(asm: str):
+    """Return the scratch (spill) accesses that sit inside a loop whose body
+    holds MFMA instructions and no nested loop: the per-tile step loops of the
+    decode kernel. A spill reload there is a vector-memory access whose wait
+    would also wait for the tile loads in flight."""
+    bad = []
+    for name, body in _kernel_bodies(asm):
+        code = [l.split(";", 1)[0].strip() for l in body]
+        labels = {}
+        for i, l in enumerate(code):
+            m = re.match(r"^(\.LBB\w+):", l)
+            if m:
+                labels[m.group(1)] = i
+        loops = []
+        for i, l in enumerate(code):
+            m = re.match(r"^s_(?:cbranch_\w+|branch)\s+(\.LBB\w+)", l)
+            if m and m.group(1) in labels and labels[m.group(1)] < i:
+                loops.append((labels[m.group(1)], i))
+        for lo, hi in loops:
+            if any(lo < a <= b < hi and (a, b) != (lo, hi) for a, b in loops):
+                continue   # not innermost
+            if not any(code[k].startswith("v_mfma") for k in range(lo, hi + 1)):
+                continue
+            for k in range(lo, hi + 1):
+                if code[k].startswith("scratch_"):
+                    bad.append(f"{name}: {k}: {code[k]}")
+    return bad

@@ -78,7 +78,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
 def _check_decode_asm(path):
     sys.path.insert(0, PKG)
     try:
-        from asm_check import check_qk_chains, check_valu_to_mfma
+        from asm_check import check_m0, check_qk_chains, check_scratch_in_step_loops, check_valu_to_mfma
     finally:
         sys.path.pop(0)
     with open(path) as f:
@@ -91,6 +91,14 @@ def _check_decode_asm(path):
     if hazards:
         raise RuntimeError(f"decode.hip: an assembly MFMA reads a VALU result without the required "
                            f"wait states (offending lines of {path}):\n" + "\n".join(hazards[:20]))
+    m0 = check_m0(text)
+    if m0:
+        raise RuntimeError(f"decode.hip: M0 is used outside the direct-to-LDS load sequences, which set "
+                           f"it without declaring it (offending lines of {path}):\n" + "\n".join(m0[:20]))
+    spills = check_scratch_in_step_loops(text)
+    if spills:
+        raise RuntimeError(f"decode.hip: a spill access sits inside a per-tile step loop "
+                           f"(offending lines of {path}):\n" + "\n".join(spills[:20]))
 
 
 def _wait(item, verbose):

@@ -1,8 +1,9 @@
 """The build-time checks of the decode kernel's generated code, on small
 hand-written instruction sequences: the inline-assembly QK accumulator chains
-(nothing may touch an open chain's registers between its links) and the
+(nothing may touch an open chain's registers between its links), the
 VALU -> assembly-MFMA operand hazard (the compiler inserts no wait states for
-inline assembly)."""
+inline assembly), M0 used only by the direct-to-LDS load sequences, and no
+spill reload inside a per-tile step loop."""
 import os
 import sys
 
@@ -10,7 +11,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, os.path.join(ROOT, "paged_mla_decode_02_amd"))
-from asm_check import check_qk_chains, check_valu_to_mfma  # noqa: E402
+from asm_check import check_m0, check_qk_chains, check_scratch_in_step_loops, check_valu_to_mfma  # noqa: E402
 
 BF = "v_mfma_f32_32x32x16_bf16"
 F8 = "v_mfma_f32_32x32x64_f8f6f4"
@@ -67,7 +68,31 @@ def test_valu_write_right_before_an_operand_read(mnem, ops):
     assert check_valu_to_mfma("\n".join(asm)) == []       # an unrelated register
 
 
-def test_built_kernel_passes_both_checks():
+def test_m0_only_in_lds_load_sequences():
+    ok = ["\ts_mov_b32 m0, s88", "\ts_nop 0", "\tglobal_load_lds_dwordx4 v[2:3], off"]
+    assert check_m0("\n".join(ok)) == []
+    for extra in ("\ts_mov_b32 m0, -1", "\tv_readlane_b32 s4, v1, m0", "\ts_sendmsg sendmsg(MSG_GS), m0"):
+        assert len(check_m0("\n".join(ok + [extra]))) == 1
+    # an M0 write whose load does not follow right away
+    assert check_m0("\n".join(["\ts_mov_b32 m0, s3", "\tv_add_u32 v1, v2, v3", ok[2]]))
+
+
+def kernel(body):
+    return ["_Zkern:", *body, "\ts_endpgm"]
+
+
+def test_scratch_in_step_loop_is_flagged():
+    step = [".LBB0_1:", f"\t{BF} v[0:15], v[16:19], v[20:23], v[0:15]", "\tds_read_b128 v[16:19], v30",
+            "\ts_cbranch_scc1 .LBB0_1"]
+    assert check_scratch_in_step_loops("\n".join(kernel(step))) == []
+    bad = step[:2] + ["\tscratch_load_dword v40, off, off offset:16"] + step[2:]
+    assert len(check_scratch_in_step_loops("\n".join(kernel(bad)))) == 1
+    # a reload in the enclosing item loop, outside the step loop, is allowed
+    outer = [".LBB0_0:", "\tscratch_load_dword v40, off, off offset:16"] + step + ["\ts_cbranch_scc0 .LBB0_0"]
+    assert check_scratch_in_step_loops("\n".join(kernel(outer))) == []
+
+
+def test_built_kernel_passes_the_checks():
     path = os.path.join(ROOT, "paged_mla_decode_02_amd", "_build", "decode.gfx950.s")
     if not os.path.exists(path):
         pytest.skip("the library has not been built here")
@@ -75,3 +100,5 @@ def test_built_kernel_passes_both_checks():
     chains, bad = check_qk_chains(text)
     assert chains > 0 and bad == []
     assert check_valu_to_mfma(text) == []
+    assert check_m0(text) == []
+    assert check_scratch_in_step_loops(text) == []
