@@ -144,10 +144,11 @@ def main():
     ap.add_argument("--workload", default="verify_causal")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work; 0 skips")
     ap.add_argument("--rotate", type=int, default=3, help="disjoint index lists cycled over steps")
-    ap.add_argument("--plan", default="length_aware", choices=["auto", "uniform", "length_aware"],
-                    help="split plan mode (the uniform plan is also timed beside it)")
-    ap.add_argument("--no-uniform", action="store_true",
-                    help="skip the comparison run with the uniform plan (counter passes use this)")
+    ap.add_argument("--plan", default="auto", choices=["auto", "uniform", "length_aware"],
+                    help="split plan mode (the library's default, AUTO, unless asked; the mode it did "
+                         "not use is also timed beside it)")
+    ap.add_argument("--no-uniform", "--no-other-plan", dest="no_uniform", action="store_true",
+                    help="skip the comparison run with the other plan mode (counter passes use this)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warm-up, one plain device copy of this many MiB: the known-size "
                          "reference for scaling hardware byte counters")
@@ -256,12 +257,12 @@ def main():
     fwd_p = [float(x) for x in np.percentile(fwd_ms, [10, 50, 90])]
 
     plan_info = mla_plan_info(words)
-    # The uniform plan (its split count depends only on the row count, the
-    # longest row and the config) timed the same way, for comparison.
-    uniform = None
-    if plan_info["mode"] != "uniform" and not args.no_uniform:
+    # The plan mode this run did not use, timed the same way, for comparison.
+    other = None
+    if not args.no_uniform:
+        other_mode = mla.PLAN_LENGTH_AWARE if plan_info["mode"] == "uniform" else mla.PLAN_UNIFORM
         dec_u = mla.MlaDecoder(case.heads, case.q_len, case.q_dtype, case.kv_dtype, case.causal,
-                               float(case.sm_scale), mode=mla.PLAN_UNIFORM)
+                               float(case.sm_scale), mode=other_mode)
         for k in range(args.warmup):
             words_u = step(k, dec=dec_u)
         evs_u = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -270,8 +271,9 @@ def main():
             words_u = step(k, evs_u[k], dec=dec_u)
         torch.cuda.synchronize()
         info_u = mla_plan_info(words_u)
-        uniform = {"launch_ms": round(float(np.mean([a.elapsed_time(b) for a, b in evs_u])), 4),
-                   "splits": info_u["S"], "workgroups": info_u["G"]}
+        other = {"plan_mode": info_u["mode"],
+                 "launch_ms": round(float(np.mean([a.elapsed_time(b) for a, b in evs_u])), 4),
+                 "splits": info_u["S"], "workgroups": info_u["G"]}
     elem = 2 if case.kv_dtype == "bf16" else 1
     keys = int(kv_lens.sum())
     kv_bytes = keys * 576 * elem
@@ -325,10 +327,10 @@ def main():
         "mfma_tflops": round(tflops_step, 2),
         "roofline": roof,
     }
-    if uniform is not None:
-        ach = flops / (uniform["launch_ms"] * 1e-3) / 1e12
-        uniform["mfma_frac"] = round(ach / peak_tflops, 4)
-        out["uniform_plan"] = uniform
+    if other is not None:
+        ach = flops / (other["launch_ms"] * 1e-3) / 1e12
+        other["mfma_frac"] = round(ach / peak_tflops, 4)
+        out["other_plan"] = other
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -80,9 +80,13 @@ typedef enum {
  * times its per-tensor scale is the real value. */
 typedef enum { MLA_BF16 = 0, MLA_FP8_E4M3 = 1 } mla_dtype;
 
-/* AUTO picks LENGTH_AWARE for fp8 KV with 128 heads and 15..32768 rows (the
- * persistent-kernel gate of ATOM pull request 2462, Summary part 2), else
- * UNIFORM. */
+/* UNIFORM gives every row the same split count (a plan that depends only on
+ * the row count, the longest row and the config); LENGTH_AWARE plans from
+ * the real lengths, as the persistent kernel of ATOM pull request 2462,
+ * Summary part 2 does. AUTO builds both and keeps the one whose estimated
+ * duration is shorter (keys plus a fixed cost per split: UNIFORM's
+ * costliest split or its total over the compute units, LENGTH_AWARE's
+ * fullest lane), UNIFORM on a tie. */
 typedef enum { MLA_PLAN_AUTO = 0, MLA_PLAN_UNIFORM = 1, MLA_PLAN_LENGTH_AWARE = 2 } mla_plan_mode;
 
 /* OR into the plan mode to have split rows (at most 16 splits) merged inside
@@ -113,7 +117,7 @@ MLA_API int32_t mla_decode_plan_capacity(int32_t rows, int32_t num_cus, int32_t 
  * of plan_words int32, caller-owned; on success word 19 holds the number of
  * words written.
  *
- * Plan words (spec version 3): a 20-word header [magic 0x4D4C4150, version 3,
+ * Plan words (spec version 4): a 20-word header [magic 0x4D4C4150, version 4,
  * rows, heads, q_len_max, kv_dtype, num_cus, mode_used, M_UNIT (128), u,
  * N_MAX (256), MIN_SPLIT_KEYS, ITEM_OVERHEAD, OCC, S, W, G, P, 20,
  * total_words], then split_indptr[rows+1], split_row[S], split_begin[S],

@@ -5,10 +5,9 @@ host and next to the decode CSR, a split count and a split_indptr per row
 (ATOM pull request 2462, "Summary", part 1); a uniform plan depends only on
 the row count and config, so graph capture and replay agree (same section);
 the persistent kernel instead plans from the real per-row KV lengths on every
-call (same page, "Summary", part 2), and its gate is fp8 KV, 128 local heads
-and 15 <= rows <= 32768. The constants and tie-breaks below are this
-library's own choice (spec version 3); the library's C++ planner must produce
-the same int32 words.
+call (same page, "Summary", part 2). The constants, tie-breaks and the AUTO
+rule below are this library's own choice (spec version 4); the library's C++
+planner must produce the same int32 words.
 
 Constants: M_UNIT 128 query rows per work item, N_MAX 256 splits per row,
 MIN_SPLIT_KEYS 256, ITEM_OVERHEAD 256 (a work item's fixed cost, in keys),
@@ -19,8 +18,13 @@ All arithmetic is integer; cdiv(a, b) = (a + b - 1) // b.
 Steps:
 1. u = cdiv(H * q_len_max, M_UNIT): M tiles per split. A query row is
    (token i, head h) at index i * H + h of its request row.
-2. Mode. AUTO means LENGTH_AWARE iff kv is fp8, H == 128 and
-   15 <= R <= 32768 (the persistent gate), else UNIFORM.
+2. Mode. AUTO builds the splits of both modes (steps 3 and 4) and estimates
+   each plan's duration in keys, a split costing its keys plus ITEM_OVERHEAD:
+   UNIFORM's is max(the costliest split, cdiv(u * the sum of split costs,
+   OCC*C)), its one-item workgroups being dealt to the compute units as they
+   free up; LENGTH_AWARE's is its fullest lane, T - the least room left
+   (step 4). AUTO takes LENGTH_AWARE when its estimate is strictly smaller,
+   else UNIFORM.
 3. UNIFORM: n = clamp(min(cdiv(OCC*C, R*u), cdiv(max L, MIN_SPLIT_KEYS)), 1,
    N_MAX); every row gets n splits; split k of row b covers keys
    [k*L_b // n, (k+1)*L_b // n) (empty ranges are legal).
@@ -61,7 +65,7 @@ Steps:
 8. LENGTH_AWARE: member j of lane l runs (s, j) for the lane's splits s in
    order. G = 1 + the largest workgroup id that has an item; the other
    workgroups below G have none.
-9. Words (int32): a 20-word header [magic 0x4D4C4150, version 1, R, H,
+9. Words (int32): a 20-word header [magic 0x4D4C4150, version 4, R, H,
    q_len_max, kv_dtype, C, mode_used (| 0x100 when the caller asked for the
    merge inside the decode kernel), M_UNIT, u, N_MAX, MIN_SPLIT_KEYS,
    ITEM_OVERHEAD, OCC, S, W, G, P, 20, total words], then split_indptr[R+1],
@@ -71,7 +75,7 @@ Steps:
 import numpy as np
 
 MAGIC = 0x4D4C4150
-VERSION = 3
+VERSION = 4
 HEADER_WORDS = 20
 M_UNIT = 128
 N_MAX = 256
@@ -95,12 +99,60 @@ def clamp(x, lo, hi):
     return max(lo, min(hi, x))
 
 
-def choose_mode(mode, kv_dtype, H, R):
-    if mode != MODE_AUTO:
-        return mode
-    if kv_dtype == KV_FP8 and H == 128 and 15 <= R <= 32768:
-        return MODE_LENGTH_AWARE
-    return MODE_UNIFORM
+def uniform_splits(lens, u, C):
+    """Step 3: (row, begin, end) of every split, in row order."""
+    R = len(lens)
+    n = clamp(min(cdiv(OCC * C, R * u), cdiv(max(lens), MIN_SPLIT_KEYS)), 1, N_MAX)
+    return [(b, k * L // n, (k + 1) * L // n) for b, L in enumerate(lens) for k in range(n)]
+
+
+def length_aware_splits(lens, u, C):
+    """Step 4: the lanes' pieces. Returns (splits in (row, first key) order,
+    each split's lane, X, the fullest lane's cost)."""
+    R = len(lens)
+    X = XCDS
+    while X > 1 and (OCC * C) // X < u:
+        X //= 2
+    lam = max(1, ((OCC * C) // X) // u)
+    n_lanes = X * lam
+    T = max(MIN_SPLIT_KEYS + ITEM_OVERHEAD, cdiv(sum(lens) + ITEM_OVERHEAD * (R + n_lanes), n_lanes),
+            cdiv(max(lens), N_MAX - 1) + ITEM_OVERHEAD)
+    room = [T] * n_lanes
+    pieces = []   # (row, begin, end, lane) in creation order
+
+    def roomiest():
+        best = 0
+        for l in range(1, n_lanes):
+            if room[l] > room[best]:
+                best = l
+        return best
+
+    order = sorted(range(R), key=lambda b: (-lens[b], b))
+    for b in order:
+        L = lens[b]
+        if L == 0:
+            pieces.append((b, 0, 0, roomiest()))
+            continue
+        pos, count = 0, 0
+        while pos < L:
+            lane = roomiest()
+            r = room[lane] - ITEM_OVERHEAD
+            if r >= L - pos or r < MIN_SPLIT_KEYS or count == N_MAX - 1:
+                take = L - pos
+            else:
+                take = r
+            pieces.append((b, pos, pos + take, lane))
+            room[lane] -= take + ITEM_OVERHEAD
+            pos += take
+            count += 1
+    pieces.sort(key=lambda p: (p[0], p[1]))
+    return [(b, lo, hi) for b, lo, hi, _ in pieces], [lane for *_, lane in pieces], X, n_lanes, T - min(room)
+
+
+def uniform_estimate(splits, u, C):
+    """Step 2: UNIFORM's duration estimate in keys."""
+    cost = [hi - lo + ITEM_OVERHEAD for _, lo, hi in splits]
+    return max(max(cost), cdiv(u * sum(cost), OCC * C))
 
 
 def plan_ref(kv_lens, H, q_len_max, kv_dtype, mode, C):
@@ -112,65 +164,30 @@ def plan_ref(kv_lens, H, q_len_max, kv_dtype, mode, C):
     if any(L < 0 for L in lens):
         raise ValueError("negative KV length")
 
-    # 1-2
+    # 1-4
     u = cdiv(H * q_len_max, M_UNIT)
     flag = mode & MERGE_IN_KERNEL
-    mode_used = choose_mode(mode & ~MERGE_IN_KERNEL, kv_dtype, H, R)
+    mode_req = mode & ~MERGE_IN_KERNEL
+    if mode_req != MODE_LENGTH_AWARE:
+        uni = uniform_splits(lens, u, C)
+    if mode_req != MODE_UNIFORM:
+        la, la_lane, X, n_lanes, la_est = length_aware_splits(lens, u, C)
+    if mode_req == MODE_AUTO:
+        mode_used = MODE_LENGTH_AWARE if la_est < uniform_estimate(uni, u, C) else MODE_UNIFORM
+    else:
+        mode_used = mode_req
 
     # 3-5: splits (row, key range), partial slots
-    split_row, split_begin, split_end = [], [], []
-    lane_splits = None
     if mode_used == MODE_UNIFORM:
-        n = clamp(min(cdiv(OCC * C, R * u), cdiv(max(lens), MIN_SPLIT_KEYS)), 1, N_MAX)
-        for b, L in enumerate(lens):
-            for k in range(n):
-                split_row.append(b)
-                split_begin.append(k * L // n)
-                split_end.append((k + 1) * L // n)
+        splits = uni
     else:
-        X = XCDS
-        while X > 1 and (OCC * C) // X < u:
-            X //= 2
-        lam = max(1, ((OCC * C) // X) // u)
-        n_lanes = X * lam
-        T = max(MIN_SPLIT_KEYS + ITEM_OVERHEAD, cdiv(sum(lens) + ITEM_OVERHEAD * (R + n_lanes), n_lanes),
-                cdiv(max(lens), N_MAX - 1) + ITEM_OVERHEAD)
-        room = [T] * n_lanes
-        pieces = []   # (row, begin, end, lane) in creation order
-
-        def roomiest():
-            best = 0
-            for l in range(1, n_lanes):
-                if room[l] > room[best]:
-                    best = l
-            return best
-
-        order = sorted(range(R), key=lambda b: (-lens[b], b))
-        for b in order:
-            L = lens[b]
-            if L == 0:
-                pieces.append((b, 0, 0, roomiest()))
-                continue
-            pos, count = 0, 0
-            while pos < L:
-                lane = roomiest()
-                r = room[lane] - ITEM_OVERHEAD
-                if r >= L - pos or r < MIN_SPLIT_KEYS or count == N_MAX - 1:
-                    take = L - pos
-                else:
-                    take = r
-                pieces.append((b, pos, pos + take, lane))
-                room[lane] -= take + ITEM_OVERHEAD
-                pos += take
-                count += 1
-        # split ids in (row, first key) order; lanes list their splits by id
-        pieces.sort(key=lambda p: (p[0], p[1]))
+        splits = la
         lane_splits = [[] for _ in range(n_lanes)]
-        for s_id, (b, lo, hi, lane) in enumerate(pieces):
-            split_row.append(b)
-            split_begin.append(lo)
-            split_end.append(hi)
+        for s_id, lane in enumerate(la_lane):
             lane_splits[lane].append(s_id)
+    split_row = [b for b, _, _ in splits]
+    split_begin = [lo for _, lo, _ in splits]
+    split_end = [hi for _, _, hi in splits]
     S = len(split_row)
     nsplit = [0] * R
     for b in split_row:

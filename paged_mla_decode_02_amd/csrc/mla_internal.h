@@ -8,11 +8,11 @@
 
 namespace mla {
 
-// Plan spec version 3 constants. The decode kernel's tile is compiled for
+// Plan spec version 4 constants. The decode kernel's tile is compiled for
 // kMUnit query rows; the planner writes the same value into every plan header
 // and the launcher refuses a plan whose header differs.
 constexpr int32_t kPlanMagic = 0x4D4C4150;
-constexpr int32_t kPlanVersion = 3;
+constexpr int32_t kPlanVersion = 4;
 constexpr int32_t kHeaderWords = 20;
 constexpr int32_t kMUnit = 128;
 constexpr int32_t kNMax = 256;

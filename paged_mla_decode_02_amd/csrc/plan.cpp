@@ -1,4 +1,4 @@
-// Host split planner (plan spec version 3).
+// Host split planner (plan spec version 4).
 //
 // A plan is a split count and split_indptr per request row, built on the host
 // next to the decode CSR ([DSV4] Tuned ASM FP8 decode with split plans, ATOM
@@ -6,7 +6,8 @@
 // count, the longest row and the config (the same page: such plans keep graph
 // capture and replay in agreement); LENGTH_AWARE plans follow the real per-row
 // lengths on every call, as the persistent decode kernel of the same page does
-// (Summary part 2), whose gate (fp8 KV, 128 heads, 15..32768 rows) AUTO uses.
+// (Summary part 2). AUTO builds both and keeps the one with the shorter
+// estimated duration.
 //
 // On top of the splits the plan fixes the launch. Work items are (split,
 // tile of 128 query rows); all M tiles of one split read the same keys, so
@@ -130,28 +131,28 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
   if (sum_len > INT32_MAX) return set_error(MLA_ERR_UNSUPPORTED, "total KV length exceeds int32");
 
   const int64_t u = cdiv((int64_t)num_heads * q_len_max, kMUnit);
-  int32_t used = base_mode;
-  if (used == MLA_PLAN_AUTO)
-    used = (kv_dtype == MLA_FP8_E4M3 && num_heads == 128 && rows >= 15 && rows <= 32768)
-               ? MLA_PLAN_LENGTH_AWARE
-               : MLA_PLAN_UNIFORM;
 
-  // Splits: (row, key range), in creation order.
-  std::vector<int32_t> srow, sbeg, send;
-  std::vector<std::vector<int32_t>> lane_splits;   // LENGTH_AWARE
+  // Splits of each mode: (row, key range), in row order.
+  struct Splits {
+    std::vector<int32_t> row, beg, end;
+  };
+  Splits uni, la;
+  std::vector<int32_t> la_lane;   // LENGTH_AWARE: each split's lane
   int32_t X = kXcds;
-  if (used == MLA_PLAN_UNIFORM) {
+  int64_t n_lanes = 0, la_est = 0;
+  if (base_mode != MLA_PLAN_LENGTH_AWARE) {
     int64_t n = std::min(cdiv((int64_t)kOcc * num_cus, (int64_t)rows * u), cdiv(max_len, kMinSplitKeys));
     n = std::clamp<int64_t>(n, 1, kNMax);
     if ((int64_t)rows * n > INT32_MAX) return set_error(MLA_ERR_UNSUPPORTED, "too many splits");
-    srow.reserve(rows * n);
+    uni.row.reserve(rows * n);
     for (int32_t b = 0; b < rows; ++b)
       for (int64_t k = 0; k < n; ++k) {
-        srow.push_back(b);
-        sbeg.push_back((int32_t)(k * kv_lens[b] / n));
-        send.push_back((int32_t)((k + 1) * kv_lens[b] / n));
+        uni.row.push_back(b);
+        uni.beg.push_back((int32_t)(k * kv_lens[b] / n));
+        uni.end.push_back((int32_t)((k + 1) * kv_lens[b] / n));
       }
-  } else {
+  }
+  if (base_mode != MLA_PLAN_UNIFORM) {
     // Lanes: u workgroups of one chiplet that run the same splits, one M
     // tile each, all with room T (keys + kItemOverhead per split). Rows go
     // longest first (ties by index) to the roomiest lane (lowest index among
@@ -159,7 +160,7 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
     const int64_t slots = (int64_t)kOcc * num_cus;
     while (X > 1 && slots / X < u) X /= 2;
     const int64_t lam = std::max<int64_t>(1, (slots / X) / u);
-    const int64_t n_lanes = X * lam;
+    n_lanes = X * lam;
     const int64_t T = std::max({(int64_t)kMinSplitKeys + kItemOverhead,
                                 cdiv(sum_len + (int64_t)kItemOverhead * (rows + n_lanes), n_lanes),
                                 cdiv(max_len, kNMax - 1) + kItemOverhead});
@@ -194,16 +195,40 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
         pos += take;
       }
     }
-    // Split ids in (row, first key) order; lanes list their splits by id.
+    // Split ids in (row, first key) order.
     std::sort(pieces.begin(), pieces.end(),
               [](const Piece& a, const Piece& b) { return a.row != b.row ? a.row < b.row : a.begin < b.begin; });
-    lane_splits.resize(n_lanes);
     for (const Piece& p : pieces) {
-      lane_splits[p.lane].push_back((int32_t)srow.size());
-      srow.push_back(p.row);
-      sbeg.push_back(p.begin);
-      send.push_back(p.end);
+      la.row.push_back(p.row);
+      la.beg.push_back(p.begin);
+      la.end.push_back(p.end);
+      la_lane.push_back(p.lane);
     }
+    la_est = T - *std::min_element(room.begin(), room.end());   // the fullest lane's cost
+  }
+
+  // AUTO: the mode whose duration estimate (keys, kItemOverhead per split) is
+  // smaller; UNIFORM's is max(costliest split, cdiv(u * total cost, OCC *
+  // CUs)), LENGTH_AWARE's its fullest lane; ties go to UNIFORM.
+  int32_t used = base_mode;
+  if (used == MLA_PLAN_AUTO) {
+    int64_t max_cost = 0, sum_cost = 0;
+    for (size_t s = 0; s < uni.row.size(); ++s) {
+      const int64_t c = (int64_t)uni.end[s] - uni.beg[s] + kItemOverhead;
+      max_cost = std::max(max_cost, c);
+      sum_cost += c;
+    }
+    const int64_t uni_est = std::max(max_cost, cdiv(u * sum_cost, (int64_t)kOcc * num_cus));
+    used = la_est < uni_est ? MLA_PLAN_LENGTH_AWARE : MLA_PLAN_UNIFORM;
+  }
+  const Splits& sp = used == MLA_PLAN_UNIFORM ? uni : la;
+  const std::vector<int32_t>& srow = sp.row;
+  const std::vector<int32_t>& sbeg = sp.beg;
+  const std::vector<int32_t>& send = sp.end;
+  std::vector<std::vector<int32_t>> lane_splits;   // LENGTH_AWARE: each lane's splits by id
+  if (used == MLA_PLAN_LENGTH_AWARE) {
+    lane_splits.resize(n_lanes);
+    for (size_t s = 0; s < la_lane.size(); ++s) lane_splits[la_lane[s]].push_back((int32_t)s);
   }
   const int32_t S = (int32_t)srow.size();
 
@@ -235,17 +260,17 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
     std::vector<int32_t> rank(S);
     std::iota(rank.begin(), rank.end(), 0);
     std::stable_sort(rank.begin(), rank.end(), [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
-    std::vector<std::vector<Item>> chiplet(X);
+    std::vector<std::vector<Item>> chiplet(kXcds);
     for (int32_t k = 0; k < S; ++k)
-      for (int32_t m = 0; m < (int32_t)u; ++m) chiplet[k % X].push_back({rank[k], m});
+      for (int32_t m = 0; m < (int32_t)u; ++m) chiplet[k % kXcds].push_back({rank[k], m});
     std::vector<Item> by_id(W);
     size_t n_min = SIZE_MAX, n_max = 0;
     for (auto& c : chiplet) { n_min = std::min(n_min, c.size()); n_max = std::max(n_max, c.size()); }
-    for (int32_t x = 0; x < X; ++x)
+    for (int32_t x = 0; x < kXcds; ++x)
       for (size_t j = 0; j < n_min; ++j) by_id[(size_t)kXcds * j + x] = chiplet[x][j];
     size_t next = (size_t)kXcds * n_min;
     for (size_t j = n_min; j < n_max; ++j)
-      for (int32_t x = 0; x < X; ++x)
+      for (int32_t x = 0; x < kXcds; ++x)
         if (j < chiplet[x].size()) by_id[next++] = chiplet[x][j];
     items = by_id;
     work_indptr.resize(G + 1);

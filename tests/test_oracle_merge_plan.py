@@ -58,6 +58,8 @@ def _check_fixture(fname):
     d = unpack_plan(words)
     for key, val in g["expect"].items():
         assert d[key] == val, (key, d[key], val)
+    auto = plan_ref(a["kv_lens"], a["H"], a["q_len_max"], a["kv_dtype"], MODE_AUTO, a["C"])
+    assert unpack_plan(auto)["mode"] == g["auto_mode"]
 
 
 def test_plan_fixture_uniform():
@@ -150,14 +152,53 @@ def test_plan_rejects_bad_arguments():
             plan_ref(args[0], args[1], args[2], KV_BF16, MODE_AUTO, 256)
 
 
-def test_auto_mode_on_the_five_workloads():
-    """AUTO follows the persistent gate (fp8 KV, 128 heads, 15..32768 rows):
-    the tiny case and the 128-head verify run one split, the long-context
-    case gets a uniform split, the large ragged batch plans from lengths."""
+def _estimates_from_words(words, C):
+    """The two duration estimates of the plan spec, recomputed from plan words
+    (not from the planner's internals): a split costs its keys plus
+    ITEM_OVERHEAD; a UNIFORM plan lasts max(its costliest split, cdiv(u times
+    its total cost, OCC*C)), a LENGTH_AWARE plan as long as its busiest
+    workgroup's items (an empty row's split taking no room)."""
+    d = unpack_plan(words)
+    cost = [e - b + ITEM_OVERHEAD for b, e in zip(d["split_begin"], d["split_end"])]
+    if d["mode"] & 0xFF == MODE_UNIFORM:
+        return max(max(cost), -(-d["u"] * sum(cost) // (OCC * C)))
+    # an empty row's split takes no room in a lane
+    wi = d["work_indptr"]
+    return max(sum(cost[s] for s in d["item_split"][wi[g]:wi[g + 1]] if d["split_end"][s] > d["split_begin"][s])
+               for g in range(d["G"]))
+
+
+def test_auto_mode_takes_the_shorter_estimate():
+    """AUTO equals the explicit mode whose plan is estimated shorter (ties to
+    UNIFORM), on random lengths and on every workload."""
+    rng = np.random.default_rng(77)
+    cases = []
+    for name, spec in CONFIGS.items():
+        kv = KV_FP8 if spec["kv_dtype"] == FP8 else KV_BF16
+        cases.append(([int(x) for x in config_lengths(name)], spec["heads"], spec["q_len"], kv, 256))
+    for _ in range(300):
+        R = int(rng.integers(1, 40))
+        lens = [int(x) for x in np.clip(np.rint(np.exp(rng.normal(7.0, 1.5, R))) - 20, 0, 100000)]
+        cases.append((lens, int(rng.integers(1, 129)), int(rng.integers(1, 17)), int(rng.integers(0, 2)),
+                      int(rng.choice([4, 16, 64, 256, 304]))))
+    for lens, H, q, kv, C in cases:
+        e_u = _estimates_from_words(plan_ref(lens, H, q, kv, MODE_UNIFORM, C), C)
+        e_la = _estimates_from_words(plan_ref(lens, H, q, kv, MODE_LENGTH_AWARE, C), C)
+        want = MODE_LENGTH_AWARE if e_la < e_u else MODE_UNIFORM
+        auto = plan_ref(lens, H, q, kv, MODE_AUTO, C)
+        assert unpack_plan(auto)["mode"] == want, (lens[:6], H, q, C, e_u, e_la)
+        assert np.array_equal(auto, plan_ref(lens, H, q, kv, want, C))
+
+
+def test_auto_mode_on_the_workloads():
+    """Under AUTO the tiny case runs one split per row and the equal-length
+    draft and top-k batches a uniform split; the 128-head verify, the long
+    rows and the ragged batch plan their lanes from the real lengths (the
+    choices that also measure faster on the GPU)."""
     C = 256
-    expect = {"tiny_causal": (MODE_UNIFORM, 1), "verify_causal": (MODE_UNIFORM, 1),
-              "draft_noncausal": (MODE_UNIFORM, None), "longctx_split": (MODE_UNIFORM, 64),
-              "ragged_persistent_causal": (MODE_LENGTH_AWARE, None)}
+    expect = {"tiny_causal": (MODE_UNIFORM, 1), "verify_causal": (MODE_LENGTH_AWARE, None),
+              "draft_noncausal": (MODE_UNIFORM, 8), "longctx_split": (MODE_LENGTH_AWARE, None),
+              "ragged_persistent_causal": (MODE_LENGTH_AWARE, None), "sparse_topk": (MODE_UNIFORM, 2)}
     for name, (mode, n) in expect.items():
         spec = CONFIGS[name]
         lens = [int(x) for x in config_lengths(name)]
