@@ -104,6 +104,25 @@ def traffic_from_counters(workload, fetch_csv, write_csv, copy_mib):
     return out
 
 
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_build():
+    """numpy's BLAS build (name, version, configuration)."""
+    try:
+        b = np.show_config(mode="dicts").get("Build Dependencies", {}).get("blas", {})
+        return " ".join(str(b.get(k, "")) for k in ("name", "version", "openblas configuration")).strip()
+    except Exception:
+        return "unknown"
+
+
 def cpu_baseline(case, budget_s):
     """Time the float64 oracle on whole rows of the workload until about
     budget_s seconds of CPU work (at least one row)."""
@@ -131,7 +150,7 @@ def cpu_baseline(case, budget_s):
         else:
             passes += 1
     return {"value": keys_done * 576 * elem / t_used / 1e9, "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": host_cpu_model(), "blas": blas_build(),
             "sample": f"{rows_done} row evaluations ({passes} full passes) over the {case.rows} rows of "
                       f"{case.name}, {keys_done} keys, float64 numpy, {t_used:.1f} s"}
 
@@ -155,6 +174,9 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="only turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-mib run into profiles/traffic_<workload>.json")
+    ap.add_argument("--graph-replay", type=int, default=0, metavar="N",
+                    help="also capture one decode call (plan uploaded, workspace allocated beforehand) "
+                         "in a HIP graph and time N back-to-back replays: the launch-amortized call time")
     ap.add_argument("--op", default="decode", choices=["decode", "cache_write", "dcp"],
                     help="decode: the hot path (default); cache_write: the latent cache writer; "
                          "dcp: one decode-context-parallel rank and the shard merge")
@@ -331,9 +353,53 @@ def main():
         ach = flops / (other["launch_ms"] * 1e-3) / 1e12
         other["mfma_frac"] = round(ach / peak_tflops, 4)
         out["other_plan"] = other
+    if args.graph_replay > 0:
+        out["graph_replay"] = graph_replay(args.graph_replay, dec, mla, inputs[0], dev, case, o, lse, flops)
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def graph_replay(n, dec, mla, inp, dev, case, o, lse, flops):
+    """One mla_decode_fwd call captured in a HIP graph (the plan built and
+    uploaded and the workspace allocated before capture), replayed n times
+    back to back between two events: the call time with the launch cost
+    amortized. The replays recompute the same outputs; the last one is
+    compared bit for bit with an eager call."""
+    import torch
+    words = dec.make_plan(case.kv_lens)
+    plan_dev = dec.upload_plan(words)
+    ws = dec.workspace(words)
+    torch.cuda.synchronize()
+
+    def call():
+        mla.decode_fwd(inp["q"], dec.q_dtype, dev["q_scale"], dev["kv_pool"], dec.kv_dtype, dev["kv_scale"],
+                       dev["qo_indptr"], dev["kv_indptr"], inp["kv_indices"], words, plan_dev, case.rows,
+                       case.heads, case.q_len, case.causal, float(case.sm_scale), o, lse, ws)
+
+    call()
+    torch.cuda.synchronize()
+    eager = (o.clone(), lse.clone())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.synchronize()
+    for _ in range(10):
+        g.replay()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(n):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / n
+    same = torch.equal(o.view(torch.int16), eager[0].view(torch.int16)) and torch.equal(lse, eager[1])
+    return {"calls": n, "us_per_call": round(us, 3), "mfma_tflops": round(flops / (us * 1e-6) / 1e12, 2),
+            "matches_eager": bool(same)}
 
 
 def bench_cache_write(args):

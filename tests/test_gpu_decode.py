@@ -68,7 +68,7 @@ def test_gather_bit_exact(lib, kv_dtype, offset):
 # and LENGTH_AWARE / UNIFORM with the split merge inside the decode kernel.
 # The benchmark times AUTO, so its path is among these.
 
-WORKLOADS = ["tiny_causal", "verify_causal", "draft_noncausal", "longctx_split",
+WORKLOADS = ["tiny_causal", "verify_causal", "verify_causal_fp8kv", "draft_noncausal", "longctx_split",
              "ragged_persistent_causal", "ragged_persistent_noncausal", "sparse_topk"]
 PLAN_MODES = {"auto": 0, "uniform": 1, "length_aware": 2, "uniform_merge": 1 | 0x100,
               "length_aware_merge": 2 | 0x100}

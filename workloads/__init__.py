@@ -226,6 +226,10 @@ CONFIGS = {
     # 32 rows, 7 draft + 1 token verify, 128 heads, bf16, lengths U[1024, 8192], 512k pool
     "verify_causal": dict(seed=2, lens_fn=_lens_c2, heads=128, q_len=8, q_dtype=BF16,
                           kv_dtype=BF16, causal=True, pool_slots=524288),
+    # the same batch (same seed, so the same lengths) with an fp8 e4m3 KV cache
+    # and bf16 Q: the shape the headline metric names (128 heads, q_len 8, fp8 KV)
+    "verify_causal_fp8kv": dict(seed=2, lens_fn=_lens_c2, heads=128, q_len=8, q_dtype=BF16,
+                                kv_dtype=FP8, causal=True, pool_slots=524288),
     # 8 rows, block of 8, 64 heads, fp8 Q and KV, 8192 keys per row, non-causal
     "draft_noncausal": dict(seed=3, kv_lens=[8192] * 8, heads=64, q_len=8, q_dtype=FP8,
                             kv_dtype=FP8, causal=False, pool_slots=524288),
