@@ -174,6 +174,10 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="only turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-mib run into profiles/traffic_<workload>.json")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="before the warm-up steps, run untimed decode calls until the GPU has been busy "
+                         "this long and two consecutive batches of 10 calls agree within 2%% (clocks settle "
+                         "under sustained load); 0 skips")
     ap.add_argument("--graph-replay", type=int, default=0, metavar="N",
                     help="also capture one decode call (plan uploaded, workspace allocated beforehand) "
                          "in a HIP graph and time N back-to-back replays: the launch-amortized call time")
@@ -256,6 +260,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    settle = settle_device(step, args.settle_ms) if args.settle_ms > 0 else None
     for k in range(args.warmup):
         words = step(k)
     torch.cuda.synchronize()
@@ -353,11 +358,37 @@ def main():
         ach = flops / (other["launch_ms"] * 1e-3) / 1e12
         other["mfma_frac"] = round(ach / peak_tflops, 4)
         out["other_plan"] = other
+    if settle is not None:
+        out["settle"] = settle
     if args.graph_replay > 0:
         out["graph_replay"] = graph_replay(args.graph_replay, dec, mla, inputs[0], dev, case, o, lse, flops)
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def settle_device(step, settle_ms, batch=10, cap_ms=3000.0):
+    """Untimed decode calls until the device has run them for settle_ms and two
+    consecutive batches of `batch` calls agree within 2% (or cap_ms of GPU
+    time has passed). Under sustained load the GPU's clocks take tens of
+    milliseconds to settle; the timed steps should see the settled device,
+    as a serving loop does. Returns the calls made and the GPU time spent."""
+    import torch
+    total, calls, prev = 0.0, 0, None
+    while True:
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for k in range(batch):
+            step(calls + k)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1)
+        total += ms
+        calls += batch
+        if (total >= settle_ms and prev is not None and abs(ms - prev) <= 0.02 * prev) or total >= cap_ms:
+            break
+        prev = ms
+    return {"calls": calls, "gpu_ms": round(total, 2), "last_batch_ms_per_call": round(ms / batch, 4)}
 
 
 def graph_replay(n, dec, mla, inp, dev, case, o, lse, flops):
