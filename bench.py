@@ -178,6 +178,8 @@ def main():
                     help="before the warm-up steps, run untimed decode calls until the GPU has been busy "
                          "this long and two consecutive batches of 10 calls agree within 2%% (clocks settle "
                          "under sustained load); 0 skips")
+    ap.add_argument("--fp8-pv", action="store_true",
+                    help="fp8 PV products (plan flag PLAN_FP8_PV; fp8-KV workloads only)")
     ap.add_argument("--graph-replay", type=int, default=0, metavar="N",
                     help="also capture one decode call (plan uploaded, workspace allocated beforehand) "
                          "in a HIP graph and time N back-to-back replays: the launch-amortized call time")
@@ -223,8 +225,11 @@ def main():
     inputs = [dict(dev, kv_indices=t) for t in idx_dev]
     plan_modes = {"auto": mla.PLAN_AUTO, "uniform": mla.PLAN_UNIFORM,
                   "length_aware": mla.PLAN_LENGTH_AWARE}
+    if args.fp8_pv and case.kv_dtype != "fp8":
+        raise SystemExit("--fp8-pv needs a workload with fp8 KV")
+    pv_flag = mla.PLAN_FP8_PV if args.fp8_pv else 0
     dec = mla.MlaDecoder(case.heads, case.q_len, case.q_dtype, case.kv_dtype, case.causal,
-                         float(case.sm_scale), mode=plan_modes[args.plan])
+                         float(case.sm_scale), mode=plan_modes[args.plan] | pv_flag)
     T = case.num_tokens
     o = torch.empty((T, case.heads, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((T, case.heads), dtype=torch.float32, device="cuda")
@@ -289,7 +294,7 @@ def main():
     if not args.no_uniform:
         other_mode = mla.PLAN_LENGTH_AWARE if plan_info["mode"] == "uniform" else mla.PLAN_UNIFORM
         dec_u = mla.MlaDecoder(case.heads, case.q_len, case.q_dtype, case.kv_dtype, case.causal,
-                               float(case.sm_scale), mode=other_mode)
+                               float(case.sm_scale), mode=other_mode | pv_flag)
         for k in range(args.warmup):
             words_u = step(k, dec=dec_u)
         evs_u = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -313,15 +318,15 @@ def main():
     # rows, since one mla_decode_fwd call launches both).
     q_elem = 2 if case.q_dtype == "bf16" else 1
     alg_bytes = (kv_bytes + keys * 4 + T * case.heads * 576 * q_elem + T * case.heads * (512 * 2 + 4))
-    # With fp8 Q and KV the QK products (576 of every 1088 flops) run on the
-    # fp8 matrix core and PV on bf16: the peak is the rate at which both
-    # parts would finish at their own dtype's peak.
-    if case.q_dtype == "fp8" and case.kv_dtype == "fp8":
-        compute_dtype = "fp8+bf16"
-        peak_tflops = (576 + 512) / (576 / MFMA_PEAK_TFLOPS["fp8"] + 512 / MFMA_PEAK_TFLOPS["bf16"])
-    else:
-        compute_dtype = "bf16"
-        peak_tflops = MFMA_PEAK_TFLOPS["bf16"]
+    # QK (576 of every 1088 flops) runs at the fp8 rate with fp8 Q and KV and
+    # at the bf16 rate otherwise (bf16 Q against fp8 KV takes two fp8
+    # products, hi and lo, per bf16 one); PV at the fp8 rate with the fp8 PV
+    # products and at the bf16 rate otherwise. The peak is the rate at which
+    # both parts would finish at their own dtype's peak.
+    qk_dt = "fp8" if (case.q_dtype == "fp8" and case.kv_dtype == "fp8") else "bf16"
+    pv_dt = "fp8" if args.fp8_pv else "bf16"
+    compute_dtype = qk_dt if qk_dt == pv_dt else f"{qk_dt}+{pv_dt}"
+    peak_tflops = (576 + 512) / (576 / MFMA_PEAK_TFLOPS[qk_dt] + 512 / MFMA_PEAK_TFLOPS[pv_dt])
     achieved_tflops = flops / (fwd_avg * 1e-3) / 1e12
     achieved_gbs = alg_bytes / (fwd_avg * 1e-3) / 1e9
     ridge = peak_tflops * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -348,7 +353,7 @@ def main():
         "dtype": compute_dtype, "data": "synthetic",
         "config": {"workload": args.workload, "rows": case.rows, "q_len": case.q_len,
                    "heads": case.heads, "q_dtype": case.q_dtype, "kv_dtype": case.kv_dtype,
-                   "causal": case.causal, "kv_keys": keys, "plan_mode": plan_info["mode"],
+                   "causal": case.causal, "kv_keys": keys, "pv_dtype": pv_dt, "plan_mode": plan_info["mode"],
                    "splits": plan_info["S"], "workgroups": plan_info["G"],
                    "index_rotation": len(inputs), "cache_flush": flush is not None},
         "mfma_tflops": round(tflops_step, 2),
@@ -563,7 +568,7 @@ def mla_plan_info(words):
     names = ["magic", "version", "R", "H", "q_len_max", "kv_dtype", "C", "mode", "M_UNIT", "u",
              "N_MAX", "MIN_SPLIT_KEYS", "ITEM_OVERHEAD", "OCC", "S", "W", "G", "P"]
     d = dict(zip(names, [int(x) for x in words[:18]]))
-    d["mode"] = {1: "uniform", 2: "length_aware"}.get(d["mode"], d["mode"])
+    d["mode"] = {1: "uniform", 2: "length_aware"}.get(d["mode"] & 0xFF, d["mode"])
     return d
 
 

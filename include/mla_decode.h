@@ -98,6 +98,17 @@ typedef enum { MLA_PLAN_AUTO = 0, MLA_PLAN_UNIFORM = 1, MLA_PLAN_LENGTH_AWARE = 
  * the request in its header mode word. */
 #define MLA_PLAN_MERGE_IN_KERNEL 0x100
 
+/* OR into the plan mode (fp8 KV only) to run the PV products in fp8: P is
+ * rounded to e4m3 after a power-of-two scale per (query row, 32-key tile)
+ * that puts the tile's largest weight in (128, 256], and the products
+ * (v_mfma_scale_f32_32x32x64_f8f6f4, two tiles per product) take that scale
+ * back out exactly, so V is never converted. It halves the matrix-core work
+ * of PV against the bf16 PV products; the price is P's 4-bit significand
+ * (the measured error stays inside the fp8 tolerance, 4e-2 of max|O|). The
+ * plan records the request in its header mode word; mla_decode_plan refuses
+ * it (UNSUPPORTED) with bf16 KV or together with MLA_PLAN_MERGE_IN_KERNEL. */
+#define MLA_PLAN_FP8_PV 0x200
+
 /* Upper bound on the int32 words mla_decode_plan can write for these sizes,
  * so that a caller can size the host plan buffer once (the plan sits next to
  * the decode CSR on the host: ATOM pull request 2462, Summary part 1).
@@ -125,9 +136,11 @@ MLA_API int32_t mla_decode_plan_capacity(int32_t rows, int32_t num_cus, int32_t 
  * S splits, W work items (split, M tile of 128 query rows: row r of a request
  * row's block is token r / heads, head r % heads), G workgroups, P
  * partial-buffer slots. mode_used is UNIFORM or LENGTH_AWARE (AUTO resolved;
- * | MLA_PLAN_MERGE_IN_KERNEL when asked). Errors: INVALID_ARG (null, negative
- * length, too few words, unknown dtype or mode, num_cus < 1), UNSUPPORTED
- * (heads, q_len_max or rows out of range, total length above 2^31 - 1). */
+ * | MLA_PLAN_MERGE_IN_KERNEL and | MLA_PLAN_FP8_PV when asked). Errors:
+ * INVALID_ARG (null, negative length, too few words, unknown dtype or mode,
+ * num_cus < 1), UNSUPPORTED (heads, q_len_max or rows out of range, total
+ * length above 2^31 - 1, MLA_PLAN_FP8_PV with bf16 KV or with
+ * MLA_PLAN_MERGE_IN_KERNEL). */
 MLA_API int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t num_heads,
                         int32_t q_len_max, mla_dtype kv_dtype, mla_plan_mode mode,
                         int32_t num_cus, int32_t* plan, int64_t plan_words);

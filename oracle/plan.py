@@ -67,7 +67,8 @@ Steps:
    workgroups below G have none.
 9. Words (int32): a 20-word header [magic 0x4D4C4150, version 4, R, H,
    q_len_max, kv_dtype, C, mode_used (| 0x100 when the caller asked for the
-   merge inside the decode kernel), M_UNIT, u, N_MAX, MIN_SPLIT_KEYS,
+   merge inside the decode kernel, | 0x200 when it asked for fp8 PV
+   products), M_UNIT, u, N_MAX, MIN_SPLIT_KEYS,
    ITEM_OVERHEAD, OCC, S, W, G, P, 20, total words], then split_indptr[R+1],
    split_row[S], split_begin[S], split_end[S], split_part[S],
    work_indptr[G+1], item_split[W], item_m[W].
@@ -88,6 +89,9 @@ MODE_AUTO, MODE_UNIFORM, MODE_LENGTH_AWARE = 0, 1, 2
 # Bit 8 of the mode: the caller asks for the split merge inside the decode
 # kernel. It is recorded in the header's mode word and changes nothing else.
 MERGE_IN_KERNEL = 0x100
+# Bit 9: the caller asks for the PV products in fp8 (fp8 KV only, not with
+# MERGE_IN_KERNEL). Also recorded in the mode word and nothing else.
+FP8_PV = 0x200
 KV_BF16, KV_FP8 = 0, 1
 
 
@@ -166,8 +170,10 @@ def plan_ref(kv_lens, H, q_len_max, kv_dtype, mode, C):
 
     # 1-4
     u = cdiv(H * q_len_max, M_UNIT)
-    flag = mode & MERGE_IN_KERNEL
-    mode_req = mode & ~MERGE_IN_KERNEL
+    flag = mode & (MERGE_IN_KERNEL | FP8_PV)
+    mode_req = mode & ~(MERGE_IN_KERNEL | FP8_PV)
+    if (flag & FP8_PV) and (kv_dtype != KV_FP8 or (flag & MERGE_IN_KERNEL)):
+        raise ValueError("fp8 PV needs fp8 KV and a separate merge")
     if mode_req != MODE_LENGTH_AWARE:
         uni = uniform_splits(lens, u, C)
     if mode_req != MODE_UNIFORM:

@@ -130,6 +130,7 @@ def workspace_size(plan_words: np.ndarray) -> int:
 
 
 PLAN_MERGE_IN_KERNEL = 0x100
+PLAN_FP8_PV = 0x200   # fp8 PV products (fp8 KV; not with PLAN_MERGE_IN_KERNEL)
 
 
 def workspace_init(plan_words: np.ndarray, workspace, stream=None):

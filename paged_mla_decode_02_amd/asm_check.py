@@ -136,29 +136,42 @@ def _kernel_bodies(asm: str):
 
 
 def check_scratch_in_step_loops(asm: str):
-    """Return the scratch (spill) accesses that sit inside a loop whose body
-    holds MFMA instructions and no nested loop: the per-tile step loops of the
+    """Return the scratch (spill) accesses that sit inside an innermost loop
+    whose body holds MFMA instructions: the per-tile step loops of the
     decode kernel. A spill reload there is a vector-memory access whose wait
-    would also wait for the tile loads in flight."""
+    would also wait for the tile loads in flight. Loops come from the
+    compiler's own loop comments on each basic block ("=>This Inner Loop
+    Header", "in Loop: Header=..."), so code after a loop that the layout
+    reaches by a backward branch is not taken for a loop body. A kernel with
+    backward branches but no loop comments is reported as such."""
     bad = []
     for name, body in _kernel_bodies(asm):
         code = [l.split(";", 1)[0].strip() for l in body]
-        labels = {}
-        for i, l in enumerate(code):
-            m = re.match(r"^(\.LBB\w+):", l)
+        loop_of, inner, cur, annotated = [], set(), None, False
+        for i, l in enumerate(body):
+            m = re.match(r"^(\.LBB\w+|; %bb\.\d+):(.*)$", l)
             if m:
-                labels[m.group(1)] = i
-        loops = []
-        for i, l in enumerate(code):
-            m = re.match(r"^s_(?:cbranch_\w+|branch)\s+(\.LBB\w+)", l)
-            if m and m.group(1) in labels and labels[m.group(1)] < i:
-                loops.append((labels[m.group(1)], i))
-        for lo, hi in loops:
-            if any(lo < a <= b < hi and (a, b) != (lo, hi) for a, b in loops):
-                continue   # not innermost
-            if not any(code[k].startswith("v_mfma") for k in range(lo, hi + 1)):
-                continue
-            for k in range(lo, hi + 1):
-                if code[k].startswith("scratch_"):
-                    bad.append(f"{name}: {k}: {code[k]}")
+                label, comment = m.group(1), m.group(2)
+                after = body[i + 1] if i + 1 < len(body) else ""
+                after = after if re.match(r"^\s*;", after) else ""
+                note = comment + " " + after
+                header = label[2:] if label.startswith(".L") else None
+                if re.search(r"=>\s*This Inner Loop Header", note):
+                    cur, annotated = header, True
+                    inner.add(header)
+                elif re.search(r"=>\s*This Loop Header", note):
+                    cur, annotated = header, True
+                else:
+                    h = re.search(r"in Loop: Header=(BB\w+)", note)
+                    cur = h.group(1) if h else None
+            loop_of.append(cur)
+        labels = {c[:-1] for c in code if re.match(r"^\.LBB\w+:$", c)}
+        backward = any(re.match(r"^s_(?:cbranch_\w+|branch)\s+(\.LBB\w+)", c) for c in code) and labels
+        if backward and not annotated and any(c.startswith("v_mfma") for c in code):
+            bad.append(f"{name}: no loop comments in the assembly; cannot place the spills")
+            continue
+        mfma_loops = {loop_of[i] for i, c in enumerate(code) if c.startswith("v_mfma") and loop_of[i] in inner}
+        for i, c in enumerate(code):
+            if c.startswith("scratch_") and loop_of[i] in mfma_loops:
+                bad.append(f"{name}: {i}: {c}")
     return bad

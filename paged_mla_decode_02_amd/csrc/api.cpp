@@ -124,7 +124,7 @@ int32_t mla::decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale,
     e = launch_zero((uint32_t*)a.counters, rows * v.u, s);
     if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("counter clear launch: ") + hipGetErrorString(e));
   }
-  e = launch_decode(a, q_dtype == MLA_FP8_E4M3, kv_dtype == MLA_FP8_E4M3, v.G, s);
+  e = launch_decode(a, q_dtype == MLA_FP8_E4M3, kv_dtype == MLA_FP8_E4M3, v.pv_fp8, v.G, s);
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
   if (v.P > 0 && v.max_splits > a.inkernel_max_splits) {
     MergeArgs mg;

@@ -122,15 +122,36 @@ static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
 static_assert(kRows == 128, "the plan's M unit");
 static_assert(kRows * kDV * 2 <= kTilesEnd, "epilogue staging of the item's 128 bf16 rows");
 
+// fp8 PV (fp8 KV only): tiles t-2 and t-1 stay in LDS until the step that
+// multiplies both, so the main tiles take a longer ring; P^T goes through LDS
+// in fp8, [2 tile parities][4 row blocks][64 lanes] x 16 bytes, followed by
+// the per-(row, tile) power-of-two scales, [2 parities][32 rows] x 4 bytes
+// (byte rb for row block rb).
+// With split bf16 queries the hi and lo operands of the last kQLds QK
+// products (dims 448..575) wait in LDS after the tiles, [4 waves][2 kQLds
+// links][64 lanes] x 32 bytes, instead of in 32 registers; 6 main tiles
+// suffice (t-2 .. t+2 are in use during step t).
+constexpr int kMainBufs8 = 6;
+constexpr int kQLds = 1;
+constexpr int kOffQ8 = kMainBufs8 * kF8MainBytes + kRopeBufs * kF8RopeBytes;
+static_assert(kOffQ8 + kWaves * 2 * kQLds * 64 * 32 <= kTilesEnd, "fp8-PV tiles and the staged queries");
+constexpr int kP8Bytes = kRowBlocks * 64 * 16;                  // 4096 per tile
+constexpr int kOffP8Scale = kOffP + 2 * kP8Bytes;
+static_assert(kOffP8Scale + 2 * 32 * 4 <= kOffL, "fp8 P^T and its scales fit the P^T region");
+
 // LDS offsets of tile t's buffers.
-template <bool KV_FP8> struct Layout;
-template <> struct Layout<false> {
+template <bool KV_FP8, bool PV8 = false> struct Layout;
+template <> struct Layout<false, false> {
   static __device__ __forceinline__ int main(int t) { return (t & 3) * kMainBytes; }
   static __device__ __forceinline__ int rope(int t) { return kMainBufs * kMainBytes + (t % 3) * kRopeBytes; }
 };
-template <> struct Layout<true> {
+template <> struct Layout<true, false> {
   static __device__ __forceinline__ int main(int t) { return (t & 3) * kF8MainBytes; }
   static __device__ __forceinline__ int rope(int t) { return kMainBufs * kF8MainBytes + (t % 3) * kF8RopeBytes; }
+};
+template <> struct Layout<true, true> {
+  static __device__ __forceinline__ int main(int t) { return (t % kMainBufs8) * kF8MainBytes; }
+  static __device__ __forceinline__ int rope(int t) { return kMainBufs8 * kF8MainBytes + (t % 3) * kF8RopeBytes; }
 };
 __device__ __forceinline__ int p_buf(int t) { return kOffP + (t & 1) * kPBytes; }
 
@@ -507,9 +528,15 @@ __device__ __forceinline__ bf16x8 p_frag(const lds_u8* smem, const LaneAddr& la,
 struct Softmax {
   float tmax, mu;
   bf16x8 pf[2];
+  // fp8 PV: P 2^k of the lane's 16 keys as e4m3 (byte 4 g + e: key
+  // 8 g + 4 h + e), 2^-k, and the E8M0 code 127 - k of 2^-k.
+  u32x4 pf8;
+  float lscale;
+  int sbyte;
 };
 struct RowState {
   float m_ref, m_seen, l_part;
+  float l_round;   // fp8 PV: the sum of the rounded weights (O's denominator)
   bool over;
 };
 // piece 0..3: scale and mask 4 scores, running max; piece 4: row max, the
@@ -518,7 +545,13 @@ struct RowState {
 // the mask and folds the scale into the exponent: the max of the raw scores
 // times the scale is the max of the scaled scores, and exp2(s c - mu) is one
 // fma.
-template <bool FAST>
+// PV8 (P for the fp8 PV products): the exponentials come out as P 2^k, k a
+// per-(row, tile) integer that puts the tile's largest P 2^k in (128, 256],
+// inside e4m3's range (largest finite 448) with its full 4 significant bits;
+// the PV product multiplies by the E8M0 scale 2^-k again, exactly, and the
+// row sum adds the same rounded weights times 2^-k. Weights below 2^-17 of
+// the tile's largest fall under e4m3's smallest subnormal and are dropped.
+template <bool FAST, bool PV8 = false>
 __device__ __forceinline__ void softmax_piece(int piece, Softmax& sm, f32x16& s, float score_c, int lim,
                                               RowState& rs) {
   if (piece < 4) {
@@ -541,15 +574,47 @@ __device__ __forceinline__ void softmax_piece(int piece, Softmax& sm, f32x16& s,
     if (rs.m_ref == -INFINITY) rs.m_ref = tmax;
     rs.over = rs.over || (tmax > rs.m_ref + kRefSlack);
     sm.mu = rs.m_ref == -INFINITY ? 0.0f : rs.m_ref;
+    if constexpr (PV8) {
+      // k = 8 - ceil(tmax - mu), kept in [-126, 126] (2^-k and 127 - k stay
+      // normal floats and valid E8M0 codes; a tile past the clamp is either
+      // entirely below 2^-118 of the reference or one that makes the item
+      // run again). A row with no visible key in the tile takes k = 0.
+      const float kf = tmax == -INFINITY ? 0.f : fminf(126.f, fmaxf(-126.f, 8.f - __builtin_ceilf(tmax - sm.mu)));
+      const int k = (int)kf;
+      sm.mu -= kf;
+      sm.sbyte = 127 - k;
+      sm.lscale = __int_as_float((127 - k) << 23);
+    }
   } else if (piece < 13) {
+    float pr2[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int r = 2 * (piece - 5) + e;
       // v_exp_f32 directly: arguments below -126 give 0 or a denormal, which
       // only drops weights under 2^-126 of the row's reference.
       const float pr = __builtin_amdgcn_exp2f(FAST ? __builtin_fmaf(s[r], score_c, -sm.mu) : s[r] - sm.mu);
-      rs.l_part += pr;
-      sm.pf[r >> 3][r & 7] = (__bf16)pr;
+      if constexpr (PV8) {
+        pr2[e] = pr;
+        rs.l_part = __builtin_fmaf(pr, sm.lscale, rs.l_part);
+      } else {
+        rs.l_part += pr;
+        sm.pf[r >> 3][r & 7] = (__bf16)pr;
+      }
+    }
+    if constexpr (PV8) {   // keys r, r + 1 (r = 2 (piece - 5)): half (piece - 5) & 1 of dword r / 4
+      const int dw = (piece - 5) >> 1;
+      if ((piece - 5) & 1) {
+        sm.pf8[dw] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pr2[0], pr2[1], (int)sm.pf8[dw], true);
+        // O is normalized by the sum of the rounded weights, so that it is a
+        // weighted mean of V with exactly the weights the PV products use (a
+        // dominant key's rounding then cancels between O's numerator and
+        // denominator); the LSE keeps the exact sum.
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)sm.pf8[dw], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)sm.pf8[dw], true);
+        rs.l_round = __builtin_fmaf((lo[0] + lo[1]) + (hi[0] + hi[1]), sm.lscale, rs.l_round);
+      } else {
+        sm.pf8[dw] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pr2[0], pr2[1], (int)sm.pf8[dw], false);
+      }
     }
   }
 }
@@ -627,6 +692,53 @@ __device__ __forceinline__ void pv_product(const lds_u8* smem, const LaneAddr& l
   if (kk == 0 && ct == 3) pb[rb] = p_frag(smem, la, pbuf, rb, 1);
 }
 
+// fp8 PV: one v_mfma_scale_f32_32x32x64_f8f6f4 covers 64 keys, the 32 of
+// tile tA (even) and the 32 of tile tA + 1. The matrix core reads its 64 k
+// positions as two blocks of 32, block b made of bytes 16 b .. 16 b + 15 of
+// both lane halves and scaled by the E8M0 code of lane half b (checked
+// against a host model of the instruction). So lane (row j, half h) of the
+// B operand (P^T) holds its own 16 P^T values of tile tA in bytes 0..15 and
+// those of tile tA + 1 in bytes 16..31 (byte 4 g + e: key 8 g + 4 h + e, the
+// order of its S^T registers), and lane half b brings the scale of tile
+// tA + b of row j; the A operand (V^T) takes the same keys with the same
+// transposed reads as the bf16 PV products, from the two tiles. Every
+// product's key positions match between A and B, and each block's P values
+// share one scale, so O^T += V^T P^T exactly up to the fp8 rounding of P.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ u32x8 v_frag8(const lds_u8* smem, const LaneAddr& la, int vA, int vB, int ct) {
+  const u32x2 a0 = v_raw_f8(smem, la, vA, 0, ct), a1 = v_raw_f8(smem, la, vA, 1, ct);
+  const u32x2 b0 = v_raw_f8(smem, la, vB, 0, ct), b1 = v_raw_f8(smem, la, vB, 1, ct);
+  return u32x8{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+}
+template <int RB>
+__device__ __forceinline__ void mfma_pv8(f32x16& acc, const u32x8& v, const u32x8& p, uint32_t scale) {
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, v), __builtin_bit_cast(i32x8, p),
+                                                       acc, 0, 0, 0, 0x7F7F7F7F, RB, (int)scale);
+}
+
+// Staged query operand j (link NQ - 2 kQLds + j) of this lane's row.
+__device__ __forceinline__ int q_staged_off(const LaneAddr& la, int j) {
+  return kOffQ8 + (la.w * 2 * kQLds + j) * 2048 + la.pl * 2;
+}
+__device__ __forceinline__ u32x8 q_staged(const lds_u8* smem, const LaneAddr& la, int j) {
+  return cat8(lds_load<u32x4>(smem, q_staged_off(la, j)), lds_load<u32x4>(smem, q_staged_off(la, j) + 16));
+}
+
+// Publish P^T(t-1) of this wave's rows: bf16, or (PV8) fp8 at parity par
+// with the row's scale code in byte w of its scale word (both lane halves
+// of a row hold the same code and write the same byte).
+template <bool PV8>
+__device__ __forceinline__ void publish_p(lds_u8* smem, const LaneAddr& la, int pbuf, int par, int lane,
+                                          const Softmax& sm) {
+  if constexpr (PV8) {
+    lds_store(smem, kOffP + par * kP8Bytes + la.w * 1024 + la.pl, sm.pf8);
+    lds_store(smem, kOffP8Scale + par * 128 + (lane & 31) * 4 + la.w, (uint8_t)sm.sbyte);
+  } else {
+    lds_store(smem, pbuf + (la.w * 2 + 0) * 1024 + la.pl, sm.pf[0]);
+    lds_store(smem, pbuf + (la.w * 2 + 1) * 1024 + la.pl, sm.pf[1]);
+  }
+}
+
 // One pipeline step t, in two phases split by a barrier.
 //   Phase A: QK(t) (if QK) from the K tile in (kmain, krope); the softmax
 //     of tile t-1 (if PREV; scores in s_old, masked by lim_old)
@@ -648,11 +760,19 @@ constexpr int kDmaStride = 3;
 // operands with fp8 KV (18 products, every second slot: hi then lo of each
 // 64 dims). fp8 K is read kK8Depth products ahead; the softmax pieces keep
 // their slots.
-template <bool QK, bool PREV, int NDMA, bool KV_FP8, bool FAST, int QKM, typename QF, int NQ, typename Dma>
+// PV8 (fp8 PV, fp8 KV): the softmax publishes P^T(t-1) in fp8 at parity
+// par = (t-1) & 1 of the fp8 P^T buffers, and phase B multiplies only when
+// pv_now: tiles tA = vmain and tA + 1 = vmain2 once both have their P^T, or
+// tile tA alone (single: the item's last tile has an even index), whose
+// second half of each product then gets zero P^T and scale 1.
+template <bool QK, bool PREV, int NDMA, bool KV_FP8, bool FAST, int QKM, bool PV8 = false, typename QF, int NQ,
+          typename Dma>
 __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, const QF (&qf)[NQ],
                                               int kmain, int krope, f32x16& s_old, float score_c,
                                               int lim_old, RowState& rs, int pbuf, int vmain,
-                                              f32x16 (&oacc)[kRowBlocks][kColTiles], Dma&& dma) {
+                                              f32x16 (&oacc)[kRowBlocks][kColTiles], Dma&& dma,
+                                              int vmain2 = 0, int par = 0, bool pv_now = false,
+                                              bool single = false, int lane = 0) {
   static_assert(kSmStride * kSoftmaxPieces <= kKSteps, "softmax pieces fit between the QK products");
   static_assert(NDMA == 0 || kDmaStride * (NDMA - 1) < 32, "loads fit between the PV products");
   // bf16 K: fragments read kKDepth products ahead; fp8 K: kK8Depth.
@@ -662,6 +782,8 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
                 "Q fragments of the QK mode");
   bf16x8 kb[kKDepth];
   u32x8 k8[kK8Depth];
+  constexpr bool kQStaged = PV8 && QKM == 2;
+  u32x8 qr[3];
   Softmax sm;
   f32x16 s_cur;
   if constexpr (QK) {
@@ -684,9 +806,15 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
         const u32x8 a = k8[p % kK8Depth];
         if (n % QKM == QKM - 1 && p + kK8Depth < kKSteps8)
           k8[p % kK8Depth] = k_prod_f8(smem, la, kmain, krope, p + kK8Depth);
-        if (n == 0) mfma8_qk_first(s_cur, a, qf[n]);
-        else if (n + 1 < NQ) mfma8_qk(s_cur, a, qf[n]);
-        else mfma8_qk_last(s_old, s_cur, a, qf[n]);   // s_old is dead: the softmax ended
+        // The staged query operands (links NQ - 2 kQLds ..), read two links ahead.
+        constexpr int kL0 = NQ - 2 * kQLds;
+        if constexpr (kQStaged) {
+          if (n + 2 >= kL0 && n + 2 < NQ) qr[(n + 2) % 3] = q_staged(smem, la, n + 2 - kL0);
+        }
+        const u32x8 b = (kQStaged && n >= kL0) ? qr[n % 3] : qf[n];
+        if (n == 0) mfma8_qk_first(s_cur, a, b);
+        else if (n + 1 < NQ) mfma8_qk(s_cur, a, b);
+        else mfma8_qk_last(s_old, s_cur, a, b);   // s_old is dead: the softmax ended
       }
     } else if constexpr (QK) {
       const bf16x8 a = kb[s % kKDepth];
@@ -697,22 +825,52 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
     }
     if constexpr (PREV) {
       if (s % kSmStride == 0 && s / kSmStride < kSoftmaxPieces)
-        softmax_piece<FAST>(s / kSmStride, sm, s_old, score_c, lim_old, rs);
-      if (s == kSmStride * kSoftmaxPieces) {   // publish P^T(t-1) of this wave's rows
-        lds_store(smem, pbuf + (la.w * 2 + 0) * 1024 + la.pl, sm.pf[0]);
-        lds_store(smem, pbuf + (la.w * 2 + 1) * 1024 + la.pl, sm.pf[1]);
-      }
+        softmax_piece<FAST, PV8>(s / kSmStride, sm, s_old, score_c, lim_old, rs);
+      if (s == kSmStride * kSoftmaxPieces) publish_p<PV8>(smem, la, pbuf, par, lane, sm);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (PREV) {
-    if constexpr (!QK) {   // the last step: the slot loop ended with the last piece
-      lds_store(smem, pbuf + (la.w * 2 + 0) * 1024 + la.pl, sm.pf[0]);
-      lds_store(smem, pbuf + (la.w * 2 + 1) * 1024 + la.pl, sm.pf[1]);
-    }
+    if constexpr (!QK) publish_p<PV8>(smem, la, pbuf, par, lane, sm);   // the slot loop ended with the last piece
   }
   if constexpr (PREV) __syncthreads();   // P^T(t-1) of all rows is visible
   // Phase B.
+  if constexpr (PV8) {
+    if (PREV && pv_now) {   // uniform
+      // Two halves of two row blocks each (P^T of two row blocks, 16
+      // registers, at a time); the V^T fragments are read once per half.
+      uint32_t sc = lds_load<uint32_t>(smem, kOffP8Scale + (lane >> 5) * 128 + (lane & 31) * 4);
+      if (!QK && single) sc = lane >= 32 ? 0x7F7F7F7Fu : sc;   // tile tA + 1 does not exist
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x8 pb8[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          pb8[r] = cat8(lds_load<u32x4>(smem, kOffP + (2 * hh + r) * 1024 + la.pl),
+                        lds_load<u32x4>(smem, kOffP + kP8Bytes + (2 * hh + r) * 1024 + la.pl));
+          if (!QK && single) pb8[r][4] = pb8[r][5] = pb8[r][6] = pb8[r][7] = 0u;   // its half of each product is zero
+        }
+        u32x8 va[2];
+        va[0] = v_frag8(smem, la, vmain, vmain2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < 2 * kColTiles; ++p) {
+          const int ct = p >> 1, r = p & 1, q = 8 * hh + p;
+          if (r == 0 && ct + 1 < kColTiles) va[(ct + 1) & 1] = v_frag8(smem, la, vmain, vmain2, ct + 1);
+          if (q % kDmaStride == 0 && q / kDmaStride < NDMA) dma(q / kDmaStride);
+          if (hh == 0 && r == 0) mfma_pv8<0>(oacc[0][ct], va[ct & 1], pb8[0], sc);
+          else if (hh == 0) mfma_pv8<1>(oacc[1][ct], va[ct & 1], pb8[1], sc);
+          else if (r == 0) mfma_pv8<2>(oacc[2][ct], va[ct & 1], pb8[0], sc);
+          else mfma_pv8<3>(oacc[3][ct], va[ct & 1], pb8[1], sc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) dma(i);
+    }
+    return;
+  }
   bf16x8 pb[kRowBlocks];
   bf16x8 vb[2];
   u32x2 vraw;
@@ -733,11 +891,13 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
 
 // MERGE: the variant for in-kernel-merge plans (the default variant carries
 // none of that code, which would cost the hot loops registers).
-template <bool Q_FP8, bool KV_FP8, bool MERGE>
+// PV8: the fp8 PV products (fp8 KV only).
+template <bool Q_FP8, bool KV_FP8, bool MERGE, bool PV8>
 __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a) {
+  static_assert(KV_FP8 || !PV8, "fp8 PV needs fp8 KV");
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmemBytes];
   lds_u8* smem = (lds_u8*)smem_raw;
-  using LY = Layout<KV_FP8>;
+  using LY = Layout<KV_FP8, PV8>;
   using Dma = TileDma<KV_FP8>;
   constexpr int QKM = !KV_FP8 ? 0 : Q_FP8 ? 1 : 2;   // QK products: bf16, fp8, split bf16 Q
 
@@ -848,10 +1008,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     // Pass 0 fixes each row's reference at its first visible tile's max. In
     // the rare case that a later tile exceeds it by more than kRefSlack, the
     // item runs once more with every row's reference at its true max.
-    RowState rs{-INFINITY, -INFINITY, 0.f, false};
+    RowState rs{-INFINITY, -INFINITY, 0.f, 0.f, false};
     f32x16 oacc[kRowBlocks][kColTiles];
     for (int pass = 0; pass < 2; ++pass) {
       rs.l_part = 0.f;
+      rs.l_round = 0.f;
       rs.over = false;
 #pragma unroll
       for (int rb = 0; rb < kRowBlocks; ++rb)
@@ -875,10 +1036,21 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         for (int t = 0; t < 2; ++t) {
           issue_slots(a.kv_indices, kv0, begin, end, t + 2, smem, w, ilane);
           if (t < ntiles)
-            Dma::all(kv, read_slots(smem, t, w, ilane), a.max_slot, smem, dma_main<KV_FP8>(t), dma_rope<KV_FP8>(t), w, ilane);
+            Dma::all(kv, read_slots(smem, t, w, ilane), a.max_slot, smem, LY::main(t), LY::rope(t), w, ilane);
         }
         if constexpr (QKM == 2) {
-          if (pass == 0) score_row = score_c * split_q_rows(qf);
+          if (pass == 0) {
+            score_row = score_c * split_q_rows(qf);
+            if constexpr (PV8) {   // the last products' operands wait in LDS (read back by this lane only)
+              const LaneAddr la_q = lane_addr<KV_FP8>(ilane, w);
+#pragma unroll
+              for (int j = 0; j < 2 * kQLds; ++j) {
+                const u32x8 v = qf[2 * (kKSteps8 - kQLds) + j];
+                lds_store(smem, q_staged_off(la_q, j), u32x4{v[0], v[1], v[2], v[3]});
+                lds_store(smem, q_staged_off(la_q, j) + 16, u32x4{v[4], v[5], v[6], v[7]});
+              }
+            }
+          }
         }
         if (ntiles > 1) wait_vm<1 + Dma::n>();
         else wait_vm<1>();
@@ -898,15 +1070,30 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
           const int dlane = opaque(lane);
           issue_slots(a.kv_indices, kv0, begin, end, t + 4, smem, w, dlane);
           const TileSrc<KV_FP8> src = Dma::src(kv, DO_DMA ? read_slots(smem, t + 2, w, dlane) : 0, a.max_slot, w, dlane);
-          const int dm = dma_main<KV_FP8>(t + 2), dr = dma_rope<KV_FP8>(t + 2);
+          const int dm = LY::main(t + 2), dr = LY::rope(t + 2);
           auto dma = [&](int i) {
             Dma::op(i, kv, src, lds_addr_of(smem), dm, dr, w, dlane);
           };
           const int lim_old = key_last - (begin + (t - 1) * kNT + 4 * (dlane >> 5));
           const LaneAddr la_s = lane_addr<KV_FP8>(dlane, w);
-          pipeline_step<DO_QK, PREV, DO_DMA ? Dma::n : 0, KV_FP8, FAST, QKM>(
-              smem, la_s, qf, LY::main(t), LY::rope(t), s_old, score_row, lim_old, rs, p_buf(t + 1),
-              LY::main(t + 11), oacc, dma);
+          if constexpr (PV8) {
+            // PV of tiles tA = (t - 1) & ~1 and tA + 1 once both have their
+            // P^T (t even), or of tA alone in the last step when it is the
+            // item's last tile.
+            // (the step without QK is the last one, t = ntiles). Alone, tile
+            // tA also stands in for the second tile's V^T: whatever another
+            // buffer holds (an older tile, or LDS never written, possibly NaN
+            // codes) must not meet the zero P^T, since 0 x NaN is NaN.
+            const int tA = (t - 1) & ~1;
+            const bool single = !DO_QK && (t & 1) != 0;
+            pipeline_step<DO_QK, PREV, DO_DMA ? Dma::n : 0, KV_FP8, FAST, QKM, true>(
+                smem, la_s, qf, LY::main(t), LY::rope(t), s_old, score_row, lim_old, rs, 0, LY::main(tA), oacc,
+                dma, LY::main(single ? tA : tA + 1), (t - 1) & 1, !DO_QK || (t & 1) == 0, single, dlane);
+          } else {
+            pipeline_step<DO_QK, PREV, DO_DMA ? Dma::n : 0, KV_FP8, FAST, QKM>(
+                smem, la_s, qf, LY::main(t), LY::rope(t), s_old, score_row, lim_old, rs, p_buf(t + 1),
+                LY::main(t + 11), oacc, dma);
+          }
           if (DO_DMA) wait_vm<1 + Dma::n>();
           else wait_vm<1>();
           __syncthreads();   // tile t+1 landed; tile t-1 and P(t-1) are free
@@ -941,7 +1128,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
 
     // Epilogue: the rows' sums and LSE, then O normalized and written.
     const float l_row = half_sum(rs.l_part);
-    if (lane < 32) lds_store(smem, kOffL + (w * 32 + lane) * 4, l_row);
+    // (cross-lane sums run on every lane, outside the lane < 32 branch)
+    const float l_o = PV8 ? half_sum(rs.l_round) : l_row;   // O's denominator
+    if (lane < 32) lds_store(smem, kOffL + (w * 32 + lane) * 4, l_o);
     if (row_ok && lane < 32) {
       const float lse = l_row > 0.f ? (rs.m_ref + __log2f(l_row)) * kLn2 : -INFINITY;
       // row mr of the block is (token tok, head): index (q0 + tok) H + head
@@ -1075,17 +1264,25 @@ __global__ __launch_bounds__(kDecodeThreads) void gather_kernel(GatherArgs a) {
 
 }  // namespace
 
+// (fp8 PV plans never merge inside the decode kernel: the planner refuses
+// that combination.)
 template <bool MERGE>
-const void* decode_fn(bool q_fp8, bool kv_fp8) {
-  if (!q_fp8 && !kv_fp8) return (const void*)decode_kernel<false, false, MERGE>;
-  if (!q_fp8 && kv_fp8) return (const void*)decode_kernel<false, true, MERGE>;
-  if (q_fp8 && !kv_fp8) return (const void*)decode_kernel<true, false, MERGE>;
-  return (const void*)decode_kernel<true, true, MERGE>;
+const void* decode_fn(bool q_fp8, bool kv_fp8, bool pv_fp8) {
+  if (kv_fp8 && pv_fp8) {
+    if constexpr (MERGE) return nullptr;
+    else return q_fp8 ? (const void*)decode_kernel<true, true, false, true> : (const void*)decode_kernel<false, true, false, true>;
+  }
+  if (!q_fp8 && !kv_fp8) return (const void*)decode_kernel<false, false, MERGE, false>;
+  if (!q_fp8 && kv_fp8) return (const void*)decode_kernel<false, true, MERGE, false>;
+  if (q_fp8 && !kv_fp8) return (const void*)decode_kernel<true, false, MERGE, false>;
+  return (const void*)decode_kernel<true, true, MERGE, false>;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, int grid, hipStream_t st) {
+hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, bool pv_fp8, int grid, hipStream_t st) {
   void* args[] = {(void*)&a};
-  const void* fn = a.inkernel_max_splits > 1 ? decode_fn<true>(q_fp8, kv_fp8) : decode_fn<false>(q_fp8, kv_fp8);
+  const void* fn = a.inkernel_max_splits > 1 ? decode_fn<true>(q_fp8, kv_fp8, pv_fp8)
+                                             : decode_fn<false>(q_fp8, kv_fp8, pv_fp8);
+  if (!fn) return hipErrorInvalidValue;
   return hipLaunchKernel(fn, dim3(grid), dim3(kDecodeThreads), args, 0, st);
 }
 

@@ -41,6 +41,7 @@ struct PlanView {
   int32_t rows, heads, q_len_max, kv_dtype, mode, m_unit, u, S, W, G, P, total;
   int32_t max_splits;   // largest split count of a row
   bool merge_in_kernel; // the caller asked for the split merge inside the decode kernel
+  bool pv_fp8;          // the caller asked for fp8 PV products (fp8 KV)
   int64_t off_split_indptr, off_split_row, off_split_begin, off_split_end, off_split_part,
       off_work_indptr, off_item_split, off_item_m;
 };

@@ -46,8 +46,9 @@ int32_t view_plan(const int32_t* plan, PlanView* v) {
   v->heads = plan[H_HEADS];
   v->q_len_max = plan[H_QLEN];
   v->kv_dtype = plan[H_KVDTYPE];
-  v->mode = plan[H_MODE] & ~MLA_PLAN_MERGE_IN_KERNEL;
+  v->mode = plan[H_MODE] & ~(MLA_PLAN_MERGE_IN_KERNEL | MLA_PLAN_FP8_PV);
   v->merge_in_kernel = (plan[H_MODE] & MLA_PLAN_MERGE_IN_KERNEL) != 0;
+  v->pv_fp8 = (plan[H_MODE] & MLA_PLAN_FP8_PV) != 0;
   v->m_unit = plan[H_MUNIT];
   v->u = plan[H_U];
   v->S = plan[H_S];
@@ -56,7 +57,8 @@ int32_t view_plan(const int32_t* plan, PlanView* v) {
   v->P = plan[H_P];
   v->total = plan[H_TOTAL];
   if (v->rows < 1 || v->S < v->rows || v->W != (int64_t)v->S * v->u || v->G < 1 || v->P < 0 ||
-      v->P > v->S || v->m_unit != kMUnit)
+      v->P > v->S || v->m_unit != kMUnit ||
+      (v->pv_fp8 && (v->kv_dtype != MLA_FP8_E4M3 || v->merge_in_kernel)))
     return set_error(MLA_ERR_PLAN_MISMATCH, "plan header is inconsistent");
   int64_t off = kHeaderWords;
   v->off_split_indptr = off; off += v->rows + 1;
@@ -116,10 +118,14 @@ extern "C" int32_t mla_decode_plan(const int32_t* kv_lens, int32_t rows, int32_t
     return set_error(MLA_ERR_UNSUPPORTED, "q_len_max must be in 1..16");
   if (kv_dtype != MLA_BF16 && kv_dtype != MLA_FP8_E4M3)
     return set_error(MLA_ERR_INVALID_ARG, "unknown kv_dtype");
-  const int32_t flag = (int32_t)mode & MLA_PLAN_MERGE_IN_KERNEL;
-  const int32_t base_mode = (int32_t)mode & ~MLA_PLAN_MERGE_IN_KERNEL;
+  const int32_t flag = (int32_t)mode & (MLA_PLAN_MERGE_IN_KERNEL | MLA_PLAN_FP8_PV);
+  const int32_t base_mode = (int32_t)mode & ~(MLA_PLAN_MERGE_IN_KERNEL | MLA_PLAN_FP8_PV);
   if (base_mode != MLA_PLAN_AUTO && base_mode != MLA_PLAN_UNIFORM && base_mode != MLA_PLAN_LENGTH_AWARE)
     return set_error(MLA_ERR_INVALID_ARG, "unknown plan mode");
+  if ((flag & MLA_PLAN_FP8_PV) && kv_dtype != MLA_FP8_E4M3)
+    return set_error(MLA_ERR_UNSUPPORTED, "MLA_PLAN_FP8_PV needs fp8 KV");
+  if ((flag & MLA_PLAN_FP8_PV) && (flag & MLA_PLAN_MERGE_IN_KERNEL))
+    return set_error(MLA_ERR_UNSUPPORTED, "MLA_PLAN_FP8_PV does not combine with MLA_PLAN_MERGE_IN_KERNEL");
   if (num_cus < 1) return set_error(MLA_ERR_INVALID_ARG, "num_cus must be >= 1");
 
   int64_t sum_len = 0, max_len = 0;

@@ -124,6 +124,10 @@ def test_plan_argument_errors(lib):
     assert plan(q=0) == UNSUPPORTED and plan(q=17) == UNSUPPORTED
     assert plan(rows=0) == UNSUPPORTED
     assert plan(kv=3) == INVALID and plan(mode=5) == INVALID and plan(C=0) == INVALID
+    # fp8 PV products: fp8 KV only, and not with the in-kernel merge
+    assert plan(kv=1, mode=0x200) == OK and int(out[7]) == 0x200 | 1
+    assert plan(kv=0, mode=0x200) == UNSUPPORTED
+    assert plan(kv=1, mode=0x300) == UNSUPPORTED
     assert plan(lens=np.array([5, -1], np.int32)) == INVALID
     assert plan(n=10) == INVALID
     n = ctypes.c_int64(0)

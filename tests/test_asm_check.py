@@ -82,14 +82,31 @@ def kernel(body):
 
 
 def test_scratch_in_step_loop_is_flagged():
-    step = [".LBB0_1:", f"\t{BF} v[0:15], v[16:19], v[20:23], v[0:15]", "\tds_read_b128 v[16:19], v30",
+    # the compiler's loop comments: an item loop BB0_0 around a step loop BB0_1
+    step = [".LBB0_1:                ;   Parent Loop BB0_0 Depth=1",
+            "                        ; =>  This Inner Loop Header: Depth=2",
+            f"\t{BF} v[0:15], v[16:19], v[20:23], v[0:15]", "\tds_read_b128 v[16:19], v30",
             "\ts_cbranch_scc1 .LBB0_1"]
-    assert check_scratch_in_step_loops("\n".join(kernel(step))) == []
-    bad = step[:2] + ["\tscratch_load_dword v40, off, off offset:16"] + step[2:]
-    assert len(check_scratch_in_step_loops("\n".join(kernel(bad)))) == 1
+    head = [".LBB0_0:                ; =>This Loop Header: Depth=1"]
+    tail = ["; %bb.2:                ;   in Loop: Header=BB0_0 Depth=1", "\ts_cbranch_scc0 .LBB0_0"]
+    assert check_scratch_in_step_loops("\n".join(kernel(head + step + tail))) == []
+    bad = step[:3] + ["\tscratch_load_dword v40, off, off offset:16"] + step[3:]
+    assert len(check_scratch_in_step_loops("\n".join(kernel(head + bad + tail)))) == 1
     # a reload in the enclosing item loop, outside the step loop, is allowed
-    outer = [".LBB0_0:", "\tscratch_load_dword v40, off, off offset:16"] + step + ["\ts_cbranch_scc0 .LBB0_0"]
+    outer = head + ["\tscratch_load_dword v40, off, off offset:16"] + step + tail
     assert check_scratch_in_step_loops("\n".join(kernel(outer))) == []
+    # so is one in item-loop code that the layout places before the step loop
+    # and reaches from its exit by a backward branch (no loop of its own)
+    late = head + ["\ts_branch .LBB0_1",
+                   ".LBB0_3:                ;   in Loop: Header=BB0_0 Depth=1",
+                   f"\t{BF} v[0:15], v[16:19], v[20:23], v[0:15]",
+                   "\tscratch_load_dword v40, off, off offset:16", "\ts_cbranch_scc0 .LBB0_0"] + \
+        step[:4] + ["\ts_cbranch_scc1 .LBB0_1", "; %bb.4:                ;   in Loop: Header=BB0_0 Depth=1",
+                    "\ts_branch .LBB0_3"]
+    assert check_scratch_in_step_loops("\n".join(kernel(late))) == []
+    # without loop comments the placement cannot be checked
+    plain = [".LBB0_1:", f"\t{BF} v[0:15], v[16:19], v[20:23], v[0:15]", "\ts_cbranch_scc1 .LBB0_1"]
+    assert len(check_scratch_in_step_loops("\n".join(kernel(plain)))) == 1
 
 
 def test_built_kernel_passes_the_checks():

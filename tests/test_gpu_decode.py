@@ -72,6 +72,12 @@ WORKLOADS = ["tiny_causal", "verify_causal", "verify_causal_fp8kv", "draft_nonca
              "ragged_persistent_causal", "ragged_persistent_noncausal", "sparse_topk"]
 PLAN_MODES = {"auto": 0, "uniform": 1, "length_aware": 2, "uniform_merge": 1 | 0x100,
               "length_aware_merge": 2 | 0x100}
+# fp8 PV products (fp8-KV workloads only)
+FP8_PV_MODES = {"auto_fp8pv": 0x200, "uniform_fp8pv": 1 | 0x200, "length_aware_fp8pv": 2 | 0x200}
+FP8_KV_WORKLOADS = ["verify_causal_fp8kv", "draft_noncausal", "longctx_split", "ragged_persistent_causal",
+                    "ragged_persistent_noncausal", "sparse_topk"]
+WORKLOAD_PLANS = [(n, p) for n in WORKLOADS for p in PLAN_MODES] + \
+                 [(n, p) for n in FP8_KV_WORKLOADS for p in FP8_PV_MODES]
 
 _WORKLOAD_CACHE = {}
 
@@ -86,12 +92,11 @@ def workload_and_reference(name):
     return _WORKLOAD_CACHE[name]
 
 
-@pytest.mark.parametrize("plan", list(PLAN_MODES))
-@pytest.mark.parametrize("name", WORKLOADS)
+@pytest.mark.parametrize("name,plan", WORKLOAD_PLANS)
 def test_workload_parity(lib, name, plan):
     print(f"workload {name} plan {plan}", flush=True)
     case, ref = workload_and_reference(name)
-    O, LSE, words = run_gpu(case, mode=PLAN_MODES[plan])
+    O, LSE, words = run_gpu(case, mode={**PLAN_MODES, **FP8_PV_MODES}[plan])
     info = unpack_plan(words)
     ratio, lse_err = assert_parity(case, O, LSE, ref=ref)
     assert len(ref) == case.rows                      # every row was compared
@@ -119,6 +124,16 @@ SMALL = [
     (7, 9, BF16, FP8, True, [1, 0, 9], 1, 2),                        # heads not a multiple of 16
     (16, 1, BF16, BF16, True, [40000], 1, 256),                      # uniform, 157 splits in one row
     (16, 1, BF16, FP8, False, [60000, 100], 2, 256),                 # lanes: about 250 splits in one row
+]
+
+
+# The fp8-KV cases again with fp8 PV products: items of one tile, odd and even
+# tile counts (the last PV product covers one or two tiles), empty rows and
+# splits, q_len above L, heads not a multiple of 16.
+SMALL += [(H, q, qd, kd, c, lens, mode | 0x200, C) for (H, q, qd, kd, c, lens, mode, C) in SMALL if kd == FP8]
+SMALL += [
+    (16, 1, BF16, FP8, True, [1, 31, 32, 33, 63, 64, 65, 95, 96, 97], 1 | 0x200, 1),   # 1..4 tiles, unsplit
+    (128, 4, FP8, FP8, False, [32 * k + 5 for k in range(12)], 2 | 0x200, 256),
 ]
 
 

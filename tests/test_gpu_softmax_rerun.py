@@ -10,8 +10,8 @@ keys, so every split of more than a few tiles takes that second pass. The test
 first proves, in float64 on the stored values, that the climb really exceeds
 64 in base 2 inside each such split, then compares every row with the oracle.
 It covers bf16 / bf16, bf16 Q with fp8 KV and fp8 / fp8; causal and
-non-causal; unsplit rows, split rows merged by the merge kernel, and split
-rows merged inside the decode kernel."""
+non-causal; unsplit rows, split rows merged by the merge kernel, split
+rows merged inside the decode kernel, and (fp8 KV) the fp8 PV products."""
 import math
 
 import numpy as np
@@ -33,6 +33,8 @@ PLANS = {
     "unsplit": (1, 1),                   # UNIFORM on one CU: one split per row
     "split": (1, 256),                   # UNIFORM on 256 CUs: two splits per long row
     "split_merge_in_kernel": (1 | 0x100, 256),
+    "unsplit_fp8pv": (1 | 0x200, 1),     # fp8 PV products (fp8 KV only)
+    "split_fp8pv": (1 | 0x200, 256),
 }
 
 
@@ -73,9 +75,13 @@ def split_climbs(case, words):
     return out
 
 
-@pytest.mark.parametrize("plan", list(PLANS))
-@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
-@pytest.mark.parametrize("dtypes", [(BF16, BF16), (BF16, FP8), (FP8, FP8)], ids=lambda d: f"q{d[0]}kv{d[1]}")
+DTYPES = [(BF16, BF16), (BF16, FP8), (FP8, FP8)]
+CASES = [pytest.param(d, c, p, id=f"q{d[0]}kv{d[1]}-{'causal' if c else 'noncausal'}-{p}")
+         for d in DTYPES for c in (True, False) for p in PLANS
+         if d[1] == FP8 or not PLANS[p][0] & 0x200]     # fp8 PV products need fp8 KV
+
+
+@pytest.mark.parametrize("dtypes,causal,plan", CASES)
 def test_logit_climb_rerun(lib, dtypes, causal, plan):
     q_dtype, kv_dtype = dtypes
     mode, cus = PLANS[plan]
@@ -87,7 +93,7 @@ def test_logit_climb_rerun(lib, dtypes, causal, plan):
     # every split of three tiles or more climbs past the headroom
     long_splits = [c for n, c in climbs if n >= 3 * TILE]
     assert long_splits and min(long_splits) > HEADROOM, climbs
-    if plan != "unsplit":
+    if not plan.startswith("unsplit"):
         assert unpack_plan(words)["S"] > case.rows          # the long rows really are split
     O, LSE, used = run_gpu(case, mode=mode, num_cus=cus)
     assert np.array_equal(used, words)

@@ -150,6 +150,20 @@ def test_plan_rejects_bad_arguments():
     for args in [([], 16, 1), ([5], 0, 1), ([5], 129, 1), ([5], 16, 0), ([5], 16, 17), ([-1], 16, 1)]:
         with pytest.raises(ValueError):
             plan_ref(args[0], args[1], args[2], KV_BF16, MODE_AUTO, 256)
+    # the fp8 PV flag needs fp8 KV and a separate merge
+    with pytest.raises(ValueError):
+        plan_ref([5], 16, 1, KV_BF16, MODE_AUTO | 0x200, 256)
+    with pytest.raises(ValueError):
+        plan_ref([5], 16, 1, KV_FP8, MODE_UNIFORM | 0x300, 256)
+
+
+def test_fp8_pv_flag_only_marks_the_mode_word():
+    lens = config_lengths("ragged_persistent_causal")
+    for mode in (MODE_AUTO, MODE_UNIFORM, MODE_LENGTH_AWARE):
+        plain = plan_ref(lens, 128, 2, KV_FP8, mode, 256)
+        flagged = plan_ref(lens, 128, 2, KV_FP8, mode | 0x200, 256)
+        assert flagged[7] == plain[7] | 0x200
+        assert np.array_equal(np.delete(flagged, 7), np.delete(plain, 7))
 
 
 def _estimates_from_words(words, C):

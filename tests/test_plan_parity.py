@@ -46,6 +46,8 @@ def test_random_plans_match_oracle():
         C = int(rng.choice([1, 3, 8, 20, 64, 256, 304]))
         mode = int(rng.integers(0, 3)) | (0x100 if rng.random() < 0.25 else 0)   # in-kernel merge flag
         kv = int(rng.integers(0, 2))
+        if kv == 1 and not mode & 0x100 and rng.random() < 0.3:
+            mode |= 0x200                                                       # fp8 PV flag
         _same([int(x) for x in lens], H, q, kv, mode, C)
 
 
