@@ -180,6 +180,8 @@ def main():
                          "under sustained load); 0 skips")
     ap.add_argument("--fp8-pv", action="store_true",
                     help="fp8 PV products (plan flag PLAN_FP8_PV; fp8-KV workloads only)")
+    ap.add_argument("--merge-in-kernel", action="store_true",
+                    help="plan flag PLAN_MERGE_IN_KERNEL (rows with at most 16 splits merged by the decode kernel)")
     ap.add_argument("--graph-replay", type=int, default=0, metavar="N",
                     help="also capture one decode call (plan uploaded, workspace allocated beforehand) "
                          "in a HIP graph and time N back-to-back replays: the launch-amortized call time")
@@ -227,7 +229,9 @@ def main():
                   "length_aware": mla.PLAN_LENGTH_AWARE}
     if args.fp8_pv and case.kv_dtype != "fp8":
         raise SystemExit("--fp8-pv needs a workload with fp8 KV")
-    pv_flag = mla.PLAN_FP8_PV if args.fp8_pv else 0
+    if args.fp8_pv and args.merge_in_kernel:
+        raise SystemExit("--fp8-pv does not combine with --merge-in-kernel")
+    pv_flag = (mla.PLAN_FP8_PV if args.fp8_pv else 0) | (mla.PLAN_MERGE_IN_KERNEL if args.merge_in_kernel else 0)
     dec = mla.MlaDecoder(case.heads, case.q_len, case.q_dtype, case.kv_dtype, case.causal,
                          float(case.sm_scale), mode=plan_modes[args.plan] | pv_flag)
     T = case.num_tokens
@@ -354,6 +358,7 @@ def main():
         "config": {"workload": args.workload, "rows": case.rows, "q_len": case.q_len,
                    "heads": case.heads, "q_dtype": case.q_dtype, "kv_dtype": case.kv_dtype,
                    "causal": case.causal, "kv_keys": keys, "pv_dtype": pv_dt, "plan_mode": plan_info["mode"],
+                   "merge_in_kernel": bool(args.merge_in_kernel),
                    "splits": plan_info["S"], "workgroups": plan_info["G"],
                    "index_rotation": len(inputs), "cache_flush": flush is not None},
         "mfma_tflops": round(tflops_step, 2),
@@ -539,6 +544,7 @@ def bench_dcp(args):
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
+    settle = settle_device(lambda k: fwd(), args.settle_ms) if args.settle_ms > 0 else None
     t_dec = timed(fwd)
     t_mrg = timed(lambda: mla.merge_shards(o_parts, lse_parts, om, lm))
     keys = int(loc.sum())
@@ -561,7 +567,8 @@ def bench_dcp(args):
                      "algorithmic_flops": flops},
         "merge": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "shard_merge_kernel",
-                  "launch_ms": round(t_mrg, 4), "algorithmic_bytes": mbytes}}), flush=True)
+                  "launch_ms": round(t_mrg, 4), "algorithmic_bytes": mbytes},
+        "settle": settle}), flush=True)
 
 
 def mla_plan_info(words):

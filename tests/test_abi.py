@@ -262,3 +262,19 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError, match="must be on"):
         lib_mod.decode_fwd(q, 0, None, pool, 0, None, i32, i32, i32, good_plan(), None, 2, 16, 1,
                            True, 0.1, o, lse)
+
+
+def test_header_documents_the_plan_constants(lib):
+    """The plan layout the header documents (spec version, M tile, N_MAX,
+    header words) is the one the planner writes and the library checks."""
+    hdr = open(os.path.join(ROOT, "include", "mla_decode.h")).read()
+    internal = open(os.path.join(ROOT, "paged_mla_decode_02_amd", "csrc", "mla_internal.h")).read()
+    const = {k: int(v, 0) for k, v in re.findall(r"constexpr int32_t (k\w+) = (0x[0-9A-Fa-f]+|\d+);", internal)}
+    assert f"spec version {const['kPlanVersion']}" in hdr
+    assert f"version {const['kPlanVersion']}," in hdr
+    assert f"M_UNIT ({const['kMUnit']})" in hdr and f"M tile of {const['kMUnit']} query rows" in hdr
+    assert f"N_MAX ({const['kNMax']})" in hdr
+    assert f"a {const['kHeaderWords']}-word header" in hdr and f"magic 0x{const['kPlanMagic']:08X}" in hdr
+    words = lib_mod.plan([100, 7], 16, 2, "bf16")
+    assert words[0] == const["kPlanMagic"] and words[1] == const["kPlanVersion"]
+    assert words[8] == const["kMUnit"] and words[10] == const["kNMax"] and words[18] == const["kHeaderWords"]
