@@ -833,7 +833,15 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
   if constexpr (PREV) {
     if constexpr (!QK) publish_p<PV8>(smem, la, pbuf, par, lane, sm);   // the slot loop ended with the last piece
   }
-  if constexpr (PREV) __syncthreads();   // P^T(t-1) of all rows is visible
+  if constexpr (!PV8) {
+    // This wave's loads of tile t+1 (issued in step t-1, before this step's
+    // slot-list load) have landed; after the barrier P^T(t-1) and tile t+1
+    // are visible to every wave. It is the step's only barrier.
+    wait_vm<1>();
+    __syncthreads();
+  } else if constexpr (PREV) {
+    __syncthreads();   // P^T(t-1) of all rows is visible
+  }
   // Phase B.
   if constexpr (PV8) {
     if (PREV && pv_now) {   // uniform
@@ -1094,9 +1102,14 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
                 smem, la_s, qf, LY::main(t), LY::rope(t), s_old, score_row, lim_old, rs, p_buf(t + 1),
                 LY::main(t + 11), oacc, dma);
           }
-          if (DO_DMA) wait_vm<1 + Dma::n>();
-          else wait_vm<1>();
-          __syncthreads();   // tile t+1 landed; tile t-1 and P(t-1) are free
+          if constexpr (PV8) {
+            // (fp8 PV reads P^T of tile tA one step after it is written, so a
+            // wave in phase A of the next step must not overwrite that buffer
+            // parity before every wave has finished this phase B)
+            if (DO_DMA) wait_vm<1 + Dma::n>();
+            else wait_vm<1>();
+            __syncthreads();   // tile t+1 landed; tile t-1 and P(t-1) are free
+          }
         };
         using T_ = std::true_type;
         using F_ = std::false_type;
