@@ -139,7 +139,7 @@ int32_t mla::decode_impl(const void* q, mla_dtype q_dtype, const float* q_scale,
     mg.skip_upto = a.inkernel_max_splits;
     mg.o = a.o;
     mg.lse = lse;
-    e = launch_merge(mg, rows, num_heads, q_len_max, s);
+    e = launch_merge(mg, rows, num_heads, q_len_max, v.max_splits, s);
     if (e != hipSuccess) return set_error(MLA_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
   }
   return MLA_OK;

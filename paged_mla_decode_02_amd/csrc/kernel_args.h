@@ -83,7 +83,8 @@ constexpr int kDecodeThreads = 256;  // decode and gather kernels: 4 waves of 64
 
 // pv_fp8: the fp8 PV products (fp8 KV only).
 hipError_t launch_decode(const DecodeArgs& a, bool q_fp8, bool kv_fp8, bool pv_fp8, int grid, hipStream_t st);
-hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, hipStream_t st);
+// max_splits: the plan's largest split count of a row (picks the merge layout).
+hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, int max_splits, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, bool kv_fp8, int splits, hipStream_t st);
 hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t st);
 hipError_t launch_zero(uint32_t* p, int32_t words, hipStream_t st);

@@ -118,6 +118,58 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
   store_merged(a, (int64_t)(q0 + i) * a.heads + h, lane, st);
 }
 
+// Rows with many splits (long rows cut over many compute units): one block of
+// eight waves per (request row b, query token i, head h). Wave w folds chunks
+// w, w + 8, w + 16, ... of 16 splits, so up to 128 splits of a row are in
+// flight at once, and the eight running states are then combined through LDS
+// (each rescaled to the largest max) by wave 0, which stores the row.
+constexpr int kWideThreads = 512;
+__global__ __launch_bounds__(kWideThreads) void merge_wide_kernel(MergeArgs a) {
+  constexpr int kW = kWideThreads / 64;
+  __shared__ f32x4 acc_s[kW][2][64];
+  __shared__ float ml_s[kW][2];
+  const int h = blockIdx.x % a.heads;
+  const int bi = blockIdx.x / a.heads;
+  const int b = bi / a.q_len_max;
+  const int i = bi - b * a.q_len_max;
+  const int s0 = a.plan[a.off_split_indptr + b];
+  const int n = a.plan[a.off_split_indptr + b + 1] - s0;
+  if (n <= a.skip_upto) return;   // unsplit, or merged in the decode kernel (uniform)
+  const int q0 = a.qo_indptr[b];
+  if (i >= a.qo_indptr[b + 1] - q0) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part0 = a.plan[a.off_split_part + s0];
+  const int64_t stride = (int64_t)a.q_len_max * a.heads;   // partial slots are consecutive
+  const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
+  MergeState st{-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  for (int k0 = kChunkWide * w; k0 < n; k0 += kChunkWide * kW)
+    merge_chunk<kChunkWide>(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, k0, n, st);
+  acc_s[w][0][lane] = st.acc0;
+  acc_s[w][1][lane] = st.acc1;
+  if (lane == 0) {
+    ml_s[w][0] = st.m;
+    ml_s[w][1] = st.l;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  MergeState t{-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int u = 0; u < kW; ++u) t.m = fmaxf(t.m, ml_s[u][0]);
+  if (t.m != -INFINITY) {
+#pragma unroll
+    for (int u = 0; u < kW; ++u) {
+      const float mu = ml_s[u][0];
+      if (mu == -INFINITY) continue;   // a wave whose splits saw no key (uniform)
+      const float c = __builtin_amdgcn_exp2f((mu - t.m) * kLog2e);
+      t.l += c * ml_s[u][1];
+      t.acc0 += c * acc_s[u][0][lane];
+      t.acc1 += c * acc_s[u][1][lane];
+    }
+  }
+  store_merged(a, (int64_t)(q0 + i) * a.heads + h, lane, t);
+}
+
 // ---------------------------------------------------------------------------
 // Merge of decode-context-parallel shard outputs: one wave per (token, head)
 // row; lane k < world reads LSE_k, the wave reduces max and sum, and every
@@ -161,9 +213,12 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int32_t words) {
 
 }  // namespace
 
-hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, hipStream_t st) {
+hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, int max_splits, hipStream_t st) {
   void* args[] = {(void*)&a};
   constexpr int kW = kBlockThreads / 64;
+  if (max_splits > kChunkWide)   // some row needs more than one round trip per wave
+    return hipLaunchKernel((const void*)merge_wide_kernel, dim3(rows * q_len_max * heads), dim3(kWideThreads), args,
+                           0, st);
   dim3 grid(rows * q_len_max * ((heads + kW - 1) / kW));
   return hipLaunchKernel((const void*)merge_kernel, grid, dim3(kBlockThreads), args, 0, st);
 }
