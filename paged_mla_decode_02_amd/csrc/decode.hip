@@ -360,17 +360,27 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
 }
-// 8 bf16 elements (times `scale`) -> 2 dwords of hi and 2 of lo.
-__device__ __forceinline__ void split_fp8x8(bf16x8 x, float scale, uint32_t* hi, uint32_t* lo) {
+// 8 bf16 elements (4 dwords of 2; times `scale` = 2^A, `inv` = 2^-A) -> 2
+// dwords of hi and 2 of lo. hi comes straight from the packed bf16 pairs:
+// v_cvt_scalef32_pk_fp8_bf16 rounds x / inv = x 2^A to e4m3 (nearest even),
+// which a host model of the instruction confirmed; lo = fp8(x 2^A - hi), the
+// product x 2^A being exact.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef short i16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ void split_fp8x8(const uint32_t* w, float scale, float inv, uint32_t* hi, uint32_t* lo) {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const float y0 = (float)x[4 * q] * scale, y1 = (float)x[4 * q + 1] * scale;
-    const float y2 = (float)x[4 * q + 2] * scale, y3 = (float)x[4 * q + 3] * scale;
-    const uint32_t h = pack_fp8x4(y0, y1, y2, y3);
+    const uint32_t w0 = w[2 * q], w1 = w[2 * q + 1];
+    i16x2v hv = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(i16x2v{0, 0}, __builtin_bit_cast(bf16x2v, w0), inv, false);
+    hv = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hv, __builtin_bit_cast(bf16x2v, w1), inv, true);
+    const uint32_t h = __builtin_bit_cast(uint32_t, hv);
     const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, false);
     const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, true);
     hi[q] = h;
-    lo[q] = pack_fp8x4(y0 - f01[0], y1 - f01[1], y2 - f23[0], y3 - f23[1]);
+    lo[q] = pack_fp8x4(__builtin_fmaf(bf16_lo(w0), scale, -f01[0]), __builtin_fmaf(bf16_hi(w0), scale, -f01[1]),
+                       __builtin_fmaf(bf16_lo(w1), scale, -f23[0]), __builtin_fmaf(bf16_hi(w1), scale, -f23[1]));
   }
 }
 // In place: q[2 p] and q[2 p + 1] hold the 32 bf16 elements of product p
@@ -378,16 +388,20 @@ __device__ __forceinline__ void split_fp8x8(bf16x8 x, float scale, uint32_t* hi,
 // and lo fp8 operands. The row's largest |x| is taken over both lane halves
 // (lanes l and l ^ 32 hold one row). Returns 2^-A.
 __device__ __forceinline__ float split_q_rows(u32x8 (&q)[2 * kKSteps8]) {
-  uint32_t m = 0;   // largest |x| as bf16 bits: the order of non-negative floats
+  // largest |x| as bf16 bits (the order of non-negative floats), two per
+  // dword with packed 16-bit max
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m2 = {0, 0};
 #pragma unroll
   for (int n = 0; n < 2 * kKSteps8; ++n)
 #pragma unroll
-    for (int d = 0; d < 8; ++d) m = max(m, max(q[n][d] & 0x7FFFu, (q[n][d] >> 16) & 0x7FFFu));
+    for (int d = 0; d < 8; ++d) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, q[n][d] & 0x7FFF7FFFu));
+  const uint32_t m = max((uint32_t)m2[0], (uint32_t)m2[1]);
   const float amax = half_max(__uint_as_float(m << 16));
   int ex = 0;
   if (amax > 0.f && __builtin_isfinite(amax)) frexpf(amax, &ex);   // amax in [2^(ex-1), 2^ex)
   ex = max(ex, -100);   // keeps 2^(8 - ex) and the score scale normal floats
-  const float scale = ldexpf(1.0f, 8 - ex);
+  const float scale = ldexpf(1.0f, 8 - ex), inv = ldexpf(1.0f, ex - 8);
 #pragma unroll
   for (int p = 0; p < kKSteps8; ++p) {
     uint32_t hi[8], lo[8];
@@ -395,8 +409,8 @@ __device__ __forceinline__ float split_q_rows(u32x8 (&q)[2 * kKSteps8]) {
     for (int u = 0; u < 4; ++u) {
       const u32x8& v = q[2 * p + (u >> 1)];
       const int d0 = 4 * (u & 1);
-      split_fp8x8(__builtin_bit_cast(bf16x8, u32x4{v[d0], v[d0 + 1], v[d0 + 2], v[d0 + 3]}), scale,
-                  hi + 2 * u, lo + 2 * u);
+      const uint32_t w4[4] = {v[d0], v[d0 + 1], v[d0 + 2], v[d0 + 3]};
+      split_fp8x8(w4, scale, inv, hi + 2 * u, lo + 2 * u);
     }
     q[2 * p] = u32x8{hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]};
     q[2 * p + 1] = u32x8{lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]};
