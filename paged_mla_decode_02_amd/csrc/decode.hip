@@ -115,7 +115,8 @@ constexpr int kOffP = kTilesEnd;                      // [2] P^T buffers (tiles 
 constexpr int kOffL = kOffP + 2 * kPBytes;            // [128] f32 row sums (epilogue)
 constexpr int kOffSlots = kOffL + kRows * 4;          // [4 waves][4][32] int32
 constexpr int kOffMisc = kOffSlots + kWaves * kSlotRing * kNT * 4;     // [4] u32 (restart, merge flags)
-constexpr int kSmemBytes = kOffMisc + 16;                                // 162320
+constexpr int kOffP8Scale = kOffMisc + 16;   // fp8 PV: [4 tile parities][32 rows] u32 of scale codes
+constexpr int kSmemBytes = kOffP8Scale + 4 * 32 * 4;                     // 162832
 constexpr int kMaxInKernelSplits = 16;
 constexpr float kRefSlack = 64.0f;       // base-2 headroom above a row's reference max
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
@@ -124,20 +125,20 @@ static_assert(kRows * kDV * 2 <= kTilesEnd, "epilogue staging of the item's 128 
 
 // fp8 PV (fp8 KV only): tiles t-2 and t-1 stay in LDS until the step that
 // multiplies both, so the main tiles take a longer ring; P^T goes through LDS
-// in fp8, [2 tile parities][4 row blocks][64 lanes] x 16 bytes, followed by
-// the per-(row, tile) power-of-two scales, [2 parities][32 rows] x 4 bytes
-// (byte rb for row block rb).
+// in fp8, [tile mod 4][4 row blocks][64 lanes] x 16 bytes (four tiles: a
+// tile's P^T is read up to one step after it is written, while the waves
+// may be a phase apart), with the per-(row, tile) power-of-two scales at
+// kOffP8Scale, [tile mod 4][32 rows] x 4 bytes (byte rb for row block rb).
 // With split bf16 queries the hi and lo operands of the last kQLds QK
 // products (dims 448..575) wait in LDS after the tiles, [4 waves][2 kQLds
 // links][64 lanes] x 32 bytes, instead of in 32 registers; 6 main tiles
 // suffice (t-2 .. t+2 are in use during step t).
 constexpr int kMainBufs8 = 6;
-constexpr int kQLds = 1;
+constexpr int kQLds = 2;
 constexpr int kOffQ8 = kMainBufs8 * kF8MainBytes + kRopeBufs * kF8RopeBytes;
 static_assert(kOffQ8 + kWaves * 2 * kQLds * 64 * 32 <= kTilesEnd, "fp8-PV tiles and the staged queries");
 constexpr int kP8Bytes = kRowBlocks * 64 * 16;                  // 4096 per tile
-constexpr int kOffP8Scale = kOffP + 2 * kP8Bytes;
-static_assert(kOffP8Scale + 2 * 32 * 4 <= kOffL, "fp8 P^T and its scales fit the P^T region");
+static_assert(kOffP + 4 * kP8Bytes <= kOffL, "fp8 P^T of four tiles fits the P^T region");
 
 // LDS offsets of tile t's buffers.
 template <bool KV_FP8, bool PV8 = false> struct Layout;
@@ -786,7 +787,7 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
                                               int lim_old, RowState& rs, int pbuf, int vmain,
                                               f32x16 (&oacc)[kRowBlocks][kColTiles], Dma&& dma,
                                               int vmain2 = 0, int par = 0, bool pv_now = false,
-                                              bool single = false, int lane = 0) {
+                                              bool single = false, int lane = 0, int rpar = 0) {
   static_assert(kSmStride * kSoftmaxPieces <= kKSteps, "softmax pieces fit between the QK products");
   static_assert(NDMA == 0 || kDmaStride * (NDMA - 1) < 32, "loads fit between the PV products");
   // bf16 K: fragments read kKDepth products ahead; fp8 K: kK8Depth.
@@ -847,29 +848,25 @@ __device__ __forceinline__ void pipeline_step(lds_u8* smem, const LaneAddr& la, 
   if constexpr (PREV) {
     if constexpr (!QK) publish_p<PV8>(smem, la, pbuf, par, lane, sm);   // the slot loop ended with the last piece
   }
-  if constexpr (!PV8) {
-    // This wave's loads of tile t+1 (issued in step t-1, before this step's
-    // slot-list load) have landed; after the barrier P^T(t-1) and tile t+1
-    // are visible to every wave. It is the step's only barrier.
-    wait_vm<1>();
-    __syncthreads();
-  } else if constexpr (PREV) {
-    __syncthreads();   // P^T(t-1) of all rows is visible
-  }
+  // This wave's loads of tile t+1 (issued in step t-1, before this step's
+  // slot-list load) have landed; after the barrier P^T(t-1) and tile t+1 are
+  // visible to every wave. It is the step's only barrier.
+  wait_vm<1>();
+  __syncthreads();
   // Phase B.
   if constexpr (PV8) {
     if (PREV && pv_now) {   // uniform
       // Two halves of two row blocks each (P^T of two row blocks, 16
       // registers, at a time); the V^T fragments are read once per half.
-      uint32_t sc = lds_load<uint32_t>(smem, kOffP8Scale + (lane >> 5) * 128 + (lane & 31) * 4);
+      uint32_t sc = lds_load<uint32_t>(smem, kOffP8Scale + (rpar + (lane >> 5)) * 128 + (lane & 31) * 4);
       if (!QK && single) sc = lane >= 32 ? 0x7F7F7F7Fu : sc;   // tile tA + 1 does not exist
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         u32x8 pb8[2];
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-          pb8[r] = cat8(lds_load<u32x4>(smem, kOffP + (2 * hh + r) * 1024 + la.pl),
-                        lds_load<u32x4>(smem, kOffP + kP8Bytes + (2 * hh + r) * 1024 + la.pl));
+          pb8[r] = cat8(lds_load<u32x4>(smem, kOffP + rpar * kP8Bytes + (2 * hh + r) * 1024 + la.pl),
+                        lds_load<u32x4>(smem, kOffP + (rpar + 1) * kP8Bytes + (2 * hh + r) * 1024 + la.pl));
           if (!QK && single) pb8[r][4] = pb8[r][5] = pb8[r][6] = pb8[r][7] = 0u;   // its half of each product is zero
         }
         u32x8 va[2];
@@ -1110,19 +1107,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
             const bool single = !DO_QK && (t & 1) != 0;
             pipeline_step<DO_QK, PREV, DO_DMA ? Dma::n : 0, KV_FP8, FAST, QKM, true>(
                 smem, la_s, qf, LY::main(t), LY::rope(t), s_old, score_row, lim_old, rs, 0, LY::main(tA), oacc,
-                dma, LY::main(single ? tA : tA + 1), (t - 1) & 1, !DO_QK || (t & 1) == 0, single, dlane);
+                dma, LY::main(single ? tA : tA + 1), (t - 1) & 3, !DO_QK || (t & 1) == 0, single, dlane, tA & 3);
           } else {
             pipeline_step<DO_QK, PREV, DO_DMA ? Dma::n : 0, KV_FP8, FAST, QKM>(
                 smem, la_s, qf, LY::main(t), LY::rope(t), s_old, score_row, lim_old, rs, p_buf(t + 1),
                 LY::main(t + 11), oacc, dma);
-          }
-          if constexpr (PV8) {
-            // (fp8 PV reads P^T of tile tA one step after it is written, so a
-            // wave in phase A of the next step must not overwrite that buffer
-            // parity before every wave has finished this phase B)
-            if (DO_DMA) wait_vm<1 + Dma::n>();
-            else wait_vm<1>();
-            __syncthreads();   // tile t+1 landed; tile t-1 and P(t-1) are free
           }
         };
         using T_ = std::true_type;
