@@ -90,7 +90,7 @@ def traffic_from_counters(workload, fetch_csv, write_csv, copy_mib):
         copy_kib = max(v for (d, k), v in vals.items() if "copyBuffer" in k)
         factor = copy_kib / (copy_mib * 1024.0)
         decode = [v for (d, k), v in vals.items() if "decode_kernel" in k]
-        merge = [v for (d, k), v in vals.items() if "merge_kernel" in k]
+        merge = [v for (d, k), v in vals.items() if "merge_kernel" in k or "merge_wide_kernel" in k]
         launches = len(decode)
         kib = (sum(decode) + sum(merge)) / launches
         out[name] = {"raw_kib_per_launch": round(kib, 3), "copy_raw_kib": round(copy_kib, 3),
@@ -344,7 +344,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
     roof["traffic"] = traffic
-    roof["kernel"] = "decode_kernel" + ("+merge_kernel" if plan_info["P"] > 0 else "")
+    roof["kernel"] = "decode_kernel" + (("+merge_wide_kernel" if plan_info["max_splits"] > 16 else "+merge_kernel")
+                                        if plan_info["P"] > 0 else "")
     roof["launch_ms"] = round(fwd_avg, 4)
     roof["launch_ms_p10_p50_p90"] = [round(x, 4) for x in fwd_p]
     roof["algorithmic_bytes"] = alg_bytes
@@ -576,6 +577,8 @@ def mla_plan_info(words):
              "N_MAX", "MIN_SPLIT_KEYS", "ITEM_OVERHEAD", "OCC", "S", "W", "G", "P"]
     d = dict(zip(names, [int(x) for x in words[:18]]))
     d["mode"] = {1: "uniform", 2: "length_aware"}.get(d["mode"] & 0xFF, d["mode"])
+    indptr = np.asarray(words[20:20 + d["R"] + 1], dtype=np.int64)   # split_indptr follows the 20-word header
+    d["max_splits"] = int(np.diff(indptr).max()) if d["R"] > 0 else 0
     return d
 
 
