@@ -38,10 +38,11 @@
 // shuffle; the V^T reads use the same key order.
 //
 // The stages form a software pipeline of one step per tile, in two phases
-// split by a barrier: phase A of step t runs the 36 QK products of tile t
-// with the softmax of tile t-1 spread between them (VALU work beside the
-// matrix core) and publishes P^T(t-1); phase B runs the 32 PV products of
-// tile t-1 with the loads of tile t+2 spread between them.
+// split by the step's only barrier: phase A of step t runs the 36 QK
+// products of tile t with the softmax of tile t-1 spread between them (VALU
+// work beside the matrix core) and publishes P^T(t-1); phase B runs the 32
+// PV products of tile t-1 with the loads of tile t+2 spread between them,
+// and the wave goes straight on to the next step's phase A.
 //
 // fp8 KV stays fp8 in LDS (half the HBM and LDS bytes). K fragments feed the
 // fp8 QK products as they are; V^T fragments are converted to bf16 in
@@ -68,9 +69,12 @@
 // (the LDS side of a direct load is fixed to consecutive 16-byte chunks).
 //
 // Loads run two tiles ahead: step t issues tile t+2's loads, and every wave
-// waits for its own loads of tile t+1 before the barrier that ends the step.
-// The loads are inline assembly, so the compiler neither waits for them early
-// nor tracks them.
+// waits for its own loads of tile t+1 before step t's barrier, after which
+// tile t+1 is visible to all waves. Waves may thus be up to one phase apart
+// between two barriers; every LDS buffer is rewritten only after a barrier
+// that every reader of its previous contents has passed. The loads are
+// inline assembly, so the compiler neither waits for them early nor tracks
+// them.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <type_traits>
@@ -762,7 +766,8 @@ __device__ __forceinline__ void publish_p(lds_u8* smem, const LaneAddr& la, int 
 //     VALU works on the softmax. The last QK product writes the scores of
 //     tile t into s_old (the softmax has ended by then); the chain itself
 //     accumulates in a variable local to the step.
-//   Barrier: P^T(t-1) of every wave is visible.
+//   Barrier (the step's only one): this wave first waits for its loads of
+//     tile t+1; after it P^T(t-1) of every wave and tile t+1 are visible.
 //   Phase B: PV(t-1) (if PREV) with V in vmain and P^T in pbuf; dma(i),
 //     i < NDMA, issues later tiles' loads, one every kDmaStride products.
 // A sched_barrier ends every slot, so the compiler keeps this order. K
@@ -1079,10 +1084,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         // next step.
         f32x16 s_old;
         // Step t: QK(t) if t < ntiles, the softmax of tile t-1 and PV(t-1) if
-        // t >= 1; tile t+2's loads are issued in phase B. The step ends with
-        // this wave's loads of tile t+1 landed and one barrier. QK, PREV and
-        // DMA are template flags, so the hot loop carries no per-slot branch;
-        // FAST selects the unmasked softmax for tile t-1.
+        // t >= 1; tile t+2's loads are issued in phase B, after the step's
+        // barrier (which also publishes tile t+1). QK, PREV and DMA are
+        // template flags, so the hot loop carries no per-slot branch; FAST
+        // selects the unmasked softmax for tile t-1.
         auto run_step = [&](int t, auto QKc, auto PREVc, auto DMAc, auto FASTc) {
           constexpr bool DO_QK = decltype(QKc)::value, PREV = decltype(PREVc)::value;
           constexpr bool DO_DMA = decltype(DMAc)::value, FAST = decltype(FASTc)::value;
