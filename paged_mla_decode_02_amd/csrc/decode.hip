@@ -144,6 +144,25 @@ static_assert(kOffQ8 + kWaves * 2 * kQLds * 64 * 32 <= kTilesEnd, "fp8-PV tiles 
 constexpr int kP8Bytes = kRowBlocks * 64 * 16;                  // 4096 per tile
 static_assert(kOffP + 4 * kP8Bytes <= kOffL, "fp8 P^T of four tiles fits the P^T region");
 
+// Query staging: at the head of a work item its 128 query rows pass through
+// LDS as four 32-row tiles (tile q: the rows of wave q) in the tile layout of
+// the query dtype, loaded by the tile loader with the block's row index in
+// place of a pool slot. Each load instruction then moves whole rows (one
+// 1 KB row, or eight 128-byte rope rows) instead of 32 bytes of 32 rows, and
+// the rows reach the registers with conflict-free LDS reads. The region
+// overlaps the first tiles and the P^T buffers, which the item uses only
+// after its queries are in registers.
+template <bool QF8> struct QStage;
+template <> struct QStage<false> {
+  static __device__ __forceinline__ int main(int q) { return q * kMainBytes; }
+  static __device__ __forceinline__ int rope(int q) { return 4 * kMainBytes + q * kRopeBytes; }
+};
+template <> struct QStage<true> {
+  static __device__ __forceinline__ int main(int q) { return q * kF8MainBytes; }
+  static __device__ __forceinline__ int rope(int q) { return 4 * kF8MainBytes + q * kF8RopeBytes; }
+};
+static_assert(kWaves * (kMainBytes + kRopeBytes) <= kOffL, "bf16 query staging below the row sums");
+
 // LDS offsets of tile t's buffers.
 template <bool KV_FP8, bool PV8 = false> struct Layout;
 template <> struct Layout<false, false> {
@@ -362,7 +381,7 @@ __device__ __forceinline__ u32x8 cat8(u32x4 a, u32x4 b) {
 // 2^-17 of the row's largest. The scores come out times 2^A, which the
 // softmax takes out with its score scale.
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)__float_as_uint(a), false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
 }
 // 8 bf16 elements (4 dwords of 2; times `scale` = 2^A, `inv` = 2^-A) -> 2
@@ -378,7 +397,8 @@ __device__ __forceinline__ void split_fp8x8(const uint32_t* w, float scale, floa
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const uint32_t w0 = w[2 * q], w1 = w[2 * q + 1];
-    i16x2v hv = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(i16x2v{0, 0}, __builtin_bit_cast(bf16x2v, w0), inv, false);
+    i16x2v hv = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(i16x2v, w0), __builtin_bit_cast(bf16x2v, w0),
+                                                          inv, false);
     hv = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hv, __builtin_bit_cast(bf16x2v, w1), inv, true);
     const uint32_t h = __builtin_bit_cast(uint32_t, hv);
     const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, false);
@@ -501,6 +521,18 @@ __device__ __forceinline__ u32x4 k_pair_f8(const lds_u8* smem, const LaneAddr& l
 // 64 p + 32 + 16 h, 16 bytes each).
 __device__ __forceinline__ u32x8 k_prod_f8(const lds_u8* smem, const LaneAddr& la, int kmain, int krope, int p) {
   return cat8(k_pair_f8(smem, la, kmain, krope, 2 * p), k_pair_f8(smem, la, kmain, krope, 2 * p + 1));
+}
+// Staged bf16 query row i = lane & 31, read for the split into fp8 operands:
+// operand n holds 16-byte chunks 4 n + 2 h and 4 n + 2 h + 1 (dims
+// 32 n + 16 h .. +15, h = lane >> 5), main chunk c of the row stored at
+// c ^ swz_main(i), rope chunk c at c ^ swz_rope(i) (the bf16 tile layout).
+__device__ __forceinline__ u32x8 q_raw_bf16(const lds_u8* smem, int qmain, int qrope, int lane, int n) {
+  const int i = lane & 31, c0 = 4 * n + 2 * (lane >> 5);
+  auto at = [&](int c) {
+    return c < 64 ? qmain + i * kMainRow + ((c ^ swz_main(i)) << 4)
+                  : qrope + i * kRopeRow + (((c - 64) ^ swz_rope(i)) << 4);
+  };
+  return cat8(lds_load<u32x4>(smem, at(c0)), lds_load<u32x4>(smem, at(c0 + 1)));
 }
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return cat(fp8x4_to_bf16(lo), fp8x4_to_bf16(hi));
@@ -965,9 +997,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     const int mr = m * kRows + 32 * w + (ilane & 31);
     const bool row_ok = mr < M;
     // (rows past the block's end get a token index past q_b; nothing of
-    // theirs is loaded or written)
+    // theirs is written)
     const int tok = div_small(mr, opaque_s(H));
-    const int head = mr - tok * H;
     // Causal mask on global positions: local key j sits at j * world + rank
     // of the row's P keys over all shards, token tok at P - q_b + tok; the
     // visible local keys are j <= (P - q_b + tok - rank) / world (one shard:
@@ -987,46 +1018,55 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     // and lo (qf[2 p + 1]); score_row then carries the row's 2^-A.
     std::conditional_t<(QKM > 0), u32x8, bf16x8> qf[QKM == 0 ? kKSteps : QKM * kKSteps8];
     float score_row = score_c;
-    // The split of bf16 queries for fp8 KV keeps its rows past the block's
-    // end at zero (loaded under a branch); the other modes load those rows as
-    // a copy of the block's last row (computed, never written), with no
-    // branch around the loads.
-    if (QKM != 2 || row_ok) {
-      // Query row (tok, head) of the block is row mr of the request row's
-      // [q_b * H, 576] block: a uniform row base plus a 32-bit lane offset.
-      constexpr int kQElem = Q_FP8 ? 1 : 2;
-      const unsigned char* qblock = (const unsigned char*)a.q + (int64_t)q0 * H * (kDLat * kQElem);
-      // (opaque: computed here, inside the branch, rather than hoisted above it
-      // and spilled)
-      const unsigned char* qsrc = qblock + (uint32_t)opaque(min(mr, M - 1)) * (uint32_t)(kDLat * kQElem);
-      const int h = ilane >> 5;
-      auto unit = [&](int ks) { return 2 * ks + h; };
-      if constexpr (QKM == 1) {
-        const u32x4* src = (const u32x4*)qsrc;
+    // Query row (tok, head) of the block is row mr of the request row's
+    // [q_b * H, 576] block. Rows past the block's end (computed, never
+    // written) take a copy of its last row; the split of bf16 queries for
+    // fp8 KV sets them to zero instead.
+    constexpr int kQElem = Q_FP8 ? 1 : 2;
+    const unsigned char* qblock = (const unsigned char*)a.q + (int64_t)q0 * H * (kDLat * kQElem);
+    // Every mode but fp8 queries with bf16 KV stages its rows through LDS
+    // (in the tile layout of the query dtype). The first slot lists of pass 0
+    // go out first, so that their latency overlaps the staging.
+    constexpr bool kStageQ = !(Q_FP8 && !KV_FP8);
+    if constexpr (kStageQ) {
+      if (ntiles > 0) {
 #pragma unroll
-        for (int p = 0; p < kKSteps8; ++p) qf[p] = cat8(src[4 * p + h], src[4 * p + 2 + h]);
-      } else if constexpr (QKM == 2) {   // raw bf16 here; split once the item's first loads are out
-        const bf16x8* src = (const bf16x8*)qsrc;
+        for (int t = 0; t < 4; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, w, ilane);
 #pragma unroll
-        for (int n = 0; n < 2 * kKSteps8; ++n) {
-          const int u0 = 4 * n + 2 * h;   // bf16 units 8 p + 2 h (+1) for n = 2 p, 8 p + 4 + 2 h (+1) for 2 p + 1
-          qf[n] = cat8(__builtin_bit_cast(u32x4, src[u0]), __builtin_bit_cast(u32x4, src[u0 + 1]));
+        for (int q = 0; q < kWaves; ++q)
+          TileDma<Q_FP8>::all(qblock, m * kRows + 32 * q + (ilane & 31), (uint32_t)(M - 1), smem,
+                              QStage<Q_FP8>::main(q), QStage<Q_FP8>::rope(q), w, ilane);
+        wait_vm<0>();
+        __syncthreads();   // every wave's query rows and slot lists have landed
+        const int ql = opaque(lane);
+        if constexpr (QKM == 0) {
+          const LaneAddr la_q = lane_addr<false>(ql, w);
+#pragma unroll
+          for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = k_frag(smem, la_q, QStage<false>::main(w), QStage<false>::rope(w), ks);
+        } else if constexpr (QKM == 1) {
+          const LaneAddr la_q = lane_addr<true>(ql, w);
+#pragma unroll
+          for (int p = 0; p < kKSteps8; ++p) qf[p] = k_prod_f8(smem, la_q, QStage<true>::main(w), QStage<true>::rope(w), p);
+        } else {   // raw bf16 here; split once the item's first loads are out
+          const bool keep = m * kRows + 32 * w + (ql & 31) < M;
+#pragma unroll
+          for (int n = 0; n < 2 * kKSteps8; ++n) {
+            const u32x8 v = q_raw_bf16(smem, QStage<false>::main(w), QStage<false>::rope(w), ql, n);
+            qf[n] = keep ? v : u32x8{};
+          }
         }
-      } else if constexpr (!Q_FP8) {
-        const bf16x8* src = (const bf16x8*)qsrc;
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = src[unit(ks)];
-      } else {
-        const u32x2* src = (const u32x2*)qsrc;
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
-          const u32x2 v = src[unit(ks)];
-          qf[ks] = cat(fp8x4_to_bf16(v[0]), fp8x4_to_bf16(v[1]));
-        }
+        __syncthreads();   // the tile loads below rewrite the staging region
       }
     } else {
+      // (opaque: computed here rather than hoisted and spilled)
+      const unsigned char* qsrc = qblock + (uint32_t)opaque(min(mr, M - 1)) * (uint32_t)(kDLat * kQElem);
+      const int h = ilane >> 5;
+      const u32x2* src = (const u32x2*)qsrc;
 #pragma unroll
-      for (auto& f : qf) f = {};
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        const u32x2 v = src[2 * ks + h];
+        qf[ks] = cat(fp8x4_to_bf16(v[0]), fp8x4_to_bf16(v[1]));
+      }
     }
 
     // Pass 0 fixes each row's reference at its first visible tile's max. In
@@ -1043,18 +1083,14 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
 #pragma unroll
         for (int ct = 0; ct < kColTiles; ++ct) oacc[rb][ct] = f32x16{};
       if (ntiles > 0) {
-        // Prologue: slot lists of tiles 0..3, then the loads of tiles 0 and
-        // 1, each preceded by one slot-list load so that every later wait
-        // count has the same form; tile 0 lands.
+        // Prologue: slot lists of tiles 0..3 (pass 0 of a staged item has
+        // them already), then the loads of tiles 0 and 1, each preceded by
+        // one slot-list load so that every later wait count has the same
+        // form; tile 0 lands.
+        if (!kStageQ || pass > 0) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, w, ilane);
-        wait_vm<0>();
-        if constexpr (QKM == 2) {
-          // The raw queries have landed with the slot lists; the empty
-          // statements tell the compiler so, and the split below then runs
-          // while the first tiles load.
-#pragma unroll
-          for (auto& f : qf) asm volatile("" : "+v"(f));
+          for (int t = 0; t < 4; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, w, ilane);
+          wait_vm<0>();
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -1138,27 +1174,26 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         run_step(ntiles, F_{}, T_{}, F_{}, F_{});
         wait_vm<0>();
       }
-      // Did any row of the item overflow its reference? (uniform)
+      // Did any row of the item overflow its reference? (uniform) One
+      // barrier publishes the waves' flags and the rows' O denominators for
+      // the epilogue; a pass 1 rewrites both before they are read again.
       if (lane == 0) lds_store(smem, kOffMisc + 4 * w, (uint32_t)(__ballot(rs.over) != 0));
+      {
+        // (cross-lane sums run on every lane, outside the lane < 32 branch)
+        const float l_o = half_sum(PV8 ? rs.l_round : rs.l_part);   // O's denominator
+        const int el = opaque(lane);
+        if (el < 32) lds_store(smem, kOffL + (w * 32 + el) * 4, l_o);
+      }
       __syncthreads();
       const u32x4 ov = lds_load<u32x4>(smem, kOffMisc);
-      __syncthreads();
       if ((ov[0] | ov[1] | ov[2] | ov[3]) == 0u) break;
       rs.m_ref = rs.m_seen;   // pass 1: no tile can exceed the true max
     }
 
-    // Epilogue: the rows' sums and LSE, then O normalized and written.
+    // Epilogue: O normalized and written, then the LSE (stored last, so that
+    // no wait inside the epilogue waits for its store).
     const float l_row = half_sum(rs.l_part);
-    // (cross-lane sums run on every lane, outside the lane < 32 branch)
-    const float l_o = PV8 ? half_sum(rs.l_round) : l_row;   // O's denominator
-    if (lane < 32) lds_store(smem, kOffL + (w * 32 + lane) * 4, l_o);
-    if (row_ok && lane < 32) {
-      const float lse = l_row > 0.f ? (rs.m_ref + __log2f(l_row)) * kLn2 : -INFINITY;
-      // row mr of the block is (token tok, head): index (q0 + tok) H + head
-      if (part < 0) a.lse[(int64_t)q0 * H + mr] = lse;
-      else a.ws_lse[(int64_t)part * a.q_len_max * H + mr] = lse;
-    }
-    __syncthreads();
+    const float lse = l_row > 0.f ? (rs.m_ref + __log2f(l_row)) * kLn2 : -INFINITY;
     // O leaves through LDS so that the stores are whole rows: the item's
     // query rows r = m 128 .. m 128 + 127 are consecutive rows of O (index
     // q0 H + r) and of its partial slot (index (part q_len_max) H + r). All
@@ -1167,7 +1202,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     {
       // Opaque copies: the addresses below are recomputed here rather than
       // hoisted out of the item loop and kept live across it.
-      const int el = opaque(lane), et = opaque(tid);
+      const int el = opaque(lane);
       const int hh = el >> 5;
       const int64_t orow0 = part < 0 ? (int64_t)q0 * H + (int64_t)m * kRows
                                      : (int64_t)part * a.q_len_max * H + (int64_t)m * kRows;
@@ -1192,14 +1227,30 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       __syncthreads();
       const int nrows = min(kRows, M - m * kRows);   // rows of the item inside the block
       uint16_t* const dst0 = part < 0 ? a.o : a.ws_o;   // bf16 O, or the split's partial O
-      // a thread takes one staged chunk (8 columns) of a row per store
-#pragma unroll 4
-      for (int i = 0; i < kRows * 64 / kDecodeThreads; ++i) {
-        const int p2 = i * kDecodeThreads + et;
-        const int r = p2 >> 6, c2 = p2 & 63;
-        if (r < nrows)
-          *(bf16x8*)(dst0 + (orow0 + r) * kDV + 8 * c2) =
-              lds_load<bf16x8>(smem, r * (kDV * 2) + ((c2 ^ (r & 15)) << 4));
+      // A lane takes one staged chunk (8 columns) of a row per store: row
+      // r = 4 i + w (uniform), chunk el. The chunks of a batch are all read
+      // before its stores, so the LDS latency is paid once per batch.
+      constexpr int kStores = kRows / kWaves, kBatch = 8;
+#pragma unroll
+      for (int i0 = 0; i0 < kStores; i0 += kBatch) {
+        bf16x8 v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int r = kWaves * (i0 + j) + w;
+          v[j] = lds_load<bf16x8>(smem, r * (kDV * 2) + ((el ^ (r & 15)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int r = kWaves * (i0 + j) + w;
+          if (r < nrows) *(bf16x8*)(dst0 + (orow0 + r) * kDV + 8 * el) = v[j];
+        }
+      }
+      // The LSE of this wave's rows: row mr of the block is (token tok, head),
+      // index (q0 + tok) H + head = q0 H + mr.
+      const int mr_e = m * kRows + 32 * w + (el & 31);
+      if (el < 32 && mr_e < M) {
+        if (part < 0) a.lse[(int64_t)q0 * H + mr_e] = lse;
+        else a.ws_lse[(int64_t)part * a.q_len_max * H + mr_e] = lse;
       }
       __syncthreads();
     }
