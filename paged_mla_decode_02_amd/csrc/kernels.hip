@@ -15,8 +15,7 @@ namespace {
 using namespace dev;
 
 constexpr int kDV = 512;
-constexpr int kChunk = 8;        // splits whose loads a lane of merge_kernel has in flight at once
-constexpr int kChunkWide = 16;   // the same in merge_wide_kernel
+constexpr int kChunkWide = 16;   // splits whose loads a lane of merge_wide_kernel has in flight at once
 
 // ---------------------------------------------------------------------------
 // Split merge: one block of four waves per (request row b, query token i,
@@ -25,11 +24,11 @@ constexpr int kChunkWide = 16;   // the same in merge_wide_kernel
 // merged by log-sum-exp, online, in chunks: a chunk's partial-O loads and LSE
 // loads are issued together (the LSE addresses are wave-uniform), so a chunk
 // costs one memory round trip, and the running (max, sum, O) are rescaled
-// when a chunk raises the max. A row with n <= 8 splits takes one round trip,
-// more splits ceil(n / 8), the four heads of a block in parallel. (Chunks of
-// 16 for the rows with 9..16 splits made every wave hold 84 registers instead
-// of 51, which cut the waves in flight per SIMD from 9 to 5 and slowed the
-// merge by 5-10% on every workload.)
+// when a chunk raises the max. The chunk size C (2, 4 or 8 splits) is the
+// smallest that covers the plan's largest split count up to 8, so a row takes
+// ceil(n / C) round trips, the four heads of a block in parallel, and a wave
+// holds no more registers than its chunk needs (the waves in flight per SIMD
+// grow as the chunk shrinks).
 struct MergeState {
   float m, l;       // running max of LSE_k, and sum of exp(LSE_k - m)
   f32x4 acc0, acc1; // sum of exp(LSE_k - m) O_k over this lane's 8 columns
@@ -91,6 +90,7 @@ __device__ __forceinline__ void store_merged(const MergeArgs& a, int64_t orow, i
   if (lane == 0) a.lse[orow] = st.m + __log2f(st.l) * kLn2;
 }
 
+template <int C>
 __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
   constexpr int kW = kBlockThreads / 64;
   const int hgroups = (a.heads + kW - 1) / kW;
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
   const int64_t stride = (int64_t)a.q_len_max * a.heads;   // partial slots are consecutive
   const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
   MergeState st{-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  for (int k0 = 0; k0 < n; k0 += kChunk)   // uniform over the block: n is the row's
-    merge_chunk<kChunk>(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, k0, n, st);
+  for (int k0 = 0; k0 < n; k0 += C)   // uniform over the block: n is the row's
+    merge_chunk<C>(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, k0, n, st);
   store_merged(a, (int64_t)(q0 + i) * a.heads + h, lane, st);
 }
 
@@ -218,7 +218,10 @@ hipError_t launch_merge(const MergeArgs& a, int rows, int heads, int q_len_max, 
     return hipLaunchKernel((const void*)merge_wide_kernel, dim3(rows * q_len_max * heads), dim3(kWideThreads), args,
                            0, st);
   dim3 grid(rows * q_len_max * ((heads + kW - 1) / kW));
-  return hipLaunchKernel((const void*)merge_kernel, grid, dim3(kBlockThreads), args, 0, st);
+  const void* fn = max_splits <= 2   ? (const void*)merge_kernel<2>
+                   : max_splits <= 4 ? (const void*)merge_kernel<4>
+                                     : (const void*)merge_kernel<8>;
+  return hipLaunchKernel(fn, grid, dim3(kBlockThreads), args, 0, st);
 }
 
 hipError_t launch_zero(uint32_t* p, int32_t words, hipStream_t st) {
