@@ -111,8 +111,15 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeArgs a) {
   const int64_t stride = (int64_t)a.q_len_max * a.heads;   // partial slots are consecutive
   const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
   MergeState st{-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  for (int k0 = 0; k0 < n; k0 += C)   // uniform over the block: n is the row's
-    merge_chunk<C>(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, k0, n, st);
+  // (uniform over the block: n is the row's) A row within one chunk takes it
+  // outside the loop: the chunk at the constant offset 0 compiled inside the
+  // loop made the verify merge 40% slower.
+  if (n <= C) {
+    merge_chunk<C>(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, 0, n, st);
+  } else {
+    for (int k0 = 0; k0 < n; k0 += C)
+      merge_chunk<C>(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, k0, n, st);
+  }
   store_merged(a, (int64_t)(q0 + i) * a.heads + h, lane, st);
 }
 
@@ -141,8 +148,13 @@ __global__ __launch_bounds__(kWideThreads) void merge_wide_kernel(MergeArgs a) {
   const int64_t stride = (int64_t)a.q_len_max * a.heads;   // partial slots are consecutive
   const int64_t base = ((int64_t)part0 * a.q_len_max + i) * a.heads + h;
   MergeState st{-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  for (int k0 = kChunkWide * w; k0 < n; k0 += kChunkWide * kW)
-    merge_chunk<kChunkWide>(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, k0, n, st);
+  // (the first chunk outside the loop, as in merge_kernel: 11% faster on long
+  // context)
+  if (kChunkWide * w < n) {
+    merge_chunk<kChunkWide>(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, kChunkWide * w, n, st);
+    for (int k0 = kChunkWide * (w + kW); k0 < n; k0 += kChunkWide * kW)
+      merge_chunk<kChunkWide>(a.ws_o + base * kDV + lane * 8, a.ws_lse + base, stride, k0, n, st);
+  }
   acc_s[w][0][lane] = st.acc0;
   acc_s[w][1][lane] = st.acc1;
   if (lane == 0) {

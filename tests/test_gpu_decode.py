@@ -216,6 +216,19 @@ def test_forced_split_matches_unsplit(lib):
     assert np.abs(O1 - O2).max() <= 1e-2 * np.abs(O1).max()
 
 
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 8, 9, 16, 17, 40])
+def test_merge_split_counts(lib, n):
+    """Every chunk size of the split merge (2, 4 and 8 splits per round trip,
+    one or two chunks) and the wide merge beyond 16 splits: a UNIFORM plan
+    cuts each row of 256 n keys into n splits of 256."""
+    case = make_case(300 + n, [256 * n, 256 * n - 77], heads=16, q_len=2, q_dtype=BF16, kv_dtype=BF16,
+                     causal=True, pool_slots=max(4096, 600 * n))
+    O, LSE, words = run_gpu(case, mode=1, num_cus=256)
+    info = unpack_plan(words)
+    assert info["S"] == 2 * n          # n splits in each of the two rows
+    assert_parity(case, O, LSE)
+
+
 def test_mask_discrimination(lib):
     """The kernel runs the mask that was asked for: close to the right-mask
     reference, far from the wrong one (the check the non-causal draft page
