@@ -12,7 +12,8 @@
 //
 // Every wave does all three stages of the attention:
 //   QK        wave w owns query rows 32w..32w+31 and keeps their queries (576
-//             dims) in registers. For tile t it computes S^T = K Q^T (keys
+//             dims) in registers, staged at the head of each item through LDS
+//             by the tile loader. For tile t it computes S^T = K Q^T (keys
 //             are the MFMA M side, the 576-dim latent the contraction): on
 //             v_mfma_f32_32x32x16_bf16 for bf16 KV, on the fp8
 //             v_mfma_f32_32x32x64_f8f6f4 for fp8 KV (fp8 Q as is; bf16 Q
