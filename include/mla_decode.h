@@ -181,6 +181,9 @@ MLA_API int32_t mla_decode_workspace_init(const int32_t* plan, void* workspace,
  *   kv_pool    device, [num_slots, 576] of kv_dtype, 16-byte aligned
  *   kv_scale   device float scalar, or NULL for 1.0
  *   qo_indptr  device [rows+1];  kv_indptr device [rows+1];  kv_indices device
+ *              (q, kv_indices, o and lse are never NULL; when they have no
+ *              entries -- every query block or every row empty -- any valid
+ *              device address will do, since nothing there is read or written)
  *   plan_host  host words from mla_decode_plan; plan_dev a device copy of the
  *              same words (the caller uploads it, e.g. from pinned memory)
  *   causal     0 = non-causal, 1 = causal on positions (see top of file)

@@ -151,6 +151,23 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
+_EMPTY_STANDIN = {}
+
+
+def _ptr_any(t) -> int:
+    """The address of a device tensor that may have no elements. An empty
+    tensor has no storage (address 0), while the library wants a valid
+    address even for an argument it will not touch: every query block or
+    index list empty. A small aligned buffer per device stands in for it."""
+    if t.numel() > 0:
+        return int(t.data_ptr())
+    import torch
+    key = str(t.device)
+    if key not in _EMPTY_STANDIN:
+        _EMPTY_STANDIN[key] = torch.zeros(64, dtype=torch.int32, device=t.device)
+    return int(_EMPTY_STANDIN[key].data_ptr())
+
+
 def _stream_handle(stream) -> Optional[int]:
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -231,10 +248,10 @@ def decode_fwd(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, kv_i
     ph = _host_i32(plan_host)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().mla_decode_fwd(
-        _ptr(q), _dtype_code(q_dtype), _ptr(q_scale), _ptr(kv_pool), _dtype_code(kv_dtype),
-        _ptr(kv_scale), int(kv_pool.shape[0]), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices),
+        _ptr_any(q), _dtype_code(q_dtype), _ptr(q_scale), _ptr(kv_pool), _dtype_code(kv_dtype),
+        _ptr(kv_scale), int(kv_pool.shape[0]), _ptr(qo_indptr), _ptr(kv_indptr), _ptr_any(kv_indices),
         ph.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(plan_dev), rows, heads, q_len_max,
-        1 if causal else 0, float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
+        1 if causal else 0, float(softmax_scale), _ptr_any(o), _ptr_any(lse), _ptr(workspace), ws_bytes,
         _stream_handle(stream))
     _check(st)
 
@@ -253,10 +270,10 @@ def decode_fwd_noalloc(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indp
                           kv_indices, rows, heads, q_len_max, o, lse)
     ph = _host_i32(plan_host)
     st = load_library().mla_decode_fwd_noalloc(
-        _ptr(q), _dtype_code(q_dtype), _ptr(q_scale), _ptr(kv_pool), _dtype_code(kv_dtype),
-        _ptr(kv_scale), int(kv_pool.shape[0]), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices),
+        _ptr_any(q), _dtype_code(q_dtype), _ptr(q_scale), _ptr(kv_pool), _dtype_code(kv_dtype),
+        _ptr(kv_scale), int(kv_pool.shape[0]), _ptr(qo_indptr), _ptr(kv_indptr), _ptr_any(kv_indices),
         ph.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(plan_dev), rows, heads, q_len_max,
-        1 if causal else 0, float(softmax_scale), _ptr(o), _ptr(lse), _stream_handle(stream))
+        1 if causal else 0, float(softmax_scale), _ptr_any(o), _ptr_any(lse), _stream_handle(stream))
     _check(st)
 
 
@@ -275,10 +292,10 @@ def decode_fwd_dcp(q, q_dtype, q_scale, kv_pool, kv_dtype, kv_scale, qo_indptr, 
     ph = _host_i32(plan_host)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().mla_decode_fwd_dcp(
-        _ptr(q), _dtype_code(q_dtype), _ptr(q_scale), _ptr(kv_pool), _dtype_code(kv_dtype),
-        _ptr(kv_scale), int(kv_pool.shape[0]), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices),
+        _ptr_any(q), _dtype_code(q_dtype), _ptr(q_scale), _ptr(kv_pool), _dtype_code(kv_dtype),
+        _ptr(kv_scale), int(kv_pool.shape[0]), _ptr(qo_indptr), _ptr(kv_indptr), _ptr_any(kv_indices),
         ph.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(plan_dev), rows, heads, q_len_max,
-        1 if causal else 0, float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
+        1 if causal else 0, float(softmax_scale), _ptr_any(o), _ptr_any(lse), _ptr(workspace), ws_bytes,
         int(dcp_world), int(dcp_rank), _ptr(kv_len_global), _stream_handle(stream))
     _check(st)
 

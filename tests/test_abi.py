@@ -278,3 +278,18 @@ def test_header_documents_the_plan_constants(lib):
     words = lib_mod.plan([100, 7], 16, 2, "bf16")
     assert words[0] == const["kPlanMagic"] and words[1] == const["kPlanVersion"]
     assert words[8] == const["kMUnit"] and words[10] == const["kNMax"] and words[18] == const["kHeaderWords"]
+
+
+def test_binding_passes_an_address_for_empty_tensors():
+    """An empty tensor has no storage (address 0); the binding hands the
+    library a valid stand-in address for it instead, and the tensor's own
+    address otherwise."""
+    import torch
+    import paged_mla_decode_02_amd as mla
+    empty = torch.empty((0, 4), dtype=torch.int32)
+    assert empty.data_ptr() == 0
+    a = mla._ptr_any(empty)
+    assert a != 0 and a % 16 == 0
+    assert mla._ptr_any(torch.empty(0, dtype=torch.bfloat16)) == a   # one stand-in per device
+    full = torch.zeros(8, dtype=torch.int32)
+    assert mla._ptr_any(full) == full.data_ptr()

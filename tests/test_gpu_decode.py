@@ -229,6 +229,52 @@ def test_merge_split_counts(lib, n):
     assert_parity(case, O, LSE)
 
 
+def _random_shape(k):
+    """Seeded random shape k: heads, block length, dtypes, mask, row lengths
+    (with empty rows), ragged query blocks, plan mode and CU count."""
+    rng = np.random.default_rng(7000 + k)
+    H = int(rng.choice([1, 3, 8, 16, 20, 33, 64, 96, 127, 128]))
+    q = int(rng.integers(1, 17))
+    qd, kd = [(BF16, BF16), (BF16, FP8), (FP8, FP8), (FP8, BF16)][k % 4]
+    rows = int(rng.integers(1, 6))
+    lens = [int(x) for x in rng.integers(0, 1500, rows)]
+    if rng.random() < 0.3:
+        lens[int(rng.integers(rows))] = 0
+    q_lens = [int(x) for x in rng.integers(0, q + 1, rows)] if rng.random() < 0.5 else None
+    mode = int(rng.choice([0, 1, 2]))
+    if kd == FP8 and rng.random() < 0.4:
+        mode |= 0x200
+    C = int(rng.choice([1, 4, 32, 256]))
+    return H, q, qd, kd, bool(rng.random() < 0.6), lens, q_lens, mode, C
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_random_shapes(lib, k):
+    """A seeded sweep of shapes no other test picks by hand, each compared with
+    the oracle on every row."""
+    H, q, qd, kd, causal, lens, q_lens, mode, C = _random_shape(k)
+    case = make_case(8000 + k, lens, heads=H, q_len=q, q_dtype=qd, kv_dtype=kd, causal=causal,
+                     pool_slots=max(4096, 2 * sum(lens)), q_lens=q_lens)
+    O, LSE, words = run_gpu(case, mode=mode, num_cus=C)
+    print(f"random shape {k}: H={H} q={q} {qd}/{kd} causal={causal} lens={lens} q_lens={q_lens} "
+          f"mode={mode:#x} C={C} S={unpack_plan(words)['S']}")
+    assert_parity(case, O, LSE)
+
+
+def test_all_empty_inputs(lib):
+    """Every row without keys (an empty index list), and every query block
+    empty (no query tokens at all): the first gives O = 0 and LSE = -inf for
+    every token, the second writes nothing."""
+    case = make_case(95, [0, 0, 0], heads=16, q_len=4, q_dtype=BF16, kv_dtype=FP8, causal=True,
+                     pool_slots=4096)
+    O, LSE, _ = run_gpu(case, mode=1, num_cus=8)
+    assert (O == 0).all() and np.isneginf(LSE).all()
+    case = make_case(96, [100, 0, 300], heads=16, q_len=4, q_dtype=BF16, kv_dtype=BF16, causal=True,
+                     pool_slots=4096, q_lens=[0, 0, 0])
+    O, LSE, _ = run_gpu(case, mode=2, num_cus=8)
+    assert O.shape[0] == 0 and LSE.shape[0] == 0
+
+
 def test_mask_discrimination(lib):
     """The kernel runs the mask that was asked for: close to the right-mask
     reference, far from the wrong one (the check the non-causal draft page
