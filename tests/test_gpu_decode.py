@@ -248,7 +248,7 @@ def _random_shape(k):
     return H, q, qd, kd, bool(rng.random() < 0.6), lens, q_lens, mode, C
 
 
-@pytest.mark.parametrize("k", range(24))
+@pytest.mark.parametrize("k", range(48))
 def test_random_shapes(lib, k):
     """A seeded sweep of shapes no other test picks by hand, each compared with
     the oracle on every row."""
