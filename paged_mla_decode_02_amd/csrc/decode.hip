@@ -241,7 +241,7 @@ template <bool KV_FP8> struct TileDma {
       t.lo = (uint32_t)row;
       t.hi = (uint32_t)(row >> 32);
       const int j = kRopeRows * w + (lane >> 3);
-      const int slot = __shfl(slot_lane, j & 31, 64);
+      const int slot = bpermute(j & 31, slot_lane);
       t.rope = kv + (int64_t)(uint32_t)slot * (2 * kDLat) + kMainRow + (((lane & 7) ^ swz_rope(j)) << 4);
     } else {
       t.slot_lane = slot_lane;
@@ -267,12 +267,12 @@ template <bool KV_FP8> struct TileDma {
       if (i < kMainOps) {
         const int k = kWaves * i + w;            // rows 2k (lanes 0-31) and 2k + 1
         const int row = 2 * k + (lane >> 5);
-        const int slot = __shfl(slot_lane, row, 64);
+        const int slot = bpermute(row, slot_lane);
         dma16_vaddr(kv + (int64_t)slot * kDLat + (((lane & 31) ^ swz_f8(row)) << 4),
                     lds0 + main_off + k * 2 * kF8MainRow);
       } else {
         const int j = kRopeRows * w + ((lane & 31) >> 2);
-        const int slot = __shfl(slot_lane, j, 64);
+        const int slot = bpermute(j, slot_lane);
         dma16_vaddr(kv + (int64_t)slot * kDLat + kF8MainRow + (((lane & 3) ^ swz_f8_rope(j)) << 4),
                     lds0 + rope_off + w * 1024);
       }
@@ -958,13 +958,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
   using Dma = TileDma<KV_FP8>;
   constexpr int QKM = !KV_FP8 ? 0 : Q_FP8 ? 1 : 2;   // QK products: bf16, fp8, split bf16 Q
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.heads;
   const unsigned char* kv = (const unsigned char*)a.kv;
   const float q_scale = a.q_scale ? *a.q_scale : 1.0f;
   const float kv_scale = a.kv_scale ? *a.kv_scale : 1.0f;
-  const float score_c = a.score_scale_log2 * q_scale * kv_scale;
+  // (wave-uniform: kept in a scalar register, never spilled to scratch)
+  const float score_c = __builtin_bit_cast(
+      float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a.score_scale_log2 * q_scale * kv_scale)));
 
   const int g = blockIdx.x;
   const int it0 = ldc(a.plan, a.off_work_indptr + g), it1 = ldc(a.plan, a.off_work_indptr + g + 1);
@@ -994,7 +996,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     // copy of the lane id: hoisted out of the item loop they would be spilled,
     // and each reload from scratch is a vector-memory access whose wait also
     // waits for the previous item's O stores.
-    const int ilane = opaque(lane);
+    const int ilane = lane_now();
     const int mr = m * kRows + 32 * w + (ilane & 31);
     const bool row_ok = mr < M;
     // (rows past the block's end get a token index past q_b; nothing of
@@ -1039,7 +1041,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
                               QStage<Q_FP8>::main(q), QStage<Q_FP8>::rope(q), w, ilane);
         wait_vm<0>();
         __syncthreads();   // every wave's query rows and slot lists have landed
-        const int ql = opaque(lane);
+        const int ql = lane_now();
         if constexpr (QKM == 0) {
           const LaneAddr la_q = lane_addr<false>(ql, w);
 #pragma unroll
@@ -1088,16 +1090,21 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         // them already), then the loads of tiles 0 and 1, each preceded by
         // one slot-list load so that every later wait count has the same
         // form; tile 0 lands.
+        // The lane-derived addresses here are computed where they are used
+        // (from an opaque lane id): shared with the item head's they would be
+        // kept live across the query staging and spilled, and a reload's wait
+        // would also wait for the tile loads issued before it.
         if (!kStageQ || pass > 0) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, w, ilane);
+          for (int t = 0; t < 4; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, w, lane_now());
           wait_vm<0>();
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          issue_slots(a.kv_indices, kv0, begin, end, t + 2, smem, w, ilane);
+          const int plane = lane_now();
+          issue_slots(a.kv_indices, kv0, begin, end, t + 2, smem, w, plane);
           if (t < ntiles)
-            Dma::all(kv, read_slots(smem, t, w, ilane), a.max_slot, smem, LY::main(t), LY::rope(t), w, ilane);
+            Dma::all(kv, read_slots(smem, t, w, plane), a.max_slot, smem, LY::main(t), LY::rope(t), w, plane);
         }
         if constexpr (QKM == 2) {
           if (pass == 0) {
@@ -1128,14 +1135,19 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         auto run_step = [&](int t, auto QKc, auto PREVc, auto DMAc, auto FASTc) {
           constexpr bool DO_QK = decltype(QKc)::value, PREV = decltype(PREVc)::value;
           constexpr bool DO_DMA = decltype(DMAc)::value, FAST = decltype(FASTc)::value;
-          const int dlane = opaque(lane);
+          const int dlane = lane_now();
+          // (opaque: no per-loop copies of this base derived up front and
+          // spilled. An opaque copy is an assembly statement, which memory
+          // accesses are not moved across: it comes before the slot-list
+          // read below, which the scheduler then interleaves with the first
+          // K-fragment reads.)
+          const int lim_old = opaque(key_last) - (begin + (t - 1) * kNT + 4 * (dlane >> 5));
           issue_slots(a.kv_indices, kv0, begin, end, t + 4, smem, w, dlane);
           const TileSrc<KV_FP8> src = Dma::src(kv, DO_DMA ? read_slots(smem, t + 2, w, dlane) : 0, a.max_slot, w, dlane);
           const int dm = LY::main(t + 2), dr = LY::rope(t + 2);
           auto dma = [&](int i) {
             Dma::op(i, kv, src, lds_addr_of(smem), dm, dr, w, dlane);
           };
-          const int lim_old = key_last - (begin + (t - 1) * kNT + 4 * (dlane >> 5));
           const LaneAddr la_s = lane_addr<KV_FP8>(dlane, w);
           if constexpr (PV8) {
             // PV of tiles tA = (t - 1) & ~1 and tA + 1 once both have their
@@ -1178,53 +1190,60 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       // Did any row of the item overflow its reference? (uniform) One
       // barrier publishes the waves' flags and the rows' O denominators for
       // the epilogue; a pass 1 rewrites both before they are read again.
-      if (lane == 0) lds_store(smem, kOffMisc + 4 * w, (uint32_t)(__ballot(rs.over) != 0));
+      if (lane_now() == 0) lds_store(smem, kOffMisc + 4 * w, (uint32_t)(__ballot(rs.over) != 0));
       {
         // (cross-lane sums run on every lane, outside the lane < 32 branch)
         const float l_o = half_sum(PV8 ? rs.l_round : rs.l_part);   // O's denominator
-        const int el = opaque(lane);
+        const int el = lane_now();
         if (el < 32) lds_store(smem, kOffL + (w * 32 + el) * 4, l_o);
       }
       __syncthreads();
       const u32x4 ov = lds_load<u32x4>(smem, kOffMisc);
-      if ((ov[0] | ov[1] | ov[2] | ov[3]) == 0u) break;
+      if (pass == 1 || (ov[0] | ov[1] | ov[2] | ov[3]) == 0u) {
+        // O normalized and staged here, in the block that produced the
+        // accumulators: staged after the loop, they would be live across its
+        // exit, where the register allocator reshuffled them and spilled a
+        // dozen to scratch (each reload a wait of its own in the epilogue).
+        // O leaves through LDS so that the stores are whole rows: the item's
+        // query rows r = m 128 .. m 128 + 127 are consecutive rows of O (index
+        // q0 H + r) and of its partial slot (index (part q_len_max) H + r).
+        // All 128 rows are staged at once in bf16 (1 KB per row, 128 KB of
+        // the tile region), 16-byte chunk c of row r at c ^ (r & 15).
+        const int el = lane_now();
+        const int hh = el >> 5;
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb) {
+          const int r = 32 * rb + (el & 31);
+          const float l = lds_load<float>(smem, kOffL + r * 4);
+          const float inv = l > 0.f ? kv_scale / l : 0.f;
+#pragma unroll
+          for (int ct = 0; ct < kColTiles; ++ct)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const f32x16& v = oacc[rb][ct];
+              // columns 4 c' .. 4 c' + 3 with c' = 32 w + 8 ct + 2 gq + hh: half hh
+              // of 16-byte chunk 16 w + 4 ct + gq
+              const int c = 16 * w + 4 * ct + gq;
+              const bf16x4 x{(__bf16)(v[4 * gq] * inv), (__bf16)(v[4 * gq + 1] * inv),
+                             (__bf16)(v[4 * gq + 2] * inv), (__bf16)(v[4 * gq + 3] * inv)};
+              lds_store(smem, r * (kDV * 2) + ((c ^ (r & 15)) << 4) + 8 * hh, x);
+            }
+        }
+        break;
+      }
       rs.m_ref = rs.m_seen;   // pass 1: no tile can exceed the true max
     }
 
-    // Epilogue: O normalized and written, then the LSE (stored last, so that
-    // no wait inside the epilogue waits for its store).
+    // Epilogue: the staged O written, then the LSE (stored last, so that no
+    // wait inside the epilogue waits for its store).
     const float l_row = half_sum(rs.l_part);
     const float lse = l_row > 0.f ? (rs.m_ref + __log2f(l_row)) * kLn2 : -INFINITY;
-    // O leaves through LDS so that the stores are whole rows: the item's
-    // query rows r = m 128 .. m 128 + 127 are consecutive rows of O (index
-    // q0 H + r) and of its partial slot (index (part q_len_max) H + r). All
-    // 128 rows are staged at once in bf16 (1 KB per row, 128 KB of the tile
-    // region), 16-byte chunk c of row r at c ^ (r & 15).
     {
       // Opaque copies: the addresses below are recomputed here rather than
       // hoisted out of the item loop and kept live across it.
-      const int el = opaque(lane);
-      const int hh = el >> 5;
+      const int el = lane_now();
       const int64_t orow0 = part < 0 ? (int64_t)q0 * H + (int64_t)m * kRows
                                      : (int64_t)part * a.q_len_max * H + (int64_t)m * kRows;
-#pragma unroll
-      for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const int r = 32 * rb + (el & 31);
-        const float l = lds_load<float>(smem, kOffL + r * 4);
-        const float inv = l > 0.f ? kv_scale / l : 0.f;
-#pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const f32x16& v = oacc[rb][ct];
-            // columns 4 c' .. 4 c' + 3 with c' = 32 w + 8 ct + 2 gq + hh: half hh
-            // of 16-byte chunk 16 w + 4 ct + gq
-            const int c = 16 * w + 4 * ct + gq;
-            const bf16x4 x{(__bf16)(v[4 * gq] * inv), (__bf16)(v[4 * gq + 1] * inv),
-                           (__bf16)(v[4 * gq + 2] * inv), (__bf16)(v[4 * gq + 3] * inv)};
-            lds_store(smem, r * (kDV * 2) + ((c ^ (r & 15)) << 4) + 8 * hh, x);
-          }
-      }
       __syncthreads();
       const int nrows = min(kRows, M - m * kRows);   // rows of the item inside the block
       uint16_t* const dst0 = part < 0 ? a.o : a.ws_o;   // bf16 O, or the split's partial O

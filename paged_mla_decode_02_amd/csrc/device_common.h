@@ -58,6 +58,21 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
+// The lane id, computed afresh where it is used (two VALU ops the compiler
+// can neither hoist nor share): a lane id kept live across the item loop is
+// a spill candidate, and a reload's wait there also waits for every tile
+// load in flight.
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// v of lane src (0..63) of the wave; no lane id of its own (unlike __shfl).
+__device__ __forceinline__ int bpermute(int src, int v) {
+  return __builtin_amdgcn_ds_bpermute(src << 2, v);
+}
+
 // The same for a wave-uniform value kept in a scalar register.
 __device__ __forceinline__ int opaque_s(int v) {
   asm volatile("" : "+s"(v));
@@ -124,10 +139,17 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int d = 8; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
   return v;
 }
+// Minimum over the wave without a lane id: lanes l ^ 16 .. l ^ 1 inside each
+// 32-lane half by ds_swizzle (bit mode: offset = and 0x1f | xor << 10), then
+// the two halves by v_permlane32_swap.
 __device__ __forceinline__ int wave_min_i32(int v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, 64));
-  return v;
+  v = min(v, __builtin_amdgcn_ds_swizzle(v, 0x1f | (16 << 10)));
+  v = min(v, __builtin_amdgcn_ds_swizzle(v, 0x1f | (8 << 10)));
+  v = min(v, __builtin_amdgcn_ds_swizzle(v, 0x1f | (4 << 10)));
+  v = min(v, __builtin_amdgcn_ds_swizzle(v, 0x1f | (2 << 10)));
+  v = min(v, __builtin_amdgcn_ds_swizzle(v, 0x1f | (1 << 10)));
+  const auto a = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return min((int)a[0], (int)a[1]);
 }
 __device__ __forceinline__ float wave_sum(float v) {
   v = group_sum(v);
