@@ -385,30 +385,14 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)__float_as_uint(a), false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
 }
-// 8 bf16 elements (4 dwords of 2; times `scale` = 2^A, `inv` = 2^-A) -> 2
-// dwords of hi and 2 of lo. hi comes straight from the packed bf16 pairs:
-// v_cvt_scalef32_pk_fp8_bf16 rounds x / inv = x 2^A to e4m3 (nearest even),
-// which a host model of the instruction confirmed; lo = fp8(x 2^A - hi), the
-// product x 2^A being exact.
+// bf16 elements in packed pairs -> fp8 hi and lo. hi comes straight from the
+// packed bf16 pairs: v_cvt_scalef32_pk_fp8_bf16 rounds x / inv = x 2^A to
+// e4m3 (nearest even), which a host model of the instruction confirmed;
+// lo = fp8(x 2^A - hi), the product x 2^A being exact.
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef short i16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ void split_fp8x8(const uint32_t* w, float scale, float inv, uint32_t* hi, uint32_t* lo) {
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const uint32_t w0 = w[2 * q], w1 = w[2 * q + 1];
-    i16x2v hv = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(i16x2v, w0), __builtin_bit_cast(bf16x2v, w0),
-                                                          inv, false);
-    hv = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hv, __builtin_bit_cast(bf16x2v, w1), inv, true);
-    const uint32_t h = __builtin_bit_cast(uint32_t, hv);
-    const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, false);
-    const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, true);
-    hi[q] = h;
-    lo[q] = pack_fp8x4(__builtin_fmaf(bf16_lo(w0), scale, -f01[0]), __builtin_fmaf(bf16_hi(w0), scale, -f01[1]),
-                       __builtin_fmaf(bf16_lo(w1), scale, -f23[0]), __builtin_fmaf(bf16_hi(w1), scale, -f23[1]));
-  }
-}
 // In place: q[2 p] and q[2 p + 1] hold the 32 bf16 elements of product p
 // (dims 64 p + 16 h .. +15, then 64 p + 32 + 16 h .. +15) and become its hi
 // and lo fp8 operands. The row's largest |x| is taken over both lane halves
@@ -430,16 +414,37 @@ __device__ __forceinline__ float split_q_rows(u32x8 (&q)[2 * kKSteps8]) {
   const float scale = ldexpf(1.0f, 8 - ex), inv = ldexpf(1.0f, ex - 8);
 #pragma unroll
   for (int p = 0; p < kKSteps8; ++p) {
-    uint32_t hi[8], lo[8];
+    // Stage by stage over the product's 16 dwords (scheduling barriers
+    // between the stages), so that the dependent conversions of different
+    // dwords interleave instead of running as one chain per dword pair.
+    uint32_t w[16], hi[8], lo[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u32x8& v = q[2 * p + (u >> 1)];
-      const int d0 = 4 * (u & 1);
-      const uint32_t w4[4] = {v[d0], v[d0 + 1], v[d0 + 2], v[d0 + 3]};
-      split_fp8x8(w4, scale, inv, hi + 2 * u, lo + 2 * u);
+    for (int d = 0; d < 8; ++d) { w[d] = q[2 * p][d]; w[8 + d] = q[2 * p + 1][d]; }
+    i16x2v ha[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      ha[k] = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(i16x2v, w[2 * k]), __builtin_bit_cast(bf16x2v, w[2 * k]), inv, false);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      hi[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(ha[k], __builtin_bit_cast(bf16x2v, w[2 * k + 1]), inv, true));
+    __builtin_amdgcn_sched_barrier(0);
+    float r[32];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi[k], false);
+      const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi[k], true);
+      r[4 * k] = __builtin_fmaf(bf16_lo(w[2 * k]), scale, -f01[0]);
+      r[4 * k + 1] = __builtin_fmaf(bf16_hi(w[2 * k]), scale, -f01[1]);
+      r[4 * k + 2] = __builtin_fmaf(bf16_lo(w[2 * k + 1]), scale, -f23[0]);
+      r[4 * k + 3] = __builtin_fmaf(bf16_hi(w[2 * k + 1]), scale, -f23[1]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) lo[k] = pack_fp8x4(r[4 * k], r[4 * k + 1], r[4 * k + 2], r[4 * k + 3]);
     q[2 * p] = u32x8{hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]};
     q[2 * p + 1] = u32x8{lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]};
+    __builtin_amdgcn_sched_barrier(0);
   }
   return ldexpf(1.0f, ex - 8);
 }
