@@ -997,10 +997,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     const int ntiles = (end - begin + kNT - 1) / kNT;
 
     // ---- this wave's query rows: m 128 + 32 w + (lane & 31)
-    // Lane-derived values of the item head are recomputed from an opaque
-    // copy of the lane id: hoisted out of the item loop they would be spilled,
-    // and each reload from scratch is a vector-memory access whose wait also
-    // waits for the previous item's O stores.
+    // Lane-derived values are recomputed from a lane id computed afresh
+    // (lane_now): kept live across the item loop they would be spilled, and
+    // each reload from scratch is a vector-memory access whose wait also waits
+    // for every earlier load and store (the previous item's O stores, the
+    // tile loads in flight).
     const int ilane = lane_now();
     const int mr = m * kRows + 32 * w + (ilane & 31);
     const bool row_ok = mr < M;
@@ -1096,7 +1097,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         // one slot-list load so that every later wait count has the same
         // form; tile 0 lands.
         // The lane-derived addresses here are computed where they are used
-        // (from an opaque lane id): shared with the item head's they would be
+        // (from a fresh lane id): shared with the item head's they would be
         // kept live across the query staging and spilled, and a reload's wait
         // would also wait for the tile loads issued before it.
         if (!kStageQ || pass > 0) {
@@ -1244,8 +1245,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     const float l_row = half_sum(rs.l_part);
     const float lse = l_row > 0.f ? (rs.m_ref + __log2f(l_row)) * kLn2 : -INFINITY;
     {
-      // Opaque copies: the addresses below are recomputed here rather than
-      // hoisted out of the item loop and kept live across it.
+      // (a fresh lane id: the addresses below are computed here rather than
+      // hoisted out of the item loop and kept live across it)
       const int el = lane_now();
       const int64_t orow0 = part < 0 ? (int64_t)q0 * H + (int64_t)m * kRows
                                      : (int64_t)part * a.q_len_max * H + (int64_t)m * kRows;
