@@ -163,6 +163,15 @@ template <> struct QStage<true> {
   static __device__ __forceinline__ int rope(int q) { return 4 * kF8MainBytes + q * kF8RopeBytes; }
 };
 static_assert(kWaves * (kMainBytes + kRopeBytes) <= kOffL, "bf16 query staging below the row sums");
+// fp8 queries with fp8 KV (bf16 PV products): the staging region fits above
+// the tile ring (it overlaps only the P^T buffers, first written in step 1),
+// so tiles 0 and 1 load while the queries land.
+constexpr int kOffQAbove = kMainBufs * kF8MainBytes + kRopeBufs * kF8RopeBytes;
+struct QStageAbove {
+  static __device__ __forceinline__ int main(int q) { return kOffQAbove + QStage<true>::main(q); }
+  static __device__ __forceinline__ int rope(int q) { return kOffQAbove + QStage<true>::rope(q); }
+};
+static_assert(kOffQAbove + kWaves * (kF8MainBytes + kF8RopeBytes) <= kOffL, "fp8 query staging above the tiles");
 
 // LDS offsets of tile t's buffers.
 template <bool KV_FP8, bool PV8 = false> struct Layout;
@@ -1037,6 +1046,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     // (in the tile layout of the query dtype). The first slot lists of pass 0
     // go out first, so that their latency overlaps the staging.
     constexpr bool kStageQ = !(Q_FP8 && !KV_FP8);
+    // fp8 queries and KV without fp8 PV: staged above the tile ring, so pass
+    // 0's first tiles are issued before the queries are waited for.
+    constexpr bool kQAbove = QKM == 1 && !PV8;
+    using QS = std::conditional_t<kQAbove, QStageAbove, QStage<Q_FP8>>;
     if constexpr (kStageQ) {
       if (ntiles > 0) {
 #pragma unroll
@@ -1044,27 +1057,46 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
 #pragma unroll
         for (int q = 0; q < kWaves; ++q)
           TileDma<Q_FP8>::all(qblock, m * kRows + 32 * q + (ilane & 31), (uint32_t)(M - 1), smem,
-                              QStage<Q_FP8>::main(q), QStage<Q_FP8>::rope(q), w, ilane);
-        wait_vm<0>();
+                              QS::main(q), QS::rope(q), w, ilane);
+        if constexpr (kQAbove) {
+          // This wave's slot lists of tiles 0 and 1 have landed (two slot
+          // lists and the query loads may still be in flight); then the
+          // pass prologue's loads of tiles 0 and 1, in its order, and the
+          // queries land (those loads may still be in flight).
+          wait_vm<2 + kWaves * TileDma<Q_FP8>::n>();
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int plane = lane_now();
+            issue_slots(a.kv_indices, kv0, begin, end, t + 2, smem, w, plane);
+            if (t < ntiles)
+              Dma::all(kv, read_slots(smem, t, w, plane), a.max_slot, smem, LY::main(t), LY::rope(t), w, plane);
+          }
+          if (ntiles > 1) wait_vm<2 * (1 + Dma::n)>();
+          else wait_vm<2 + Dma::n>();
+        } else {
+          wait_vm<0>();
+        }
         __syncthreads();   // every wave's query rows and slot lists have landed
         const int ql = lane_now();
         if constexpr (QKM == 0) {
           const LaneAddr la_q = lane_addr<false>(ql, w);
 #pragma unroll
-          for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = k_frag(smem, la_q, QStage<false>::main(w), QStage<false>::rope(w), ks);
+          for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = k_frag(smem, la_q, QS::main(w), QS::rope(w), ks);
         } else if constexpr (QKM == 1) {
           const LaneAddr la_q = lane_addr<true>(ql, w);
 #pragma unroll
-          for (int p = 0; p < kKSteps8; ++p) qf[p] = k_prod_f8(smem, la_q, QStage<true>::main(w), QStage<true>::rope(w), p);
+          for (int p = 0; p < kKSteps8; ++p) qf[p] = k_prod_f8(smem, la_q, QS::main(w), QS::rope(w), p);
         } else {   // raw bf16 here; split once the item's first loads are out
           const bool keep = m * kRows + 32 * w + (ql & 31) < M;
 #pragma unroll
           for (int n = 0; n < 2 * kKSteps8; ++n) {
-            const u32x8 v = q_raw_bf16(smem, QStage<false>::main(w), QStage<false>::rope(w), ql, n);
+            const u32x8 v = q_raw_bf16(smem, QS::main(w), QS::rope(w), ql, n);
             qf[n] = keep ? v : u32x8{};
           }
         }
-        __syncthreads();   // the tile loads below rewrite the staging region
+        // the tile loads below rewrite the staging region (above the tile
+        // ring it is next written by the P^T of step 1, after step 0's barrier)
+        if constexpr (!kQAbove) __syncthreads();
       }
     } else {
       // (opaque: computed here rather than hoisted and spilled)
@@ -1105,12 +1137,14 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
           for (int t = 0; t < 4; ++t) issue_slots(a.kv_indices, kv0, begin, end, t, smem, w, lane_now());
           wait_vm<0>();
         }
+        if (!kQAbove || pass > 0) {   // (pass 0 above the ring: issued with the queries)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int plane = lane_now();
-          issue_slots(a.kv_indices, kv0, begin, end, t + 2, smem, w, plane);
-          if (t < ntiles)
-            Dma::all(kv, read_slots(smem, t, w, plane), a.max_slot, smem, LY::main(t), LY::rope(t), w, plane);
+          for (int t = 0; t < 2; ++t) {
+            const int plane = lane_now();
+            issue_slots(a.kv_indices, kv0, begin, end, t + 2, smem, w, plane);
+            if (t < ntiles)
+              Dma::all(kv, read_slots(smem, t, w, plane), a.max_slot, smem, LY::main(t), LY::rope(t), w, plane);
+          }
         }
         if constexpr (QKM == 2) {
           if (pass == 0) {
