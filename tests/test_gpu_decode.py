@@ -229,6 +229,22 @@ def test_merge_split_counts(lib, n):
     assert_parity(case, O, LSE)
 
 
+@pytest.mark.parametrize("qd,kd,mode", [(BF16, BF16, 1), (BF16, FP8, 1), (FP8, FP8, 1), (FP8, BF16, 1),
+                                         (BF16, FP8, 0x201), (FP8, FP8, 0x201)],
+                         ids=["bf16-bf16", "bf16-fp8", "fp8-fp8", "fp8-bf16", "bf16-fp8-pv8", "fp8-fp8-pv8"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_one_and_two_tile_items(lib, qd, kd, mode, causal):
+    """Items of one, two and three 32-key tiles (the prologue's one-tile and
+    two-tile wait counts, and the last-step paths), for every dtype pair and
+    both masks: rows of 1 .. 96 keys, one split each."""
+    lens = [1, 5, 31, 32, 33, 63, 64, 65, 96]
+    case = make_case(9100 + 7 * len(qd) + len(kd) + (mode >> 9) + 2 * causal, lens, heads=16, q_len=4,
+                     q_dtype=qd, kv_dtype=kd, causal=causal, pool_slots=4096)
+    O, LSE, words = run_gpu(case, mode=mode, num_cus=1)
+    assert unpack_plan(words)["S"] == len(lens)
+    assert_parity(case, O, LSE)
+
+
 def _random_shape(k):
     """Seeded random shape k: heads, block length, dtypes, mask, row lengths
     (with empty rows), ragged query blocks, plan mode and CU count."""
