@@ -973,7 +973,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
   constexpr int QKM = !KV_FP8 ? 0 : Q_FP8 ? 1 : 2;   // QK products: bf16, fp8, split bf16 Q
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w_k = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.heads;
   const unsigned char* kv = (const unsigned char*)a.kv;
   const float q_scale = a.q_scale ? *a.q_scale : 1.0f;
@@ -985,6 +985,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
   const int g = blockIdx.x;
   const int it0 = ldc(a.plan, a.off_work_indptr + g), it1 = ldc(a.plan, a.off_work_indptr + g + 1);
   for (int it = it0; it < it1; ++it) {
+    // An opaque copy of the wave index: the LDS offsets and addresses derived
+    // from it are computed in the item instead of being hoisted out of the
+    // item loop into scalar registers, which the compiler then spilled.
+    const int w = opaque_s(w_k);
     const int s = ldc(a.plan, a.off_item_split + it);
     const int m = ldc(a.plan, a.off_item_m + it);
     const int b = ldc(a.plan, a.off_split_row + s);
