@@ -1255,13 +1255,20 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
         // the tile region), 16-byte chunk c of row r at c ^ (r & 15).
         const int el = lane_now();
         const int hh = el >> 5;
+        // (column tiles outer: the register allocator then permutes and
+        // spills fewer of the accumulators here)
+        float inv_rb[kRowBlocks];
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb) {
-          const int r = 32 * rb + (el & 31);
-          const float l = lds_load<float>(smem, kOffL + r * 4);
-          const float inv = l > 0.f ? kv_scale / l : 0.f;
+          const float l = lds_load<float>(smem, kOffL + (32 * rb + (el & 31)) * 4);
+          inv_rb[rb] = l > 0.f ? kv_scale / l : 0.f;
+        }
 #pragma unroll
-          for (int ct = 0; ct < kColTiles; ++ct)
+        for (int ct = 0; ct < kColTiles; ++ct) {
+#pragma unroll
+          for (int rb = 0; rb < kRowBlocks; ++rb) {
+            const int r = 32 * rb + (el & 31);
+            const float inv = inv_rb[rb];
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
               const f32x16& v = oacc[rb][ct];
@@ -1272,6 +1279,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
                              (__bf16)(v[4 * gq + 2] * inv), (__bf16)(v[4 * gq + 3] * inv)};
               lds_store(smem, r * (kDV * 2) + ((c ^ (r & 15)) << 4) + 8 * hh, x);
             }
+          }
         }
         break;
       }
