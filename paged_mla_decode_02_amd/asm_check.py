@@ -175,3 +175,43 @@ def check_scratch_in_step_loops(asm: str):
             if c.startswith("scratch_") and loop_of[i] in mfma_loops:
                 bad.append(f"{name}: {i}: {c}")
     return bad
+
+
+_DECODE_FLAGS = re.compile(r"decode_kernelILb([01])ELb([01])ELb([01])ELb([01])E")
+
+
+def check_waits_behind_tile_loads(asm: str):
+    """Return the vector-memory waits the compiler inserted (s_waitcnt vmcnt
+    outside inline assembly) while direct-to-LDS loads may be in flight: after
+    a global_load_lds with no hand-written vmcnt(0) in between, in program
+    order. The kernel counts its tile and query loads with waits of its own;
+    a wait the compiler adds is for a spill reload or another vector load,
+    and since the vector-memory counter is in order it also waits for every
+    tile load issued before that load. Checked in the default decode kernels
+    (no in-kernel merge, no fp8 PV products); the opt-in variants still have
+    such waits in their item heads."""
+    bad = []
+    for name, body in _kernel_bodies(asm):
+        m = _DECODE_FLAGS.search(name)
+        if not m or m.group(3) == "1" or m.group(4) == "1":
+            continue
+        in_asm, pending = False, False
+        for i, l in enumerate(body):
+            if ";;#ASMSTART" in l:
+                in_asm = True
+                continue
+            if ";;#ASMEND" in l:
+                in_asm = False
+                continue
+            c = l.split(";", 1)[0].strip()
+            if not c:
+                continue
+            if c.startswith("global_load_lds"):
+                pending = True
+            elif c.startswith("s_waitcnt") and "vmcnt" in c:
+                if in_asm:
+                    if re.search(r"vmcnt\(0\)", c):
+                        pending = False
+                elif pending:
+                    bad.append(f"{name}: {i}: {c}")
+    return bad

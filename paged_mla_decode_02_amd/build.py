@@ -78,7 +78,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
 def _check_decode_asm(path):
     sys.path.insert(0, PKG)
     try:
-        from asm_check import check_m0, check_qk_chains, check_scratch_in_step_loops, check_valu_to_mfma
+        from asm_check import (check_m0, check_qk_chains, check_scratch_in_step_loops, check_valu_to_mfma,
+                               check_waits_behind_tile_loads)
     finally:
         sys.path.pop(0)
     with open(path) as f:
@@ -99,6 +100,10 @@ def _check_decode_asm(path):
     if spills:
         raise RuntimeError(f"decode.hip: a spill access sits inside a per-tile step loop "
                            f"(offending lines of {path}):\n" + "\n".join(spills[:20]))
+    waits = check_waits_behind_tile_loads(text)
+    if waits:
+        raise RuntimeError(f"decode.hip: the compiler waits for vector memory while tile loads are in flight "
+                           f"(a spill reload or another load; offending lines of {path}):\n" + "\n".join(waits[:20]))
 
 
 def _wait(item, verbose):

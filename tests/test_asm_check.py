@@ -2,8 +2,9 @@
 hand-written instruction sequences: the inline-assembly QK accumulator chains
 (nothing may touch an open chain's registers between its links), the
 VALU -> assembly-MFMA operand hazard (the compiler inserts no wait states for
-inline assembly), M0 used only by the direct-to-LDS load sequences, and no
-spill reload inside a per-tile step loop."""
+inline assembly), M0 used only by the direct-to-LDS load sequences, no
+spill reload inside a per-tile step loop, and no compiler-inserted
+vector-memory wait while tile loads are in flight."""
 import os
 import sys
 
@@ -11,7 +12,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, os.path.join(ROOT, "paged_mla_decode_02_amd"))
-from asm_check import check_m0, check_qk_chains, check_scratch_in_step_loops, check_valu_to_mfma  # noqa: E402
+from asm_check import (check_m0, check_qk_chains, check_scratch_in_step_loops, check_valu_to_mfma,  # noqa: E402
+                       check_waits_behind_tile_loads)
 
 BF = "v_mfma_f32_32x32x16_bf16"
 F8 = "v_mfma_f32_32x32x64_f8f6f4"
@@ -109,6 +111,26 @@ def test_scratch_in_step_loop_is_flagged():
     assert len(check_scratch_in_step_loops("\n".join(kernel(plain)))) == 1
 
 
+def test_compiler_wait_behind_tile_loads_is_flagged():
+    def decode(flags, body):
+        name = f"_ZN3mla12_GLOBAL__N_113decode_kernelI{flags}EEvNS_10DecodeArgsE"
+        return "\n".join([f"{name}:"] + body + ["\ts_endpgm"])
+    dma = [";;#ASMSTART", "\ts_mov_b32 m0, s4", "\ts_nop 0", "\tglobal_load_lds_dwordx4 v[2:3], off", ";;#ASMEND"]
+    own_wait = [";;#ASMSTART", "\ts_waitcnt vmcnt(0)", ";;#ASMEND"]
+    reload = ["\tscratch_load_dword v9, off, off offset:12", "\ts_waitcnt vmcnt(0)", "\tv_add_u32_e32 v1, v9, v1"]
+    default = "Lb0ELb1ELb0ELb0E"
+    # a reload after the kernel's own full wait is harmless
+    assert check_waits_behind_tile_loads(decode(default, dma + own_wait + reload)) == []
+    # between a tile load and the kernel's own wait it also waits for the tile
+    assert len(check_waits_behind_tile_loads(decode(default, dma + reload + own_wait))) == 1
+    # a partial wait of the kernel's own leaves loads in flight
+    partial = [";;#ASMSTART", "\ts_waitcnt vmcnt(6)", ";;#ASMEND"]
+    assert len(check_waits_behind_tile_loads(decode(default, dma + partial + reload))) == 1
+    # the opt-in variants (in-kernel merge, fp8 PV) are not checked
+    assert check_waits_behind_tile_loads(decode("Lb0ELb1ELb0ELb1E", dma + reload)) == []
+    assert check_waits_behind_tile_loads(decode("Lb0ELb1ELb1ELb0E", dma + reload)) == []
+
+
 def test_built_kernel_passes_the_checks():
     path = os.path.join(ROOT, "paged_mla_decode_02_amd", "_build", "decode.gfx950.s")
     if not os.path.exists(path):
@@ -119,3 +141,4 @@ def test_built_kernel_passes_the_checks():
     assert check_valu_to_mfma(text) == []
     assert check_m0(text) == []
     assert check_scratch_in_step_loops(text) == []
+    assert check_waits_behind_tile_loads(text) == []
