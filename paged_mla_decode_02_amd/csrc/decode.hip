@@ -1301,8 +1301,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       uint16_t* const dst0 = part < 0 ? a.o : a.ws_o;   // bf16 O, or the split's partial O
       // A lane takes one staged chunk (8 columns) of a row per store: row
       // r = 4 i + w (uniform), chunk el. The chunks of a batch are all read
-      // before its stores, so the LDS latency is paid once per batch.
-      constexpr int kStores = kRows / kWaves, kBatch = 8;
+      // before its stores, so the LDS latency is paid once per batch (two
+      // batches of 16: the queries are dead here, so the registers are free;
+      // one batch of 32 made the compiler spill inside the step loops).
+      constexpr int kStores = kRows / kWaves, kBatch = 16;
 #pragma unroll
       for (int i0 = 0; i0 < kStores; i0 += kBatch) {
         bf16x8 v[kBatch];
