@@ -421,6 +421,9 @@ __device__ __forceinline__ float split_q_rows(u32x8 (&q)[2 * kKSteps8]) {
   if (amax > 0.f && __builtin_isfinite(amax)) frexpf(amax, &ex);   // amax in [2^(ex-1), 2^ex)
   ex = max(ex, -100);   // keeps 2^(8 - ex) and the score scale normal floats
   const float scale = ldexpf(1.0f, 8 - ex), inv = ldexpf(1.0f, ex - 8);
+  // (2^A, 0) and (0, 2^A) as bf16 pairs (2^A is exact in bf16)
+  const uint32_t sc_bits = __float_as_uint(scale) >> 16;
+  const bf16x2v sc_lo = __builtin_bit_cast(bf16x2v, sc_bits), sc_hi = __builtin_bit_cast(bf16x2v, sc_bits << 16);
 #pragma unroll
   for (int p = 0; p < kKSteps8; ++p) {
     // Stage by stage over the product's 16 dwords (scheduling barriers
@@ -441,12 +444,17 @@ __device__ __forceinline__ float split_q_rows(u32x8 (&q)[2 * kKSteps8]) {
     float r[32];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi[k], false);
-      const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi[k], true);
-      r[4 * k] = __builtin_fmaf(bf16_lo(w[2 * k]), scale, -f01[0]);
-      r[4 * k + 1] = __builtin_fmaf(bf16_hi(w[2 * k]), scale, -f01[1]);
-      r[4 * k + 2] = __builtin_fmaf(bf16_lo(w[2 * k + 1]), scale, -f23[0]);
-      r[4 * k + 3] = __builtin_fmaf(bf16_hi(w[2 * k + 1]), scale, -f23[1]);
+      // -hi from the sign-flipped codes; x 2^A - hi as one bf16 dot product
+      // per element against (2^A, 0) or (0, 2^A), accumulating -hi (exact:
+      // the product is exact and the residual fits in a float)
+      const uint32_t nh = hi[k] ^ 0x80808080u;
+      const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)nh, false);
+      const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)nh, true);
+      const bf16x2v a0 = __builtin_bit_cast(bf16x2v, w[2 * k]), a1 = __builtin_bit_cast(bf16x2v, w[2 * k + 1]);
+      r[4 * k] = __builtin_amdgcn_fdot2_f32_bf16(a0, sc_lo, f01[0], false);
+      r[4 * k + 1] = __builtin_amdgcn_fdot2_f32_bf16(a0, sc_hi, f01[1], false);
+      r[4 * k + 2] = __builtin_amdgcn_fdot2_f32_bf16(a1, sc_lo, f23[0], false);
+      r[4 * k + 3] = __builtin_amdgcn_fdot2_f32_bf16(a1, sc_hi, f23[1], false);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
