@@ -31,6 +31,20 @@ __device__ __forceinline__ uint8_t to_e4m3fn(float v) {
   return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xFF);
 }
 
+// x / s rounded to nearest, from r = 1 / s (itself correctly rounded, one
+// division per thread) and one fused correction: by Markstein's theorem
+// (IBM J. Res. Dev. 34(1), 1990), when r is the correctly rounded reciprocal
+// and q0 lies within one ulp of x / s, q0 + r (x - q0 s) rounded once is the
+// correctly rounded quotient, for quotients in the normal range. Zero, tiny
+// (below 2^-100), saturating (above 448) and non-finite quotients keep q0:
+// the e4m3fn encoding maps them to the same code as the exact quotient.
+__device__ __forceinline__ float div_rn(float x, float s, float r) {
+  const float q0 = x * r;
+  const float rem = __builtin_fmaf(-q0, s, x);   // exact
+  const float q1 = __builtin_fmaf(rem, r, q0);
+  const float aq = __builtin_fabsf(q0);
+  return (aq >= 0x1p-100f && aq <= 448.0f) ? q1 : q0;
+}
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.tokens) return;
@@ -38,11 +52,12 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   if (slot < 0 || slot >= a.num_slots) return;   // padding token, or out of the pool
   const int lane = threadIdx.x & 63;
   const float scale = a.kv_scale ? *a.kv_scale : 1.0f;
+  const float rscale = 1.0f / scale;
   for (int e = lane; e < kRow; e += 64) {
     const float x = e < kNope ? load_src(a.kv_c, a.kv_c_dtype, (int64_t)t * a.kv_c_stride + e)
                               : load_src(a.k_pe, a.k_pe_dtype, (int64_t)t * a.k_pe_stride + e - kNope);
     const int64_t o = slot * kRow + e;
-    if (a.kv_fp8) ((uint8_t*)a.pool)[o] = to_e4m3fn(x / scale);   // correctly rounded division
+    if (a.kv_fp8) ((uint8_t*)a.pool)[o] = to_e4m3fn(div_rn(x, scale, rscale));
     else ((__bf16*)a.pool)[o] = (__bf16)x;                           // round to nearest even
   }
 }
@@ -85,9 +100,10 @@ __global__ __launch_bounds__(256) void cache_write_vec_kernel(CacheWriteArgs a) 
   const int64_t o = slot * kRow + 8 * p;
   if (a.kv_fp8) {
     const float scale = a.kv_scale ? *a.kv_scale : 1.0f;
+    const float rscale = 1.0f / scale;
     uint64_t w = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) w |= (uint64_t)to_e4m3fn(x[k] / scale) << (8 * k);
+    for (int k = 0; k < 8; ++k) w |= (uint64_t)to_e4m3fn(div_rn(x[k], scale, rscale)) << (8 * k);
     *(uint64_t*)((uint8_t*)a.pool + o) = w;
   } else {
     typedef __bf16 v8 __attribute__((ext_vector_type(8)));

@@ -91,6 +91,49 @@ def test_cache_write_fp8_scales_and_strided_rows(mla, scale):
     _case(mla, 7, "fp8", "fp32", "fp32", strided=True, scale=scale)
 
 
+@pytest.mark.parametrize("scale", [0.0371, 3.0, 1.0 / 3.0, 123.456, 0.999999])
+@pytest.mark.parametrize("pad", [0, 5])
+def test_cache_write_fp8_quotients_near_ties(mla, scale, pad):
+    """Quotients x / scale within a few float32 ulps of e4m3fn rounding ties
+    (midpoints of neighbouring codes), of the largest finite value and of the
+    subnormal range, for scales that are not powers of two: every code must be
+    the one the correctly rounded quotient gives. fp32 sources, so x is exact;
+    pad 5 leaves the rows unaligned (the per-element kernel)."""
+    s = np.float32(scale)
+    codes = e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = np.concatenate([(codes[:-1] + codes[1:]) / 2, [448.0, 464.0, 2.0 ** -10, 2.0 ** -9]])
+    xs = []
+    for m in mids:
+        v = np.float32(m * float(s))
+        for k in range(-3, 4):
+            w = v
+            for _ in range(abs(k)):
+                w = np.nextafter(w, np.float32(np.inf) if k > 0 else np.float32(-np.inf))
+            xs.append(w)
+    xs = np.array(xs, dtype=np.float32)
+    xs = np.concatenate([xs, -xs, np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1e30, -1e-30], np.float32)])
+    tokens = (len(xs) + 575) // 576
+    full = np.zeros(tokens * 576, np.float32)
+    full[:len(xs)] = xs
+    full = full.reshape(tokens, 576)
+    rng = np.random.default_rng(31)
+    slots_n = 2 * tokens + 7
+    pool0 = rng.integers(0, 256, (slots_n, 576), dtype=np.uint8)
+    pool = torch.from_numpy(pool0).cuda()
+    kv_c_big = torch.from_numpy(np.pad(full[:, :512], ((0, 0), (0, pad)))).cuda()
+    kv_c = kv_c_big[:, :512]
+    k_pe = torch.from_numpy(np.ascontiguousarray(full[:, 512:])).cuda()
+    slots = rng.permutation(slots_n)[:tokens].astype(np.int64)
+    print(f"cache_write ties scale={scale} pad={pad} tokens={tokens}", flush=True)
+    mla.cache_write(kv_c, k_pe, torch.from_numpy(slots).cuda(), pool, "fp8",
+                    torch.tensor([float(s)], dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    want = oracle_write(pool0, full[:, :512], full[:, 512:], slots, "fp8", kv_scale=float(s))
+    got = pool.cpu().numpy()
+    mism = got != want
+    assert not mism.any(), (np.argwhere(mism)[:5], got[mism][:5], want[mism][:5])
+
+
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("c_dt", ["bf16", "fp32"])
 def test_cache_write_unaligned_rows(mla, kv_dtype, c_dt):
