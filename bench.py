@@ -484,7 +484,8 @@ def bench_cache_write(args):
         "config": {"workload": "cache_write", "tokens": T, "src": "bf16", "kv_dtype": kv_dtype,
                    "pool_slots": slots_n},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "cache_write_kernel",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "cache_write_fp8x16_kernel" if kv_dtype == "fp8" else "cache_write_bf16_vec_kernel",
                      "launch_ms": round(launch_ms, 4), "algorithmic_bytes": alg}}), flush=True)
 
 
