@@ -126,9 +126,9 @@ def test_compiler_wait_behind_tile_loads_is_flagged():
     # a partial wait of the kernel's own leaves loads in flight
     partial = [";;#ASMSTART", "\ts_waitcnt vmcnt(6)", ";;#ASMEND"]
     assert len(check_waits_behind_tile_loads(decode(default, dma + partial + reload))) == 1
-    # the opt-in variants (in-kernel merge, fp8 PV) are not checked
+    # the in-kernel merge is checked too; the fp8 PV products are not
+    assert len(check_waits_behind_tile_loads(decode("Lb0ELb1ELb1ELb0E", dma + reload))) == 1
     assert check_waits_behind_tile_loads(decode("Lb0ELb1ELb0ELb1E", dma + reload)) == []
-    assert check_waits_behind_tile_loads(decode("Lb0ELb1ELb1ELb0E", dma + reload)) == []
 
 
 def test_built_kernel_passes_the_checks():
