@@ -29,13 +29,20 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 # The sources of the kernels one mla_decode_fwd call launches (decode, merge).
 KERNEL_SRCS = [os.path.join(ROOT, "paged_mla_decode_02_amd", "csrc", f) for f in ("decode.hip", "kernels.hip")]
+# The source of the latent cache write (mla_cache_write).
+CACHE_WRITE_SRCS = [os.path.join(ROOT, "paged_mla_decode_02_amd", "csrc", "cache_write.hip")]
 
 
-def kernel_sha():
+def traffic_srcs(workload):
+    """The sources whose kernels a traffic record's workload launches."""
+    return CACHE_WRITE_SRCS if workload.startswith("cache_write") else KERNEL_SRCS
+
+
+def kernel_sha(srcs=None):
     """Hash of the kernel code: the sources with // comments and blank lines
     dropped, so a comment edit does not invalidate a traffic record."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in srcs or KERNEL_SRCS:
         for line in open(path, encoding="utf-8"):
             code = line.split("//", 1)[0].rstrip()
             if code:
@@ -55,20 +62,22 @@ def visible_pairs(kv_lens, q_lens, causal):
 
 
 def measured_traffic(workload):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source."""
+    """HBM bytes per launch (decode + merge, or one cache write) from
+    committed rocprofv3 counter runs, if they were taken on the current
+    kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("kernel_sha") != kernel_sha():
+    if d.get("kernel_sha") != kernel_sha(traffic_srcs(workload)):
         return None
     return d.get("bytes_per_launch")
 
 
 def traffic_from_counters(workload, fetch_csv, write_csv, copy_mib):
-    """HBM bytes per mla_decode_fwd call from two rocprofv3 --pmc passes
-    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) of `bench.py --copy-mib N`.
+    """HBM bytes per mla_decode_fwd call (or, for a cache_write_* workload,
+    per mla_cache_write call) from two rocprofv3 --pmc passes (FETCH_SIZE,
+    WRITE_SIZE; KiB per dispatch) of `bench.py --copy-mib N`.
     Each counter is divided by what it reads for the known-size device copy
     (the largest __amd_rocclr_copyBuffer dispatch: copy_mib MiB read and
     written). Writes profiles/traffic_<workload>.json and returns it."""
@@ -83,14 +92,16 @@ def traffic_from_counters(workload, fetch_csv, write_csv, copy_mib):
             vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
         return vals
 
-    out = {"workload": workload, "kernel_sha": kernel_sha(), "copy_mib": copy_mib}
+    out = {"workload": workload, "kernel_sha": kernel_sha(traffic_srcs(workload)), "copy_mib": copy_mib}
+    main_kernel, extra = (("cache_write", ()) if workload.startswith("cache_write")
+                          else ("decode_kernel", ("merge_kernel", "merge_wide_kernel")))
     total = 0.0
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals = per_dispatch(path, name)
         copy_kib = max(v for (d, k), v in vals.items() if "copyBuffer" in k)
         factor = copy_kib / (copy_mib * 1024.0)
-        decode = [v for (d, k), v in vals.items() if "decode_kernel" in k]
-        merge = [v for (d, k), v in vals.items() if "merge_kernel" in k or "merge_wide_kernel" in k]
+        decode = [v for (d, k), v in vals.items() if main_kernel in k]
+        merge = [v for (d, k), v in vals.items() if any(e in k for e in extra)]
         launches = len(decode)
         kib = (sum(decode) + sum(merge)) / launches
         out[name] = {"raw_kib_per_launch": round(kib, 3), "copy_raw_kib": round(copy_kib, 3),
@@ -173,7 +184,8 @@ def main():
                          "reference for scaling hardware byte counters")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="only turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a "
-                         "--copy-mib run into profiles/traffic_<workload>.json")
+                         "--copy-mib run into profiles/traffic_<workload>.json (with --op cache_write: "
+                         "profiles/traffic_cache_write_<kv-dtype>.json)")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="before the warm-up steps, run untimed decode calls until the GPU has been busy "
                          "this long and two consecutive batches of 10 calls agree within 2%% (clocks settle "
@@ -194,7 +206,8 @@ def main():
     ap.add_argument("--kv-dtype", default="fp8", choices=["fp8", "bf16"], help="cache_write: pool dtype")
     args = ap.parse_args()
     if args.traffic_from:
-        print(json.dumps(traffic_from_counters(args.workload, *args.traffic_from, args.copy_mib or 256)))
+        wl = f"cache_write_{args.kv_dtype}" if args.op == "cache_write" else args.workload
+        print(json.dumps(traffic_from_counters(wl, *args.traffic_from, args.copy_mib or 256)))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -462,6 +475,13 @@ def bench_cache_write(args):
     slot_sets = [torch.from_numpy(rng.permutation(slots_n)[:T].astype(np.int64)).cuda() for _ in range(3)]
     scale = torch.tensor([0.05], dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    if args.copy_mib > 0:   # the known-size reference for the byte counters
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for k in range(args.warmup):
         mla.cache_write(kv_c, k_pe, slot_sets[k % 3], pool, kv_dtype, scale)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -484,7 +504,7 @@ def bench_cache_write(args):
         "config": {"workload": "cache_write", "tokens": T, "src": "bf16", "kv_dtype": kv_dtype,
                    "pool_slots": slots_n},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(f"cache_write_{kv_dtype}"),
                      "kernel": "cache_write_fp8x16_kernel" if kv_dtype == "fp8" else "cache_write_bf16_vec_kernel",
                      "launch_ms": round(launch_ms, 4), "algorithmic_bytes": alg}}), flush=True)
 
