@@ -101,7 +101,8 @@ def traffic_from_counters(workload, fetch_csv, write_csv, copy_mib):
         copy_kib = max(v for (d, k), v in vals.items() if "copyBuffer" in k)
         factor = copy_kib / (copy_mib * 1024.0)
         decode = [v for (d, k), v in vals.items() if main_kernel in k]
-        merge = [v for (d, k), v in vals.items() if any(e in k for e in extra)]
+        # (the W-way shard merge of a dcp run is timed on its own, not part of a decode call)
+        merge = [v for (d, k), v in vals.items() if any(e in k for e in extra) and "shard_merge" not in k]
         launches = len(decode)
         kib = (sum(decode) + sum(merge)) / launches
         out[name] = {"raw_kib_per_launch": round(kib, 3), "copy_raw_kib": round(copy_kib, 3),
@@ -206,7 +207,8 @@ def main():
     ap.add_argument("--kv-dtype", default="fp8", choices=["fp8", "bf16"], help="cache_write: pool dtype")
     args = ap.parse_args()
     if args.traffic_from:
-        wl = f"cache_write_{args.kv_dtype}" if args.op == "cache_write" else args.workload
+        wl = (f"cache_write_{args.kv_dtype}" if args.op == "cache_write"
+              else dcp_workload(args) if args.op == "dcp" else args.workload)
         print(json.dumps(traffic_from_counters(wl, *args.traffic_from, args.copy_mib or 256)))
         return
 
@@ -509,6 +511,10 @@ def bench_cache_write(args):
                      "launch_ms": round(launch_ms, 4), "algorithmic_bytes": alg}}), flush=True)
 
 
+def dcp_workload(args):
+    return f"dcp_verify_rank0_w{args.dcp_world}_h{args.heads}"
+
+
 def bench_dcp(args):
     """One decode-context-parallel rank at the verify shape: 32 rows, q_len 8,
     `heads` gathered query heads, bf16, causal; the rows' lengths of the verify
@@ -547,6 +553,13 @@ def bench_dcp(args):
     om = torch.empty_like(o)
     lm = torch.empty_like(lse)
     stream = torch.cuda.current_stream()
+    if args.copy_mib > 0:   # the known-size reference for the byte counters
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def fwd():
         mla.decode_fwd_dcp(dev["q"], "bf16", None, dev["kv_pool"], "bf16", None, dev["qo_indptr"], indptr,
@@ -584,7 +597,8 @@ def bench_dcp(args):
         "config": {"workload": "dcp_verify_rank0", "dcp_world": W, "heads": H, "rows": case.rows,
                    "q_len": 8, "local_keys": keys, "splits": int(words[14])},
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS["bf16"],
-                     "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4),
+                     "traffic": measured_traffic(dcp_workload(args)),
                      "kernel": "decode_kernel (+merge_kernel if split)", "launch_ms": round(t_dec, 4),
                      "algorithmic_flops": flops},
         "merge": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
